@@ -1,0 +1,413 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each pin is a function ``pin_*`` that raises AssertionError when the oracle
+disagrees with: a library routine (torch SDPA in float64 on the CPU), an
+independent formulation (complex-multiplication RoPE, the absorbed query, the
+fused value path), a scalar mpmath brute force, closed forms, or a hand-worked
+fixture under tests/golden/.  ``test_planted_mistakes`` plants plausible bugs
+into the oracle (on the CPU) and checks that some pin catches each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.palu as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(1234)
+
+
+def _rand_case(rng, batch=2, H=4, Hkv=2, d_h=8, G=2, r=5, L=7, ragged=True):
+    n_g = Hkv // G
+    w = n_g * d_h
+    q = rng.standard_normal((batch, H, d_h))
+    zk = [rng.standard_normal((batch, L, r)) for _ in range(G)]
+    zv = [rng.standard_normal((batch, L, r + 1)) for _ in range(G)]
+    Bk = [rng.standard_normal((r, w)) / math.sqrt(r) for _ in range(G)]
+    Bv = [rng.standard_normal((r + 1, w)) / math.sqrt(r) for _ in range(G)]
+    lens = rng.integers(1, L + 1, size=batch) if ragged else np.full(batch, L)
+    return q, zk, zv, Bk, Bv, lens
+
+
+# ------------------------------------------------------------------ independent references
+def _rope_complex(u, pos, base):
+    """RoPE as complex multiplication: u_i + i*u_{i+d/2} times exp(i*pos*theta_i),
+    theta_i = base^(-2i/d)."""
+    d = u.shape[-1]
+    h = d // 2
+    theta = np.array([base ** (-(2.0 * i) / d) for i in range(h)])
+    zc = (u[..., :h] + 1j * u[..., h:]) * np.exp(1j * np.asarray(pos, dtype=np.float64)[..., None] * theta)
+    return np.concatenate([zc.real, zc.imag], axis=-1)
+
+
+def _sdpa(q, K, V, scale):
+    import torch
+    import torch.nn.functional as F
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, None, None, :]
+    Kt = torch.from_numpy(np.ascontiguousarray(K))[None, None]
+    Vt = torch.from_numpy(np.ascontiguousarray(V))[None, None]
+    return F.scaled_dot_product_attention(qt, Kt, Vt, scale=scale)[0, 0, 0].numpy()
+
+
+# ------------------------------------------------------------------ pins
+def pin_identity_vs_sdpa(use_rope):
+    """A = W, B = I, r = w: the method reduces to standard attention over
+    K = x W_k, V = x W_v (spec check (a)); reference: torch SDPA fp64."""
+    rng = np.random.default_rng(7)
+    batch, H, Hkv, d_h, G, D, L = 2, 6, 2, 8, 2, 12, 9
+    n_g = Hkv // G
+    w = n_g * d_h
+    x = rng.standard_normal((batch, L, D))
+    Wk = [rng.standard_normal((D, w)) / math.sqrt(D) for _ in range(G)]
+    Wv = [rng.standard_normal((D, w)) / math.sqrt(D) for _ in range(G)]
+    q = rng.standard_normal((batch, H, d_h))
+    lens = np.array([L, 4])
+    zk = [O.project(x.reshape(-1, D), Wk[j]).reshape(batch, L, w) for j in range(G)]
+    zv = [O.project(x.reshape(-1, D), Wv[j]).reshape(batch, L, w) for j in range(G)]
+    eye = [np.eye(w) for _ in range(G)]
+    scale = 1.0 / math.sqrt(d_h)
+    out = O.decode_attention(q, zk, zv, eye, eye, lens, n_kv_heads=Hkv, use_rope=use_rope, sm_scale=scale)
+    for b in range(batch):
+        Lb = lens[b]
+        for h in range(H):
+            kv = h // (H // Hkv)
+            j, c = kv // n_g, kv % n_g
+            K = (x[b, :Lb] @ Wk[j])[:, c * d_h:(c + 1) * d_h]
+            V = (x[b, :Lb] @ Wv[j])[:, c * d_h:(c + 1) * d_h]
+            qh = q[b, h]
+            if use_rope:
+                K = _rope_complex(K, np.arange(Lb), 10000.0)
+                qh = _rope_complex(qh, Lb - 1, 10000.0)
+            ref = _sdpa(qh, K, V, scale)
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+def pin_absorbed_and_fused_value():
+    """No-RoPE heads: attention through the absorbed query (q . B_k^T) against
+    z_k and values through (P . z_v) . B_v equal the rebuilt-K/V result
+    (spec check (b))."""
+    rng = np.random.default_rng(11)
+    q, zk, zv, Bk, Bv, lens = _rand_case(rng, batch=3, H=8, Hkv=4, d_h=6, G=2, r=4, L=11)
+    batch, H, d_h = q.shape
+    Hkv, G = 4, 2
+    n_g = Hkv // G
+    scale = 0.37
+    out = O.decode_attention(q, zk, zv, Bk, Bv, lens, n_kv_heads=Hkv, use_rope=False, sm_scale=scale)
+    for b in range(batch):
+        Lb = lens[b]
+        for h in range(H):
+            kv = h // (H // Hkv)
+            j, c = kv // n_g, kv % n_g
+            q_abs = Bk[j][:, c * d_h:(c + 1) * d_h] @ q[b, h]          # [r]
+            s = scale * (zk[j][b, :Lb] @ q_abs)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = (p @ zv[j][b, :Lb]) @ Bv[j][:, c * d_h:(c + 1) * d_h]
+            np.testing.assert_allclose(out[b, h], o, rtol=0, atol=1e-12)
+
+
+def pin_mpmath_bruteforce():
+    """Scalar evaluation of every sum at 50 digits (mpmath) on tiny shapes
+    (spec check (c), brute force)."""
+    import mpmath as mp
+    mp.mp.dps = 50
+    rng = np.random.default_rng(3)
+    for (d_h, r, L, G, use_rope) in [(2, 1, 3, 1, True), (4, 3, 4, 2, True), (4, 2, 2, 2, False),
+                                     (2, 3, 4, 1, True)]:
+        Hkv = 2 * G
+        H = 2 * Hkv
+        n_g = Hkv // G
+        w = n_g * d_h
+        q = rng.standard_normal((1, H, d_h))
+        zk = [rng.standard_normal((1, L, r)) for _ in range(G)]
+        zv = [rng.standard_normal((1, L, r)) for _ in range(G)]
+        Bk = [rng.standard_normal((r, w)) for _ in range(G)]
+        Bv = [rng.standard_normal((r, w)) for _ in range(G)]
+        base, scale = 10000.0, 0.5
+        out = O.decode_attention(q, zk, zv, Bk, Bv, [L], n_kv_heads=Hkv, use_rope=use_rope,
+                                 rope_base=base, sm_scale=scale)
+        for h in range(H):
+            kv = h // (H // Hkv)
+            j, c = kv // n_g, kv % n_g
+
+            def rot(vec, pos):
+                if not use_rope:
+                    return vec
+                hd = d_h // 2
+                res = list(vec)
+                for i in range(hd):
+                    ang = mp.mpf(pos) * mp.power(mp.mpf(base), -mp.mpf(2 * i) / d_h)
+                    a, bb = vec[i], vec[i + hd]
+                    res[i] = a * mp.cos(ang) - bb * mp.sin(ang)
+                    res[i + hd] = a * mp.sin(ang) + bb * mp.cos(ang)
+                return res
+
+            keys, vals = [], []
+            for t in range(L):
+                k = [mp.fsum(mp.mpf(zk[j][0, t, kk]) * mp.mpf(Bk[j][kk, c * d_h + d]) for kk in range(r))
+                     for d in range(d_h)]
+                v = [mp.fsum(mp.mpf(zv[j][0, t, kk]) * mp.mpf(Bv[j][kk, c * d_h + d]) for kk in range(r))
+                     for d in range(d_h)]
+                keys.append(rot(k, t))
+                vals.append(v)
+            qr = rot([mp.mpf(x) for x in q[0, h]], L - 1)
+            s = [mp.mpf(scale) * mp.fsum(qr[d] * keys[t][d] for d in range(d_h)) for t in range(L)]
+            e = [mp.exp(si) for si in s]
+            z = mp.fsum(e)
+            ref = [mp.fsum(e[t] * vals[t][d] for t in range(L)) / z for d in range(d_h)]
+            np.testing.assert_allclose(out[0, h], np.array([float(x) for x in ref]), rtol=0, atol=1e-13)
+
+
+def pin_softmax_closed_forms():
+    rng = np.random.default_rng(5)
+    L, d = 6, 4
+    K = rng.standard_normal((L, d))
+    V = rng.standard_normal((L, d))
+    # L = 1: the output is the single value row
+    np.testing.assert_allclose(O.attend(rng.standard_normal(d), K[:1], V[:1], 0.7), V[0], rtol=0, atol=1e-15)
+    # zero query: uniform weights, output is the mean row
+    np.testing.assert_allclose(O.attend(np.zeros(d), K, V, 0.7), V.mean(axis=0), rtol=0, atol=1e-14)
+    # weights sum to one: with all-ones values the output is exactly ones
+    np.testing.assert_allclose(O.attend(rng.standard_normal(d), K, np.ones((L, 3)), 1.3), np.ones(3),
+                               rtol=0, atol=1e-14)
+    # one dominant score: output tends to that row
+    Kd = np.zeros((L, d))
+    Kd[3, 0] = 1.0
+    np.testing.assert_allclose(O.attend(np.array([800.0, 0, 0, 0]), Kd, V, 1.0), V[3], rtol=0, atol=1e-12)
+    # shift invariance of the scores (adding a constant to all scores)
+    q = rng.standard_normal(d)
+    Kc = np.concatenate([K, np.ones((L, 1))], axis=1)
+    a = O.attend(np.concatenate([q, [0.0]]), Kc, V, 1.0)
+    b = O.attend(np.concatenate([q, [37.0]]), Kc, V, 1.0)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def pin_rope():
+    rng = np.random.default_rng(9)
+    base = 10000.0
+    for d in (2, 4, 8, 128):
+        u = rng.standard_normal((5, d))
+        pos = rng.integers(0, 70000, size=5)
+        # equals complex multiplication with theta_i = base^(-2i/d) (fixes the half-split pairing)
+        np.testing.assert_allclose(O.rope(u, pos, base), _rope_complex(u, pos, base), rtol=0, atol=1e-9)
+        # isometry, identity at 0, composition
+        np.testing.assert_allclose(np.linalg.norm(O.rope(u, pos, base), axis=-1), np.linalg.norm(u, axis=-1),
+                                   rtol=1e-13)
+        np.testing.assert_array_equal(O.rope(u, np.zeros(5), base), u)
+        a, b = 1234, 5678
+        np.testing.assert_allclose(O.rope(O.rope(u, a, base), b, base), O.rope(u, a + b, base), rtol=0, atol=1e-10)
+        # scores depend only on the relative position
+        k, qv = rng.standard_normal(d), rng.standard_normal(d)
+        s1 = O.rope(qv, 100, base) @ O.rope(k, 40, base)
+        s2 = O.rope(qv, 1100, base) @ O.rope(k, 1040, base)
+        assert abs(s1 - s2) < 1e-10 * max(1.0, abs(s1))
+    # d = 2: theta_0 = 1, a plain planar rotation by t radians
+    t = 3
+    np.testing.assert_allclose(O.rope(np.array([1.0, 0.0]), t, base), [math.cos(t), math.sin(t)], rtol=0,
+                               atol=1e-15)
+    # d = 4: second pair rotates at base^(-1/2)
+    th = base ** -0.5
+    np.testing.assert_allclose(O.rope(np.array([0.0, 1.0, 0.0, 0.0]), 2, base),
+                               [0.0, math.cos(2 * th), 0.0, math.sin(2 * th)], rtol=0, atol=1e-15)
+
+
+def pin_gqa():
+    """With GQA, replicating every kv head to its query heads (MHA) gives the
+    same output; with H = H_kv the mapping is the identity."""
+    rng = np.random.default_rng(13)
+    batch, H, Hkv, d_h, G, r, L = 2, 8, 4, 4, 2, 3, 6
+    n_g = Hkv // G
+    q, zk, zv, Bk, Bv, lens = _rand_case(rng, batch, H, Hkv, d_h, G, r, L)
+    out = O.decode_attention(q, zk, zv, Bk, Bv, lens, n_kv_heads=Hkv, use_rope=True)
+    # MHA layout: group j now holds n_g * (H/Hkv) kv heads, each a copy of its source
+    rep = H // Hkv
+    Bk2 = [np.concatenate([Bk[j][:, (c // rep) * d_h:(c // rep + 1) * d_h] for c in range(n_g * rep)], axis=1)
+           for j in range(G)]
+    Bv2 = [np.concatenate([Bv[j][:, (c // rep) * d_h:(c // rep + 1) * d_h] for c in range(n_g * rep)], axis=1)
+           for j in range(G)]
+    out2 = O.decode_attention(q, zk, zv, Bk2, Bv2, lens, n_kv_heads=H, use_rope=True)
+    np.testing.assert_allclose(out, out2, rtol=0, atol=1e-13)
+
+
+def pin_split_merge():
+    """Merging partials of any split of the history equals the single pass."""
+    rng = np.random.default_rng(17)
+    L, d = 37, 8
+    q, K, V = rng.standard_normal(d), rng.standard_normal((L, d)), rng.standard_normal((L, d))
+    full = O.attend(q, K, V, 0.4)
+    for _ in range(10):
+        cuts = sorted(set(rng.integers(1, L, size=rng.integers(1, 6)).tolist()))
+        edges = [0] + cuts + [L]
+        parts = [O.attend_partial(q, K[a:b], V[a:b], 0.4) for a, b in zip(edges[:-1], edges[1:])]
+        np.testing.assert_allclose(O.merge_partials(parts), full, rtol=0, atol=1e-13)
+
+
+def pin_golden_decode():
+    with open(os.path.join(GOLDEN, "decode_worked.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        out = O.decode_attention(q, [np.array(case["zk"], float)], [np.array(case["zv"], float)],
+                                 [np.array(case["Bk"], float)], [np.array(case["Bv"], float)],
+                                 case["seq_lens"], n_kv_heads=case["n_kv_heads"], use_rope=case["use_rope"],
+                                 sm_scale=case["sm_scale"])
+        np.testing.assert_allclose(out, np.array(case["expected"]), rtol=0, atol=1e-14)
+
+
+def pin_rope_closed_form_d2():
+    """Closed form with d_h = 2 and RoPE: keys [1,0] at t=0 and 0 at t=1, query
+    [ln 3, 0] at p=1: the score of key 0 is ln3*cos(1), of key 1 zero."""
+    q = np.array([[[math.log(3.0), 0.0]]])
+    zk = [np.array([[[1.0, 0.0], [0.0, 0.0]]])]
+    zv = [np.array([[[1.0, 1.0], [0.0, 1.0]]])]
+    Bk = [np.eye(2)]
+    Bv = [np.array([[1.0, 2.0], [3.0, -1.0]])]
+    out = O.decode_attention(q, zk, zv, Bk, Bv, [2], n_kv_heads=1, use_rope=True, sm_scale=1.0)
+    p0 = 3.0 ** math.cos(1.0) / (3.0 ** math.cos(1.0) + 1.0)
+    ref = p0 * np.array([4.0, 1.0]) + (1 - p0) * np.array([3.0, -1.0])
+    np.testing.assert_allclose(out[0, 0], ref, rtol=0, atol=1e-14)
+
+
+def pin_project():
+    """z = x A against integer brute force (exact)."""
+    rng = np.random.default_rng(19)
+    x = rng.integers(-5, 6, size=(7, 9))
+    A = rng.integers(-5, 6, size=(9, 4))
+    ref = [[sum(int(x[i, k]) * int(A[k, j]) for k in range(9)) for j in range(4)] for i in range(7)]
+    np.testing.assert_array_equal(O.project(x, A), np.array(ref, dtype=np.float64))
+
+
+def pin_int4_golden():
+    with open(os.path.join(GOLDEN, "int4_worked.json")) as f:
+        fx = json.load(f)
+    z = np.array(fx["z"], dtype=np.float32)
+    codes, scales = O.quant_int4(z)
+    np.testing.assert_array_equal(codes, np.array(fx["codes"], dtype=np.int8))
+    np.testing.assert_array_equal(scales.astype(np.float64), np.array(fx["scales"]))
+    packed = O.pack_int4(codes)
+    assert packed.tobytes().hex() == fx["packed_hex"]
+    np.testing.assert_array_equal(O.unpack_int4(packed, fx["r"]), codes)
+
+
+def pin_int4_properties():
+    rng = np.random.default_rng(23)
+    for r in (32, 40, 154, 160):
+        z = (rng.standard_normal((50, r)) * rng.uniform(0.01, 100, size=(50, 1))).astype(np.float32)
+        codes, scales = O.quant_int4(z)
+        assert codes.min() >= -7 and codes.max() <= 7
+        assert scales.shape == (50, O.chunks_per_row(r))
+        deq = O.dequant_int4(codes, scales)
+        s = np.repeat(scales.astype(np.float64), 32, axis=-1)[:, :r]
+        assert np.all(np.abs(z - deq) <= 0.5 * s * (1 + 1e-5))
+        # every chunk reaches |code| = 7 at its largest element (scale is amax/7)
+        for c in range(O.chunks_per_row(r)):
+            seg = codes[:, c * 32:min(r, c * 32 + 32)]
+            assert np.all(np.abs(seg).max(axis=-1) == 7)
+        # dequantised values are exact in fp32: q*s has at most 3 + 11 significant bits
+        np.testing.assert_array_equal(deq.astype(np.float32).astype(np.float64), deq)
+        np.testing.assert_array_equal(O.unpack_int4(O.pack_int4(codes), r), codes)
+    # exact round trip for z = k*s with amax = 7*s
+    s = 0.25
+    k = np.array([[7, -7, 0, 1, -1, 3, -3, 5] * 4], dtype=np.float32)
+    codes, scales = O.quant_int4(k * s)
+    np.testing.assert_array_equal(codes, k.astype(np.int8))
+    assert float(scales[0, 0]) == s
+    # all-zero chunk: zero scale, zero codes
+    codes, scales = O.quant_int4(np.zeros((1, 32), np.float32))
+    assert float(scales[0, 0]) == 0.0 and not codes.any()
+
+
+def pin_upcast():
+    # bf16 bit patterns: 0x3F80 = 1.0, 0xC040 = -3.0, 0x0001 = smallest subnormal 2^-133
+    bits = np.array([0x3F80, 0xC040, 0x0001], dtype=np.uint16)
+    np.testing.assert_array_equal(O.upcast(bits, "bf16"), [1.0, -3.0, 2.0 ** -133])
+    np.testing.assert_array_equal(O.upcast(np.array([0.1], np.float16), "f16"), [float(np.float16(0.1))])
+
+
+PINS = [pin_absorbed_and_fused_value, pin_mpmath_bruteforce, pin_softmax_closed_forms, pin_rope, pin_gqa,
+        pin_split_merge, pin_golden_decode, pin_rope_closed_form_d2, pin_project, pin_int4_golden,
+        pin_int4_properties, pin_upcast]
+
+
+@pytest.mark.parametrize("use_rope", [False, True])
+def test_identity_vs_sdpa(use_rope):
+    pin_identity_vs_sdpa(use_rope)
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ------------------------------------------------------------------ planted mistakes
+def _interleaved_rope(u, pos, base):
+    d = u.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * O.rope_theta(d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x, y = u[..., 0::2], u[..., 1::2]
+    out = np.empty_like(u)
+    out[..., 0::2] = x * c - y * s
+    out[..., 1::2] = x * s + y * c
+    return out
+
+
+def _wrong_sign_rope(u, pos, base):
+    return O.__dict__["_orig_rope"](u, -np.asarray(pos), base)
+
+
+def _theta_off_by_one(head_dim, base):
+    i = np.arange(1, head_dim // 2 + 1, dtype=np.float64)
+    return base ** (-2.0 * i / head_dim)
+
+
+def _attend_no_scale(q, K, V, sm_scale):
+    return O.__dict__["_orig_attend"](q, K, V, 1.0)
+
+
+def _reconstruct_dropped_row(z, B):
+    return z[:, 1:] @ B[1:]
+
+
+def _quant_ties_away(z):
+    codes, scales = O.__dict__["_orig_quant"](z)
+    z = np.asarray(z, np.float32)
+    s = np.repeat(scales.astype(np.float32), 32, axis=-1)[..., :z.shape[-1]]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qf = np.where(s == 0, 0, np.sign(z / s) * np.floor(np.abs(z / s) + 0.5))
+    return np.clip(qf, -7, 7).astype(np.int8), scales
+
+
+def _merge_no_rescale(parts):
+    return sum(p[2] for p in parts) / sum(p[1] for p in parts)
+
+
+MUTANTS = [
+    ("rope", _interleaved_rope),
+    ("rope", _wrong_sign_rope),
+    ("rope_theta", _theta_off_by_one),
+    ("attend", _attend_no_scale),
+    ("reconstruct", _reconstruct_dropped_row),
+    ("quant_int4", _quant_ties_away),
+    ("merge_partials", _merge_no_rescale),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[f"{n}:{m.__name__}" for n, m in MUTANTS])
+def test_planted_mistakes(name, mutant, monkeypatch):
+    """A plausible bug planted in the oracle must make at least one pin fail."""
+    monkeypatch.setitem(O.__dict__, "_orig_rope", O.rope)
+    monkeypatch.setitem(O.__dict__, "_orig_attend", O.attend)
+    monkeypatch.setitem(O.__dict__, "_orig_quant", O.quant_int4)
+    monkeypatch.setattr(O, name, mutant)
+    caught = False
+    for pin in [lambda: pin_identity_vs_sdpa(True), lambda: pin_identity_vs_sdpa(False)] + PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught = True
+            break
+    assert caught, f"no pin caught the planted mistake in {name}"
