@@ -1,0 +1,204 @@
+/*
+ * palu.h - C ABI of the Palu latent-cache attention library for MI355X (gfx950).
+ *
+ * The method (Palu, "KV-Cache Compression with Low-Rank Projection",
+ * arXiv 2407.21118; explained on the page "PALU low-rank projection
+ * decomposition", section "Low-rank projection decomposition", formula
+ * block) factors the key/value projections as W_k ~ A_k B_k, W_v ~ A_v B_v
+ * with A in R^{d_model x r} and B in R^{r x d}.  Only the latents
+ * z_k = x A_k and z_v = x A_v are cached; keys and values are rebuilt on the
+ * fly as K = z_k B_k and V = z_v B_v.  The same page (section "Rollout",
+ * engine integration) places the method at three points of a serving engine:
+ * the model runner produces the latents (palu_project), the cache manager
+ * stores them (the caller-owned buffers described by palu_latent_cache) and
+ * the attention kernel consumes them (palu_decode_attn).  Quantization of
+ * the latents composes with the low-rank cache (abstract; page section
+ * "Rollout", route C): palu_quant_latent.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked "device" point to GPU memory of the current HIP device;
+ *    pointers marked "host" point to CPU memory that is read during the call
+ *    only and not retained.  The caller allocates and frees every buffer; the
+ *    library never allocates device memory.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the legacy default
+ *    stream).  Argument errors are detected on the host, before anything is
+ *    enqueued, and reported synchronously; a failed launch is reported as
+ *    PALU_ERR_HIP.  Faults during execution surface at the caller's next
+ *    synchronisation.
+ *  - Calls are thread-safe; the library keeps no mutable global state other
+ *    than a per-thread error message (palu_last_error).
+ *  - Device-side preconditions that the host cannot check (values inside
+ *    device arrays) are stated per argument; out-of-range sequence lengths
+ *    are clamped to [0, max_len] by the kernels.
+ *
+ * Data formats
+ *  - PALU_F32 / PALU_F16 / PALU_BF16: IEEE binary32, binary16, bfloat16.
+ *  - PALU_I4 (latents only): symmetric 4-bit codes in [-7, 7] (4-bit two's
+ *    complement; element 2i in the low nibble of byte i) with one binary16
+ *    scale per 32 consecutive elements of a token's latent row; a latent
+ *    value is code * scale.  Rows are padded with zero nibbles to a multiple
+ *    of 32 elements.
+ *
+ * Latent cache layout (one attention layer; keys and values in separate
+ * buffers).  For head-group j with rank r_j the row pitch is
+ *     F32: 4 * roundup(r_j, 4) bytes, F16/BF16: 2 * roundup(r_j, 8) bytes,
+ *     I4: 16 * ceil(r_j / 32) bytes,
+ * and the scale-row pitch (I4 only) is 2 * ceil(r_j / 32) bytes.  Buffers are
+ * [batch][group j][max_len][pitch_j] with groups of one sequence stored one
+ * after another:  offset(b, j, t) = b * max_len * sum_j pitch_j
+ *                                 + max_len * sum_{j' < j} pitch_j' + t * pitch_j.
+ * palu_latent_bytes / palu_latent_offset compute these.  Pad bytes of a row
+ * are not data but must hold finite values (palu_project writes zeros).
+ *
+ * Factor matrices (row-major):
+ *  - A_kv  [sum_j r_k,j + sum_j r_v,j][d_model]: the transpose of
+ *    [A_k^0 | .. | A_k^{G-1} | A_v^0 | .. | A_v^{G-1}] (key ranks first), i.e.
+ *    the weight layout of a Linear(d_model -> n_lat): row c holds column c of A;
+ *  - B_k   concatenation over j of B_k^j [r_k,j][n_g * head_dim] (the
+ *    formula's own orientation);
+ *  - B_v   concatenation over j of B_v^j [r_v,j][n_g * head_dim];
+ *    column block c of B^j belongs to kv head j * n_g + c (n_g = kv heads per
+ *    group), i.e. groups hold contiguous kv heads.
+ */
+#ifndef PALU_H_
+#define PALU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PALU_OK = 0,
+  PALU_ERR_INVALID_ARG = 1,          /* null pointer, inconsistent shape, bad value */
+  PALU_ERR_UNSUPPORTED = 2,          /* valid but not implemented (shape/dtype combination) */
+  PALU_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below palu_decode_workspace_bytes() */
+  PALU_ERR_HIP = 4                   /* HIP runtime error while querying the device or launching */
+} palu_status;
+
+typedef enum { PALU_F32 = 0, PALU_F16 = 1, PALU_BF16 = 2, PALU_I4 = 3 } palu_dtype;
+
+/* One attention layer.  Host memory; read during a call only. */
+typedef struct {
+  int32_t n_q_heads;       /* H */
+  int32_t n_kv_heads;      /* H_kv; H % H_kv == 0 (query head h reads kv head h / (H/H_kv)) */
+  int32_t head_dim;        /* d_h, even */
+  int32_t n_groups;        /* G; H_kv % G == 0; group j holds kv heads [j*n_g, (j+1)*n_g) */
+  const int32_t* rank_k;   /* host [G]: rank of the key latent of each group, > 0 */
+  const int32_t* rank_v;   /* host [G]: rank of the value latent of each group, > 0 */
+  int32_t use_rope;        /* 1: rotary embedding on rebuilt keys and on the query; 0: none */
+  double rope_base;        /* theta_i = rope_base^(-2i/d_h); pairs (i, i + d_h/2) */
+  palu_dtype latent_dtype; /* F32 | F16 | BF16 | I4 */
+  palu_dtype act_dtype;    /* q, B_k, B_v, x, A_kv, out: F32 | F16 | BF16 */
+} palu_attn_desc;
+
+/* Caller-owned latent cache of one layer.  zk/zv (and sk/sv for I4) are
+ * device pointers laid out as described above. */
+typedef struct {
+  void* zk;                /* device: key latents (codes for I4) */
+  void* zv;                /* device: value latents (codes for I4) */
+  void* sk;                /* device: I4 key scales (binary16), else NULL */
+  void* sv;                /* device: I4 value scales (binary16), else NULL */
+  int32_t max_len;         /* tokens per (sequence, group) block, > 0 */
+} palu_latent_cache;
+
+/* Human-readable name of a status code (static string). */
+const char* palu_status_string(palu_status s);
+
+/* Detail of the last error returned on the calling thread (static per-thread
+ * buffer; empty string if none). */
+const char* palu_last_error(void);
+
+/* Bytes of one latent buffer of the layout above.  which: 0 = keys, 1 = values.
+ * scales: 0 = the latent (code) buffer, 1 = the I4 scale buffer.
+ * Returns 0 for an invalid descriptor. */
+size_t palu_latent_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len,
+                         int32_t which, int32_t scales);
+
+/* Byte offset of row t of (sequence b, group j) in a latent (scales = 0) or
+ * scale (scales = 1) buffer.  Returns -1 for invalid arguments. */
+int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t which,
+                           int32_t scales, int32_t b, int32_t j, int32_t t);
+
+/*
+ * palu_quant_latent - symmetric int4 quantisation of latent rows
+ * (quantization composing with the low-rank cache: arXiv 2407.21118v2
+ * abstract; PALU page, section "Rollout", route C).
+ *   z        device [n_rows] rows of r values of z_dtype (F32 | F16 | BF16),
+ *            row i starting at element i * z_row_stride (z_row_stride >= r)
+ *   codes    device [n_rows][16 * ceil(r/32)] bytes (output)
+ *   scales   device [n_rows][ceil(r/32)] binary16 (output)
+ * Per 32-element chunk: s = fp16(amax / 7) (binary32 divide, round to
+ * nearest even), code = clamp(rint(z / s), -7, 7) in binary32 with ties to
+ * even, code = 0 where s == 0.  Pad nibbles are written as zero.
+ * Errors: INVALID_ARG for null pointers, n_rows < 0, r <= 0, z_row_stride < r;
+ * UNSUPPORTED for z_dtype == I4.
+ */
+palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r,
+                              int64_t z_row_stride, void* codes, void* scales, hipStream_t stream);
+
+/*
+ * palu_project - prefill: write the latents of n_tok new tokens of sequence
+ * `seq` (PALU page, section "Inference flow", prefill steps 3-4: compute
+ * z_k = x A_k, z_v = x A_v and cache them instead of K/V).
+ *   x        device [n_tok][d_model] act_dtype
+ *   A_kv     device [sum r_k + sum r_v][d_model] act_dtype (layout above)
+ *   cache    latent buffers (host struct, device pointers); rows
+ *            pos0 .. pos0 + n_tok - 1 of every group of sequence `seq` are
+ *            written (int4 quantised when latent_dtype == I4, else rounded to
+ *            nearest even from the fp32 accumulation).
+ * Row padding of F32/F16/BF16 latents is written as zero; I4 pad nibbles are
+ * zero.  Rows of other sequences or positions are not touched.
+ * Errors: INVALID_ARG for null pointers, d_model <= 0, n_tok < 0, seq < 0,
+ * pos0 < 0, pos0 + n_tok > max_len, misaligned buffers (x, A_kv and latent
+ * buffers must be 16-byte aligned); UNSUPPORTED when latent_dtype is neither
+ * act_dtype nor I4, or d_model is not a multiple of 64.
+ */
+palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok,
+                         const void* A_kv, const palu_latent_cache* cache, int32_t seq, int32_t pos0,
+                         hipStream_t stream);
+
+/* Workspace bytes palu_decode_attn needs for `batch` sequences on the
+ * current device (0 for an invalid descriptor). */
+size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len);
+
+/*
+ * palu_decode_attn - one decode step of attention over the latent cache
+ * (PALU page, section "Inference flow", decode steps 1-3; section "Why the
+ * GPU kernel matters": the rebuild is fused into the attention kernel so that
+ * full K and V are never materialised).  For every sequence b and query head
+ * h (kv head c = h / (H/H_kv), group j = c / n_g):
+ *   K = z_k^j[0:L_b] B_k^j, V = z_v^j[0:L_b] B_v^j (columns of kv head c);
+ *   with use_rope, K rows are rotated by their cache index t and q_h by p_b;
+ *   out[b][h] = softmax(sm_scale * K q_h) V.
+ * Without RoPE the score uses the absorbed query (q_h B_k^T) against z_k and,
+ * in all cases, values enter as (softmax . z_v) . B_v; both equal the formula
+ * up to rounding.  Arithmetic is binary32 throughout.
+ *   q          device [batch][H][d_h] act_dtype
+ *   cache      latent buffers; rows [0, L_b) of each (b, j) are read
+ *   B_k, B_v   device, layout above, act_dtype
+ *   seq_lens   device int32 [batch]: L_b (clamped to [0, max_len]); L_b == 0
+ *              gives a zero output row
+ *   q_pos      device int32 [batch]: RoPE position of the query, or NULL for
+ *              L_b - 1 (the new token's latent already appended)
+ *   sm_scale   score scale, typically 1/sqrt(d_h); finite
+ *   out        device [batch][H][d_h] act_dtype
+ *   workspace  device, at least palu_decode_workspace_bytes(desc, batch,
+ *              cache->max_len) bytes, 256-byte aligned; contents are scratch
+ * Errors: INVALID_ARG for null pointers, batch < 0, head counts that do not
+ * divide, odd head_dim, rank <= 0, max_len <= 0, non-finite sm_scale,
+ * I4 scales missing; WORKSPACE_TOO_SMALL; UNSUPPORTED for shapes without a
+ * compiled kernel (palu_last_error names the reason).
+ */
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
+                             const void* B_k, const void* B_v, const int32_t* seq_lens,
+                             const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PALU_H_ */

@@ -1,0 +1,330 @@
+// C ABI of the Palu latent-cache library: argument validation, the latent
+// cache layout, launch planning and dispatch.  Every argument error is found
+// here, on the host, before anything is enqueued.
+#include "palu.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "decode.h"
+#include "project.h"
+#include "quant.h"
+
+using namespace palu;
+
+namespace {
+
+thread_local char g_err[512];
+
+palu_status fail(palu_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+palu_status ok() {
+  g_err[0] = 0;
+  return PALU_OK;
+}
+
+palu_status hip_fail(hipError_t e, const char* what) {
+  return fail(PALU_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t roundup(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Row pitch (bytes) of a latent row of rank r.
+int64_t row_pitch(palu_dtype dt, int r) {
+  switch (dt) {
+    case PALU_F32: return 4 * roundup(r, 4);
+    case PALU_F16:
+    case PALU_BF16: return 2 * roundup(r, 8);
+    case PALU_I4: return 16 * ((r + 31) / 32);
+  }
+  return -1;
+}
+int64_t scale_pitch(int r) { return 2 * ((r + 31) / 32); }
+
+bool valid_dtype(palu_dtype d) { return d == PALU_F32 || d == PALU_F16 || d == PALU_BF16 || d == PALU_I4; }
+
+palu_status check_desc(const palu_attn_desc* d) {
+  if (!d) return fail(PALU_ERR_INVALID_ARG, "desc is NULL");
+  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 || d->n_groups <= 0)
+    return fail(PALU_ERR_INVALID_ARG, "head counts, head_dim and n_groups must be positive");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(PALU_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  if (d->n_kv_heads % d->n_groups != 0)
+    return fail(PALU_ERR_INVALID_ARG, "n_kv_heads (%d) must be a multiple of n_groups (%d)", d->n_kv_heads,
+                d->n_groups);
+  if (d->head_dim % 2 != 0) return fail(PALU_ERR_INVALID_ARG, "head_dim must be even");
+  if (d->n_groups > kMaxGroups) return fail(PALU_ERR_UNSUPPORTED, "at most %d groups", kMaxGroups);
+  if (!d->rank_k || !d->rank_v) return fail(PALU_ERR_INVALID_ARG, "rank_k / rank_v is NULL");
+  for (int j = 0; j < d->n_groups; ++j)
+    if (d->rank_k[j] <= 0 || d->rank_v[j] <= 0) return fail(PALU_ERR_INVALID_ARG, "rank of group %d is not positive", j);
+  if (!valid_dtype(d->latent_dtype) || !valid_dtype(d->act_dtype) || d->act_dtype == PALU_I4)
+    return fail(PALU_ERR_INVALID_ARG, "invalid dtype");
+  if (d->use_rope && !(std::isfinite(d->rope_base) && d->rope_base > 0))
+    return fail(PALU_ERR_INVALID_ARG, "rope_base must be positive and finite");
+  return PALU_OK;
+}
+
+struct Layout {
+  int64_t pk[kMaxGroups], pv[kMaxGroups], spk[kMaxGroups], spv[kMaxGroups];
+  int64_t goff_k[kMaxGroups], goff_v[kMaxGroups], soff_k[kMaxGroups], soff_v[kMaxGroups];
+  int64_t seq_k, seq_v, seq_sk, seq_sv;   // bytes of one sequence block
+};
+
+void make_layout(const palu_attn_desc* d, int64_t max_len, Layout* L) {
+  int64_t ok_ = 0, ov = 0, osk = 0, osv = 0;
+  for (int j = 0; j < d->n_groups; ++j) {
+    L->pk[j] = row_pitch(d->latent_dtype, d->rank_k[j]);
+    L->pv[j] = row_pitch(d->latent_dtype, d->rank_v[j]);
+    L->spk[j] = d->latent_dtype == PALU_I4 ? scale_pitch(d->rank_k[j]) : 0;
+    L->spv[j] = d->latent_dtype == PALU_I4 ? scale_pitch(d->rank_v[j]) : 0;
+    L->goff_k[j] = ok_; L->goff_v[j] = ov; L->soff_k[j] = osk; L->soff_v[j] = osv;
+    ok_ += max_len * L->pk[j]; ov += max_len * L->pv[j];
+    osk += max_len * L->spk[j]; osv += max_len * L->spv[j];
+  }
+  L->seq_k = ok_; L->seq_v = ov; L->seq_sk = osk; L->seq_sv = osv;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute units of the current device (cached per device).
+std::atomic<int> g_cu[64];
+
+palu_status device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64) {
+    int c = g_cu[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *out = c; return PALU_OK; }
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (dev >= 0 && dev < 64) g_cu[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return PALU_OK;
+}
+
+struct DecodePlan {
+  DecodeKey key;
+  int P, rvp, qabs_stride, nq;
+  size_t hdr_bytes, rec_bytes, qabs_bytes, total;
+};
+
+Elt elt_of(palu_dtype d) { return d == PALU_F32 ? Elt::F32 : d == PALU_F16 ? Elt::F16 : Elt::BF16; }
+
+palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodePlan* pl) {
+  palu_status s = check_desc(d);
+  if (s != PALU_OK) return s;
+  if (batch < 0) return fail(PALU_ERR_INVALID_ARG, "batch must be >= 0");
+  if (max_len <= 0) return fail(PALU_ERR_INVALID_ARG, "max_len must be positive");
+  if (batch > kMaxBatch) return fail(PALU_ERR_UNSUPPORTED, "batch above %d", kMaxBatch);
+  if (d->latent_dtype == PALU_I4)
+    return fail(PALU_ERR_UNSUPPORTED, "int4 latents are not supported by palu_decode_attn yet");
+  if (d->latent_dtype != d->act_dtype)
+    return fail(PALU_ERR_UNSUPPORTED, "latent_dtype must equal act_dtype for float latents");
+  int rk_max = 0, rv_max = 0;
+  for (int j = 0; j < d->n_groups; ++j) {
+    rk_max = d->rank_k[j] > rk_max ? d->rank_k[j] : rk_max;
+    rv_max = d->rank_v[j] > rv_max ? d->rank_v[j] : rv_max;
+  }
+  const int ng = d->n_kv_heads / d->n_groups, qpk = d->n_q_heads / d->n_kv_heads;
+  pl->key = DecodeKey{elt_of(d->latent_dtype), d->head_dim, ng, qpk, rk_max, rv_max, d->use_rope != 0};
+  int rk_cap = 0, rv_cap = 0;
+  if (!decode_supported(pl->key, &rk_cap, &rv_cap))
+    return fail(PALU_ERR_UNSUPPORTED,
+                "no decode kernel for dtype %d, head_dim %d, %d kv heads per group, %d query heads per kv head, "
+                "ranks <= (%d, %d), rope %d",
+                (int)d->latent_dtype, d->head_dim, ng, qpk, rk_max, rv_max, d->use_rope);
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != PALU_OK) return s;
+  const int64_t tiles_bound = (int64_t)batch * ((max_len + kDecTile - 1) / kDecTile);
+  int64_t P = (cus + d->n_groups - 1) / d->n_groups;
+  if (P > tiles_bound) P = tiles_bound;
+  if (P < 1) P = 1;
+  pl->P = (int)P;
+  pl->nq = ng * qpk;
+  pl->rvp = (int)roundup(rv_cap, 16);
+  pl->qabs_stride = (int)roundup(rk_cap, 4);
+  pl->hdr_bytes = (size_t)roundup((int64_t)(batch + 1) * 4, 256);
+  pl->rec_bytes = (size_t)roundup((int64_t)d->n_groups * (P + batch) * pl->nq * (2 + pl->rvp) * 4, 256);
+  pl->qabs_bytes = d->use_rope ? 0 : (size_t)roundup((int64_t)batch * d->n_q_heads * pl->qabs_stride * 4, 256);
+  pl->total = pl->hdr_bytes + pl->rec_bytes + pl->qabs_bytes;
+  return PALU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* palu_status_string(palu_status s) {
+  switch (s) {
+    case PALU_OK: return "PALU_OK";
+    case PALU_ERR_INVALID_ARG: return "PALU_ERR_INVALID_ARG";
+    case PALU_ERR_UNSUPPORTED: return "PALU_ERR_UNSUPPORTED";
+    case PALU_ERR_WORKSPACE_TOO_SMALL: return "PALU_ERR_WORKSPACE_TOO_SMALL";
+    case PALU_ERR_HIP: return "PALU_ERR_HIP";
+  }
+  return "PALU_ERR_UNKNOWN";
+}
+
+const char* palu_last_error(void) { return g_err; }
+
+size_t palu_latent_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len, int32_t which,
+                         int32_t scales) {
+  if (check_desc(desc) != PALU_OK || batch < 0 || max_len <= 0 || (which != 0 && which != 1)) return 0;
+  if (scales && desc->latent_dtype != PALU_I4) return 0;
+  Layout L;
+  make_layout(desc, max_len, &L);
+  const int64_t per = scales ? (which ? L.seq_sv : L.seq_sk) : (which ? L.seq_v : L.seq_k);
+  return (size_t)(per * batch);
+}
+
+int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t which, int32_t scales, int32_t b,
+                           int32_t j, int32_t t) {
+  if (check_desc(desc) != PALU_OK || max_len <= 0 || (which != 0 && which != 1)) return -1;
+  if (b < 0 || j < 0 || j >= desc->n_groups || t < 0 || t >= max_len) return -1;
+  if (scales && desc->latent_dtype != PALU_I4) return -1;
+  Layout L;
+  make_layout(desc, max_len, &L);
+  if (scales)
+    return which ? b * L.seq_sv + L.soff_v[j] + t * L.spv[j] : b * L.seq_sk + L.soff_k[j] + t * L.spk[j];
+  return which ? b * L.seq_v + L.goff_v[j] + t * L.pv[j] : b * L.seq_k + L.goff_k[j] + t * L.pk[j];
+}
+
+palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r, int64_t z_row_stride,
+                              void* codes, void* scales, hipStream_t stream) {
+  if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (n_rows < 0 || r <= 0 || z_row_stride < r) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r / z_row_stride");
+  if (z_dtype == PALU_I4) return fail(PALU_ERR_UNSUPPORTED, "input must be F32, F16 or BF16");
+  if (!valid_dtype(z_dtype)) return fail(PALU_ERR_INVALID_ARG, "invalid dtype");
+  if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (n_rows == 0) return ok();
+  hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantiser launch");
+  return ok();
+}
+
+palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
+                         const palu_latent_cache* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
+  palu_status s = check_desc(desc);
+  if (s != PALU_OK) return s;
+  if (!x || !A_kv || !cache || !cache->zk || !cache->zv) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (d_model <= 0 || n_tok < 0 || seq < 0 || pos0 < 0) return fail(PALU_ERR_INVALID_ARG, "bad d_model/n_tok/seq/pos0");
+  if (cache->max_len <= 0) return fail(PALU_ERR_INVALID_ARG, "max_len must be positive");
+  if ((int64_t)pos0 + n_tok > cache->max_len) return fail(PALU_ERR_INVALID_ARG, "pos0 + n_tok exceeds max_len");
+  const bool quant = desc->latent_dtype == PALU_I4;
+  if (!quant && desc->latent_dtype != desc->act_dtype)
+    return fail(PALU_ERR_UNSUPPORTED, "latent_dtype must equal act_dtype or be I4");
+  if (quant && (!cache->sk || !cache->sv)) return fail(PALU_ERR_INVALID_ARG, "I4 scales are NULL");
+  if (d_model % 64 != 0) return fail(PALU_ERR_UNSUPPORTED, "d_model must be a multiple of 64");
+  if (!aligned16(x) || !aligned16(A_kv) || !aligned16(cache->zk) || !aligned16(cache->zv))
+    return fail(PALU_ERR_INVALID_ARG, "x, A_kv and latent buffers must be 16-byte aligned");
+  if (2 * desc->n_groups > kMaxLatentRows) return fail(PALU_ERR_UNSUPPORTED, "too many groups");
+  if (n_tok == 0) return ok();
+  Layout L;
+  make_layout(desc, cache->max_len, &L);
+  ProjectParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.A = A_kv;
+  p.zk = (uint8_t*)cache->zk; p.zv = (uint8_t*)cache->zv;
+  p.sk = (uint8_t*)cache->sk; p.sv = (uint8_t*)cache->sv;
+  p.n_tok = n_tok; p.d_model = d_model; p.pos0 = pos0;
+  p.G = desc->n_groups; p.seq = seq; p.quant = quant ? 1 : 0;
+  int64_t col = 0;
+  int max_rank = 0;
+  for (int j = 0; j < desc->n_groups; ++j) {
+    p.rank[j] = desc->rank_k[j]; p.col_off[j] = col; col += desc->rank_k[j];
+    max_rank = desc->rank_k[j] > max_rank ? desc->rank_k[j] : max_rank;
+  }
+  for (int j = 0; j < desc->n_groups; ++j) {
+    p.rank[desc->n_groups + j] = desc->rank_v[j]; p.col_off[desc->n_groups + j] = col; col += desc->rank_v[j];
+    max_rank = desc->rank_v[j] > max_rank ? desc->rank_v[j] : max_rank;
+  }
+  p.seq_bytes_k = L.seq_k; p.seq_bytes_v = L.seq_v; p.seq_sbytes_k = L.seq_sk; p.seq_sbytes_v = L.seq_sv;
+  for (int j = 0; j < desc->n_groups; ++j) {
+    p.goff_k[j] = L.goff_k[j]; p.goff_v[j] = L.goff_v[j];
+    p.soff_k[j] = L.soff_k[j]; p.soff_v[j] = L.soff_v[j];
+    p.pk[j] = (int)L.pk[j]; p.pv[j] = (int)L.pv[j];
+  }
+  hipError_t e = launch_project((int)desc->act_dtype, p, max_rank, stream);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return ok();
+}
+
+size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len) {
+  DecodePlan pl;
+  if (plan_decode(desc, batch, max_len, &pl) != PALU_OK) return 0;
+  return pl.total;
+}
+
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
+                             const void* B_k, const void* B_v, const int32_t* seq_lens, const int32_t* q_pos,
+                             int32_t batch, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  DecodePlan pl;
+  palu_status s = plan_decode(desc, batch, cache->max_len, &pl);
+  if (s != PALU_OK) return s;
+  if (!q || !B_k || !B_v || !seq_lens || !out || !cache->zk || !cache->zv)
+    return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (!std::isfinite(sm_scale)) return fail(PALU_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!aligned16(cache->zk) || !aligned16(cache->zv))
+    return fail(PALU_ERR_INVALID_ARG, "latent buffers must be 16-byte aligned");
+  if (batch == 0) return ok();
+  if (!workspace) return fail(PALU_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(PALU_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < pl.total)
+    return fail(PALU_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
+
+  Layout L;
+  make_layout(desc, cache->max_len, &L);
+  DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q; p.zk = (const uint8_t*)cache->zk; p.zv = (const uint8_t*)cache->zv;
+  p.Bk = B_k; p.Bv = B_v; p.seq_lens = seq_lens; p.q_pos = q_pos;
+  uint8_t* ws = (uint8_t*)workspace;
+  p.hdr = (int*)ws;
+  p.rec = (float*)(ws + pl.hdr_bytes);
+  p.qabs = desc->use_rope ? nullptr : (const float*)(ws + pl.hdr_bytes + pl.rec_bytes);
+  p.out = out;
+  p.batch = batch; p.max_len = cache->max_len; p.H = desc->n_q_heads; p.G = desc->n_groups; p.P = pl.P;
+  p.rvp = pl.rvp; p.rec_stride = pl.nq * (2 + pl.rvp); p.qabs_stride = pl.qabs_stride;
+  p.qscale = sm_scale * 1.4426950408889634f;
+  p.rope_base = desc->rope_base;
+  p.seq_bytes_k = L.seq_k; p.seq_bytes_v = L.seq_v;
+  const int w = (desc->n_kv_heads / desc->n_groups) * desc->head_dim;
+  int64_t bk = 0, bv = 0;
+  for (int j = 0; j < desc->n_groups; ++j) {
+    p.goff_k[j] = L.goff_k[j]; p.goff_v[j] = L.goff_v[j];
+    p.boff_k[j] = bk; p.boff_v[j] = bv;
+    bk += (int64_t)desc->rank_k[j] * w; bv += (int64_t)desc->rank_v[j] * w;
+    p.rk[j] = desc->rank_k[j]; p.rv[j] = desc->rank_v[j];
+    p.pk[j] = (int)L.pk[j]; p.pv[j] = (int)L.pv[j];
+  }
+  hipError_t e;
+  if (!desc->use_rope) {
+    e = launch_qabs(pl.key, p, stream);
+    if (e != hipSuccess) return hip_fail(e, "absorbed-query launch");
+  }
+  e = launch_decode(pl.key, p, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = launch_merge(pl.key, p, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+}  // extern "C"

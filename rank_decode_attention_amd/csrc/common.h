@@ -1,0 +1,79 @@
+// Device-side helpers shared by the gfx950 kernels of the Palu library.
+// CDNA4 only: 64-lane wavefronts, MFMA matrix cores, LDS DMA and LDS
+// transpose reads.  Lane layouts used below were checked on gfx950:
+//   v_mfma_f32_16x16x32_{f16,bf16}: A lane l -> row l%16, k = 8*(l/16)+[0..7];
+//     B lane l -> col l%16, same k; C lane l -> col l%16, rows 4*(l/16)+[0..3].
+//   v_mfma_f32_16x16x4_f32: A lane l -> row l%16, k = l/16; B col l%16, k = l/16.
+//   ds_read_b64_tr_b16: in each 16-lane group, source lane s = 4e+q addresses
+//     4 consecutive 16-bit elements (row e, columns 4q..4q+3) of a row-major
+//     tile; result lane i receives element i of rows e = 0..3.
+//   global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace palu {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define PALU_LDS __attribute__((address_space(3)))
+
+// 8 x 16-bit operand of a 16x16x32 MFMA, for element type T.
+template <class T> struct Vec8;
+template <> struct Vec8<_Float16> { typedef f16x8 type; };
+template <> struct Vec8<__bf16> { typedef bf16x8 type; };
+
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global -> LDS copy; `lds_wave_base` must be wave-uniform, lane l
+// writes bytes [16*l, 16*l+16) after it.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (PALU_LDS void*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+// Workgroup barrier without the memory fence of __syncthreads(): outstanding
+// LDS-DMA prefetches are not drained.  Callers order their own accesses.
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const void* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((PALU_LDS i16x4*)lds_addr);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+
+// Round-to-nearest-even conversions from binary32.
+template <class T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+template <class T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace palu

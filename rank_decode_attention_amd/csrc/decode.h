@@ -1,0 +1,53 @@
+// Host/device interface of the decode kernels (internal to the library).
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace palu {
+
+constexpr int kMaxGroups = 16;
+constexpr int kMaxBatch = 2048;  // sequences per call (tile prefix sums live in LDS)
+constexpr int kDecTile = 32;     // tokens per pipeline tile
+constexpr int kDecWaves = 8;     // waves per decode block (2 per SIMD)
+
+// Element types of a decode instantiation.
+enum class Elt : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct DecodeParams {
+  const void* q;            // [batch][H][DH]
+  const uint8_t* zk;        // latent buffers (cache layout)
+  const uint8_t* zv;
+  const void* Bk;           // concatenated B_k^j [r][w]
+  const void* Bv;
+  const int* seq_lens;      // [batch]
+  const int* q_pos;         // [batch] or null
+  const float* qabs;        // no-RoPE: [batch][H][qabs_stride] pre-scaled absorbed queries
+  int* hdr;                 // workspace: tile_start[batch + 1]
+  float* rec;               // workspace: split records
+  void* out;                // [batch][H][DH]
+  int batch, max_len, H, G, P;
+  int rec_stride;           // floats per record = NQ * (2 + rvp)
+  int rvp;                  // record row length (max value rank rounded up to 16)
+  int qabs_stride;
+  float qscale;             // sm_scale * log2(e)
+  double rope_base;
+  int64_t seq_bytes_k, seq_bytes_v;
+  int64_t goff_k[kMaxGroups], goff_v[kMaxGroups];   // byte offset of group block inside a sequence block
+  int64_t boff_k[kMaxGroups], boff_v[kMaxGroups];   // element offset of B^j inside B_k / B_v
+  int rk[kMaxGroups], rv[kMaxGroups];               // ranks
+  int pk[kMaxGroups], pv[kMaxGroups];               // row pitches in bytes
+};
+
+// Key of a compiled decode-attention instantiation.
+struct DecodeKey {
+  Elt elt; int head_dim; int kv_per_group; int q_per_kv; int rk_max; int rv_max; bool rope;
+};
+
+// Returns false if no compiled instantiation covers the key (rk_max / rv_max
+// are upper bounds that the chosen kernel must reach).
+bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap);
+hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_qabs(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_merge(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
+
+}  // namespace palu

@@ -1,0 +1,851 @@
+// Fused decode attention over the low-rank latent cache (gfx950).
+//
+// Method: PALU page, section "Low-rank projection decomposition" (formula
+// block: K = z_k B_k, V = z_v B_v) and section "Inference flow" (decode:
+// read the latents, rebuild or fuse, attend); arXiv 2407.21118v2 abstract
+// (keys and values rebuilt on the fly; RoPE-based attention; fused kernels).
+//
+// Design (ours; the pages give no kernel):
+//  * Work is the flattened list of 32-token tiles of all sequences (each
+//    sequence padded to a whole tile).  Block (g, p) takes the p-th equal
+//    share of the tiles of head-group g, so ragged batches balance exactly.
+//    Where a share crosses a sequence boundary the block closes a split
+//    record (m, l, acc) and opens the next; record index p + b is unique.
+//  * B_k^g stays in VGPRs for the whole block (loaded once through LDS with
+//    transpose reads); each wave owns 16 frequency rows of PPW heads in both
+//    RoPE halves, so the pair (i, i + d/2) of a rebuilt key sits in one lane.
+//  * Latent tiles stream HBM -> LDS with LDS DMA (global_load_lds_dwordx4),
+//    three buffers deep, XOR-swizzled for conflict-free MFMA operand reads.
+//  * K^T tile = B_k^T z_k^T on MFMA (16x16x32 for 16-bit, 16x16x4 for fp32),
+//    RoPE on the fp32 accumulator with angle recurrences seeded in fp64,
+//    scores by in-lane dots + a 4-lane reduction, online softmax in the log2
+//    domain, and acc += P z_v on MFMA with P split into hi + lo 16-bit parts
+//    (exact to ~2^-22) and z_v read through ds_read_b64_tr_b16.
+//  * Without RoPE the score is the absorbed query (q B_k^T, pre-computed per
+//    call, hi/lo split) against z_k on MFMA; K is never rebuilt.
+//  * A second kernel merges the split records and applies B_v per head.
+#include "common.h"
+#include "decode.h"
+
+#include <type_traits>
+
+namespace palu {
+
+template <class LT_, int DH_, int NG_, int QPK_, int NKC_, int RKMAX_, int RVMAX_, bool ROPE_>
+struct DecCfg {
+  typedef LT_ LT;
+  static constexpr bool F32 = std::is_same<LT, float>::value;
+  static constexpr int ESZ = sizeof(LT);
+  static constexpr int DH = DH_, NG = NG_, QPK = QPK_, NKC = NKC_;
+  static constexpr int RKMAX = RKMAX_, RVMAX = RVMAX_;
+  static constexpr bool ROPE = ROPE_;
+  static constexpr int TT = kDecTile, NW = kDecWaves, NT = 64 * kDecWaves;
+  static constexpr int NJ = DH / 32;                    // 16-row frequency blocks per head half
+  static constexpr int PPW = ROPE ? NG * NJ / NW : 0;   // kv heads per wave
+  static constexpr int RT = 2 * PPW;                    // 16-row MFMA tiles per wave
+  static constexpr int NQ = NG * QPK;                   // query heads per group
+  static constexpr int KC = F32 ? 16 : 32;              // k per operand chunk
+  static constexpr int W = NG * DH;                     // group width
+  static constexpr int CPRK = RKMAX * ESZ / 16, CPRV = RVMAX * ESZ / 16;
+  // LDS rows are padded so that consecutive token rows start 4 banks apart
+  // (keys, 16-byte MFMA operand reads) or 8 banks apart (values, 8-byte
+  // transpose reads); the pitch is fixed per instantiation so every operand
+  // address is one per-lane base plus a compile-time offset.
+  static constexpr int PITK = cdiv(CPRK, 8) * 8 + 1;    // key row pitch in 16-byte slots
+  static constexpr int PITV = cdiv(CPRV, 8) * 8 + 2;    // value row pitch in 16-byte slots
+  static constexpr int SLK = cdiv(TT * PITK, 64) * 64;  // 16-byte slots of the key region
+  static constexpr int SLV = cdiv(TT * PITV, 64) * 64;
+  static constexpr int NIK = cdiv(SLK, 64 * NW), NIV = cdiv(SLV, 64 * NW);
+  static constexpr int NDMA = NIK + NIV;                // DMA instructions per wave per tile
+  static constexpr int BUFB = (SLK + SLV) * 16;         // bytes per pipeline buffer
+  static constexpr int NNT = RVMAX / 16;                // value n-tiles
+  static constexpr int NNTW = cdiv(NNT, NW);
+  static constexpr int NSP = ROPE ? NJ : NW;            // partial-score slots per head
+  static constexpr int STG_ROWS = KC;                   // B_k rows staged per pass
+  static constexpr int NSI = cdiv(STG_ROWS * W * ESZ / 16, 64 * NW);  // DMA instr per wave per pass
+
+  static_assert(RKMAX % KC == 0 && RVMAX % 16 == 0, "rank caps");
+  static_assert(NKC * KC == RKMAX, "register chunks");
+  static_assert(!ROPE || (NG * NJ) % NW == 0, "wave mapping needs NG*DH/32 divisible by 8");
+  static_assert(!ROPE || NW % NJ == 0, "wave mapping");
+  static_assert(F32 ? NQ <= 16 : NQ <= 8, "query heads per group");
+  static_assert(STG_ROWS * W * ESZ <= BUFB, "B_k staging must fit one buffer");
+  static_assert(DH % 32 == 0, "head_dim");
+};
+
+// Operand registers of one 16x16xK MFMA input: 8 x 16-bit or 4 x fp32.
+template <class LT> struct Op { typedef typename Vec8<LT>::type type; };
+template <> struct Op<float> { typedef f32x4 type; };
+
+template <class LT>
+__device__ __forceinline__ f32x4 mma(const typename Op<LT>::type& a, const typename Op<LT>::type& b, f32x4 c) {
+  if constexpr (std::is_same<LT, float>::value) {
+    c = mfma16x16x4(a[0], b[0], c);
+    c = mfma16x16x4(a[1], b[1], c);
+    c = mfma16x16x4(a[2], b[2], c);
+    c = mfma16x16x4(a[3], b[3], c);
+    return c;
+  } else {
+    return mfma16x16x32(a, b, c);
+  }
+}
+
+// cos/sin of the angle t*theta: the product and its reduction to one turn are
+// done in fp64 (exact enough for t up to 2^31), then the hardware sin/cos,
+// which take their argument in turns, evaluate the reduced angle.
+__device__ __forceinline__ void sincos_angle(double t, double theta_turns, float* c, float* s) {
+  double rev = t * theta_turns;
+  rev -= rint(rev);
+  const float r = (float)rev;
+  *c = __builtin_amdgcn_cosf(r);
+  *s = __builtin_amdgcn_sinf(r);
+}
+
+template <class C>
+struct DecState {
+  typedef typename C::LT LT;
+  typedef typename Op<LT>::type op_t;
+  op_t breg[C::ROPE ? C::RT : 1][C::ROPE ? C::NKC : 1];   // B_k^T operand (RoPE path)
+  op_t aq[C::ROPE ? 1 : C::NKC];                          // absorbed query operand (no-RoPE path)
+  float qr[C::ROPE ? C::PPW : 1][C::QPK][2][4];           // rotated, pre-scaled query values
+  float cs[4], sn[4];                                     // angle at the current tile (u = 0)
+  float c16[4], s16[4];                                   // rotation by 16 tokens
+  f32x4 acc[C::NNTW];                                     // P z_v accumulators
+  float m_run, l_run;
+  int L;                                                  // history length of the current sequence
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParams p) {
+  typedef typename C::LT LT;
+  typedef typename Op<LT>::type op_t;
+  __shared__ uint4 buf0[C::BUFB / 16];
+  __shared__ uint4 buf1[C::BUFB / 16];
+  __shared__ uint4 buf2[C::BUFB / 16];
+  __shared__ uint4 dummy[64];
+  __shared__ float spart[2 * C::NSP * C::NQ * C::TT];
+  __shared__ int tstart[kMaxBatch + 1];
+  __shared__ int slen[kMaxBatch];
+  __shared__ int wsum[C::NW];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int g = blockIdx.x % p.G, pb = blockIdx.x / p.G;
+  const int batch = p.batch;
+
+  // ---------------------------------------------------------------- tile prefix sums
+  {
+    // each thread scans up to 4 consecutive sequences, then a block scan
+    const int per = cdiv(batch, C::NT);
+    int loc[4];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int bb = tid * per + i;
+      int v = 0;
+      if (i < per && bb < batch) {
+        int L = p.seq_lens[bb];
+        L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
+        slen[bb] = L;
+        v = cdiv(L, C::TT);
+      }
+      loc[i] = v;
+      s += v;
+    }
+    // inclusive wave scan of s
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int o = __shfl_up(incl, d, 64);
+      if (l >= d) incl += o;
+    }
+    if (l == 63) wsum[w] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int i = 0; i < w; ++i) wbase += wsum[i];
+    int run = wbase + incl - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int bb = tid * per + i;
+      if (i < per && bb < batch) tstart[bb] = run;
+      run += loc[i];
+    }
+    if (tid == C::NT - 1) tstart[batch] = run;
+    __syncthreads();
+  }
+  const int total = tstart[batch];
+  if (g == 0 && pb == 0) {
+    for (int i = tid; i <= batch; i += C::NT) p.hdr[i] = tstart[i];
+  }
+  const int tpb = cdiv(total, p.P);
+  const int n_begin = pb * tpb;
+  const int n_end = min(total, n_begin + tpb);
+  if (n_begin >= n_end) return;
+
+  const int rk = p.rk[g], rv = p.rv[g];
+  const int pk = p.pk[g], pv = p.pv[g];
+  const int cprk = pk >> 4, cprv = pv >> 4;
+  const int nkc = cdiv(rk, C::KC);
+  const int nnt = cdiv(rv, 16);
+
+  DecState<C> st;
+
+  // ---------------------------------------------------------------- per-lane DMA slot geometry
+  // slot (row, pos) of each DMA instruction is fixed for the block; only the
+  // sequence base and tile start change per tile.
+  // Slot q of a region holds chunk (q % PIT) of token row (q / PIT); slots
+  // past the row's data (padding) load a valid chunk that is never read.
+  int dk_geo[C::NIK], dv_geo[C::NIV];   // (row << 16) | byte offset inside the row
+#pragma unroll
+  for (int m = 0; m < C::NIK; ++m) {
+    const int slot = (m * C::NW + w) * 64 + l;
+    int row = slot / C::PITK, pos = slot - row * C::PITK;
+    row = row < C::TT ? row : C::TT - 1;
+    pos = pos < cprk ? pos : 0;
+    dk_geo[m] = (row << 16) | (pos * 16);
+  }
+#pragma unroll
+  for (int m = 0; m < C::NIV; ++m) {
+    const int slot = (m * C::NW + w) * 64 + l;
+    int row = slot / C::PITV, pos = slot - row * C::PITV;
+    row = row < C::TT ? row : C::TT - 1;
+    pos = pos < cprv ? pos : 0;
+    dv_geo[m] = (row << 16) | (pos * 16);
+  }
+  const uint8_t* zk_seq = p.zk + p.goff_k[g];
+  const uint8_t* zv_seq = p.zv + p.goff_v[g];
+  const int64_t sbk = p.seq_bytes_k, sbv = p.seq_bytes_v;
+
+  // locate the sequence holding tile n (n >= tstart[b0]); returns b
+  auto seq_of = [&](int n, int b0) __attribute__((always_inline)) {
+    int b = b0;
+    while (tstart[b + 1] <= n) ++b;
+    return b;
+  };
+  auto seq_len = [&](int b) { return slen[b]; };
+
+  auto issue_tile = [&](uint4* bufp, int b, int t0, int L) __attribute__((always_inline)) {
+    const uint8_t* kb = zk_seq + (int64_t)b * sbk;
+    const uint8_t* vb = zv_seq + (int64_t)b * sbv;
+#pragma unroll
+    for (int m = 0; m < C::NIK; ++m) {
+      int sbase = (m * C::NW + w) * 64;
+      int tg = min(t0 + (dk_geo[m] >> 16), L - 1);
+      void* dst = sbase < C::SLK ? (void*)(bufp + sbase) : (void*)dummy;
+      dma16(kb + (int64_t)tg * pk + (dk_geo[m] & 0xFFFF), dst);
+    }
+#pragma unroll
+    for (int m = 0; m < C::NIV; ++m) {
+      int sbase = (m * C::NW + w) * 64;
+      int tg = min(t0 + (dv_geo[m] >> 16), L - 1);
+      void* dst = sbase < C::SLV ? (void*)(bufp + C::SLK + sbase) : (void*)dummy;
+      dma16(vb + (int64_t)tg * pv + (dv_geo[m] & 0xFFFF), dst);
+    }
+  };
+
+  // rotation frequencies theta_f = base^(-2f/DH), stored in turns per token
+  __shared__ double theta_lds[C::DH / 2];
+  if (tid < C::DH / 2) theta_lds[tid] = exp2(-(2.0 * tid / C::DH) * log2(p.rope_base)) * 0.15915494309189535;
+  __syncthreads();
+  auto rope_theta = [&](int f) __attribute__((always_inline)) { return theta_lds[f]; };
+
+  // ---------------------------------------------------------------- B_k^g into registers (RoPE path)
+  const int jf = w % C::NJ;                       // frequency block of this wave
+  const int cbase = C::ROPE ? (w / C::NJ) * C::PPW : 0;   // first local kv head of this wave
+  if constexpr (C::ROPE) {
+    const LT* Bg = (const LT*)p.Bk + p.boff_k[g];
+    constexpr int STG_SLOTS = C::STG_ROWS * C::W * C::ESZ / 16;
+    auto stage = [&](uint4* bufp, int kc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < C::NSI; ++m) {
+        int sbase = (m * C::NW + w) * 64;
+        int slot = sbase + l;
+        slot = slot < STG_SLOTS ? slot : STG_SLOTS - 1;
+        int e0 = slot * (16 / C::ESZ);              // element index in the staged block
+        int row = e0 / C::W, col = e0 - row * C::W;
+        int kr = kc * C::KC + row;
+        kr = kr < rk ? kr : rk - 1;
+        void* dst = sbase < STG_SLOTS ? (void*)(bufp + sbase) : (void*)dummy;
+        dma16(Bg + (int64_t)kr * C::W + col, dst);
+      }
+    };
+    auto gather = [&](const uint4* bufp, int kc) __attribute__((always_inline)) {
+      const LT* sb = (const LT*)bufp;
+      const int kq = l >> 4, s = l & 15;
+#pragma unroll
+      for (int rt = 0; rt < C::RT; ++rt) {
+        const int x = rt >> 1, half = rt & 1;
+        const int i0 = (cbase + x) * C::DH + half * (C::DH / 2) + 16 * jf;
+        op_t v;
+        if constexpr (C::F32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int krow = 4 * kq + e;
+            float val = sb[krow * C::W + i0 + s];
+            v[e] = (kc * C::KC + krow) < rk ? val : 0.f;
+          }
+        } else {
+          i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * C::W + i0 + 4 * (s & 3));
+          i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * C::W + i0 + 4 * (s & 3));
+          typedef short s8 __attribute__((ext_vector_type(8)));
+          s8 both;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            both[e] = (kc * C::KC + 8 * kq + e) < rk ? lo[e] : (short)0;
+            both[e + 4] = (kc * C::KC + 8 * kq + 4 + e) < rk ? hi[e] : (short)0;
+          }
+          v = __builtin_bit_cast(op_t, both);
+        }
+        st.breg[rt][kc] = v;
+      }
+    };
+    // three-deep staging pipeline over the NKC chunks of B_k rows
+    stage(buf0, 0);
+    if (1 < nkc) stage(buf1, 1);
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc) {
+      if (kc < nkc) {
+        if (kc + 1 < nkc) wait_vmcnt<C::NSI>(); else wait_vmcnt<0>();
+        barrier();
+        if (kc + 2 < nkc) {
+          if ((kc + 2) % 3 == 0) stage(buf0, kc + 2);
+          else if ((kc + 2) % 3 == 1) stage(buf1, kc + 2);
+          else stage(buf2, kc + 2);
+        }
+        if (kc % 3 == 0) gather(buf0, kc);
+        else if (kc % 3 == 1) gather(buf1, kc);
+        else gather(buf2, kc);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < C::RT; ++rt) st.breg[rt][kc] = op_t{};
+      }
+    }
+    wait_lgkm0();
+    barrier();   // staging buffers free before tile DMA overwrites them
+
+    // frequencies of this lane's 4 rows and the 16/32-token rotation steps
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int f = 16 * jf + 4 * (l >> 4) + e;
+      sincos_angle(16.0, rope_theta(f), &st.c16[e], &st.s16[e]);
+    }
+  }
+
+  // ---------------------------------------------------------------- pipeline
+  int b_dma = seq_of(n_begin, 0);
+  auto issue_n = [&](uint4* bufp, int n) __attribute__((always_inline)) {
+    b_dma = seq_of(n, b_dma);
+    issue_tile(bufp, b_dma, (n - tstart[b_dma]) * C::TT, seq_len(b_dma));
+  };
+  issue_n(buf0, n_begin);
+  if (n_begin + 1 < n_end) issue_n(buf1, n_begin + 1);
+
+  st.L = 0;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int i = 0; i < C::NNTW; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int bcur = seq_of(n_begin, 0);
+
+  auto step = [&](const uint4* bufp, int n, int parity) __attribute__((always_inline)) {
+    // ---- segment bookkeeping
+    bcur = seq_of(n, bcur);
+    const int b = bcur;
+    const bool seg_start = (n == n_begin) || (n == tstart[b]);
+    const bool seg_end = (n == n_end - 1) || (n + 1 == tstart[b + 1]);
+    const int t0 = (n - tstart[b]) * C::TT;
+    if (seg_start) {
+      st.L = seq_len(b);
+      const int pos = p.q_pos ? p.q_pos[b] : st.L - 1;
+      if constexpr (C::ROPE) {
+        const LT* qb = (const LT*)p.q + (int64_t)b * p.H * C::DH;
+        float qc[4], qs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sincos_angle((double)pos, rope_theta(16 * jf + 4 * (l >> 4) + e), &qc[e], &qs[e]);
+#pragma unroll
+        for (int x = 0; x < C::PPW; ++x)
+#pragma unroll
+          for (int qq = 0; qq < C::QPK; ++qq) {
+            const int h = (g * C::NG + cbase + x) * C::QPK + qq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int f = 16 * jf + 4 * (l >> 4) + e;
+              float qlo = to_f32(qb[h * C::DH + f]);
+              float qhi = to_f32(qb[h * C::DH + f + C::DH / 2]);
+              st.qr[x][qq][0][e] = (qlo * qc[e] - qhi * qs[e]) * p.qscale;
+              st.qr[x][qq][1][e] = (qlo * qs[e] + qhi * qc[e]) * p.qscale;
+            }
+          }
+      } else {
+        const int kq = l >> 4, row = l & 15;
+        const int hq = C::F32 ? row : (row & 7);
+        const bool lo_part = !C::F32 && row >= 8;
+        const bool valid = hq < C::NQ;
+        const float* qa = p.qabs + ((int64_t)b * p.H + g * C::NQ + (valid ? hq : 0)) * p.qabs_stride;
+#pragma unroll
+        for (int kc = 0; kc < C::NKC; ++kc) {
+          op_t v;
+          if constexpr (C::F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              int k = kc * C::KC + 4 * kq + e;
+              v[e] = (valid && k < rk) ? qa[k] : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              int k = kc * C::KC + 8 * kq + e;
+              float val = (valid && k < rk) ? qa[k] : 0.f;
+              LT hi = from_f32<LT>(val);
+              LT lo = from_f32<LT>(val - to_f32(hi));
+              v[e] = lo_part ? lo : hi;
+            }
+          }
+          st.aq[kc] = v;
+        }
+      }
+    }
+    if constexpr (C::ROPE) {
+      if (seg_start || ((n - n_begin) & 63) == 0) {
+        // exact seeding of the angle recurrence at this tile's first token
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sincos_angle((double)(t0 + (l & 15)), rope_theta(16 * jf + 4 * (l >> 4) + e), &st.cs[e], &st.sn[e]);
+      }
+    }
+
+    const uint8_t* zkt = (const uint8_t*)bufp;
+    const uint8_t* zvt = (const uint8_t*)(bufp + C::SLK);
+    float* sp = spart + parity * (C::NSP * C::NQ * C::TT);
+    const int kq = l >> 4, tl = l & 15;
+
+    // ---- scores
+    if constexpr (C::ROPE) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4 cacc[C::RT];
+#pragma unroll
+        for (int rt = 0; rt < C::RT; ++rt) cacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = 16 * u + tl;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kc = 0; kc < C::NKC; ++kc) {
+          if (kc < nkc) {
+            // k >= r_k multiplies zero rows of B_k (row padding is finite)
+            op_t bop = *(const op_t*)(zkt + (t * C::PITK + 4 * kc + kq) * 16);
+#pragma unroll
+            for (int rt = 0; rt < C::RT; ++rt) cacc[rt] = mma<LT>(st.breg[rt][kc], bop, cacc[rt]);
+          }
+        }
+        // RoPE on the accumulator: lane holds token t, rows f_e of both halves
+        float c[4], s[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (u == 0) { c[e] = st.cs[e]; s[e] = st.sn[e]; }
+          else {
+            c[e] = st.cs[e] * st.c16[e] - st.sn[e] * st.s16[e];
+            s[e] = st.sn[e] * st.c16[e] + st.cs[e] * st.s16[e];
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < C::PPW; ++x) {
+          float klo[4], khi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float a = cacc[2 * x][e], bb = cacc[2 * x + 1][e];
+            klo[e] = a * c[e] - bb * s[e];
+            khi[e] = a * s[e] + bb * c[e];
+          }
+#pragma unroll
+          for (int qq = 0; qq < C::QPK; ++qq) {
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              part = fmaf(st.qr[x][qq][0][e], klo[e], part);
+              part = fmaf(st.qr[x][qq][1][e], khi[e], part);
+            }
+            part += shfl_xor(part, 16);
+            part += shfl_xor(part, 32);
+            const int hq = (cbase + x) * C::QPK + qq;
+            if (kq == 0) sp[(jf * C::NQ + hq) * C::TT + t] = part;
+          }
+        }
+      }
+      // advance the angle recurrence by one tile
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // rotation by 32 tokens = the 16-token rotation applied twice
+        const float c32 = st.c16[e] * st.c16[e] - st.s16[e] * st.s16[e];
+        const float s32 = 2.f * st.c16[e] * st.s16[e];
+        float c2 = st.cs[e] * c32 - st.sn[e] * s32;
+        float s2 = st.sn[e] * c32 + st.cs[e] * s32;
+        st.cs[e] = c2; st.sn[e] = s2;
+      }
+    } else {
+      // absorbed query: wave w sums chunks w, w + NW, ...
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4 cacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = 16 * u + tl;
+#pragma unroll
+        for (int kc = 0; kc < C::NKC; ++kc) {
+          if ((kc % C::NW) == w && kc < nkc) {
+            op_t bop = *(const op_t*)(zkt + (t * C::PITK + 4 * kc + kq) * 16);
+            cacc = mma<LT>(st.aq[kc], bop, cacc);
+          }
+        }
+        if constexpr (!C::F32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cacc[e] += shfl_xor(cacc[e], 32);   // hi + lo rows
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int hq = 4 * kq + e;
+          const bool wr = C::F32 ? (hq < C::NQ) : (kq < 2 && hq < C::NQ);
+          if (wr) sp[(w * C::NQ + hq) * C::TT + t] = cacc[e];
+        }
+      }
+    }
+    wait_lgkm0();
+    barrier();
+
+    // ---- online softmax (every wave, redundantly) in the P-operand layout
+    const int row = l & 15;
+    const int hq = C::F32 ? row : (row & 7);
+    const bool lo_part = !C::F32 && row >= 8;
+    const bool hvalid = hq < C::NQ;
+    float sc[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int tt = C::F32 ? (kq + 4 * x) : (8 * kq + x);
+      float v = 0.f;
+      if (hvalid) {
+#pragma unroll
+        for (int j = 0; j < C::NSP; ++j) v += sp[(j * C::NQ + hq) * C::TT + tt];
+      }
+      const bool tvalid = hvalid && (t0 + tt < st.L);
+      sc[x] = tvalid ? v : -INFINITY;
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int x = 1; x < 8; ++x) tmax = fmaxf(tmax, sc[x]);
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    float alpha = 1.f, m_new = st.m_run;
+    float pr[8];
+    if (hvalid) {
+      m_new = fmaxf(st.m_run, tmax);
+      alpha = exp2f(st.m_run - m_new);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pr[x] = exp2f(sc[x] - m_new);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pr[x] = 0.f;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) psum += pr[x];
+    psum += shfl_xor(psum, 16);
+    psum += shfl_xor(psum, 32);
+    st.l_run = st.l_run * alpha + psum;
+    st.m_run = m_new;
+
+    // alpha of the accumulator rows held by this lane (rows 4*kq + e)
+    float arow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) arow[e] = shfl(alpha, 4 * kq + e);
+
+    // ---- acc += P z_v
+    if constexpr (C::F32) {
+#pragma unroll
+      for (int i = 0; i < C::NNTW; ++i) {
+        const int nt = w + i * C::NW;
+        if (nt < nnt) {
+          f32x4 a = st.acc[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] *= arow[e];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int tt = kq + 4 * x;
+            const int col = 16 * nt + row;
+            float zvv = *(const float*)(zvt + tt * C::PITV * 16 + col * 4);
+            a = mfma16x16x4(pr[x], zvv, a);
+          }
+          st.acc[i] = a;
+        }
+      }
+    } else {
+      op_t pop;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        LT hi = from_f32<LT>(pr[x]);
+        LT lo = from_f32<LT>(pr[x] - to_f32(hi));
+        pop[x] = lo_part ? lo : hi;
+      }
+      const int s = l & 15;
+#pragma unroll
+      for (int i = 0; i < C::NNTW; ++i) {
+        const int nt = w + i * C::NW;
+        if (nt < nnt) {
+          f32x4 a = st.acc[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] *= arow[e];
+          // rows (tokens) 8kq + s/4 (+4), columns 16 nt + 4 (s%4) .. +3
+          const int ta = 8 * kq + (s >> 2), tb = ta + 4;
+          const int colb = (16 * nt + 4 * (s & 3)) * 2;
+          i16x4 va = ds_read_tr16(zvt + ta * C::PITV * 16 + colb);
+          i16x4 vb = ds_read_tr16(zvt + tb * C::PITV * 16 + colb);
+          typedef short s8 __attribute__((ext_vector_type(8)));
+          s8 both = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+          a = mfma16x16x32(pop, __builtin_bit_cast(op_t, both), a);
+          st.acc[i] = a;
+        }
+      }
+    }
+
+    // ---- close the split record at the end of a segment
+    if (seg_end) {
+      const int k = pb + b;
+      float* rec = p.rec + ((int64_t)g * (p.P + batch) + k) * p.rec_stride;
+      float* racc = rec + 2 * C::NQ;
+#pragma unroll
+      for (int i = 0; i < C::NNTW; ++i) {
+        const int nt = w + i * C::NW;
+        if (nt < nnt) {
+          f32x4 a = st.acc[i];
+          if constexpr (!C::F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] += shfl_xor(a[e], 32);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int hrow = 4 * kq + e;
+            const bool wr = C::F32 ? (hrow < C::NQ) : (kq < 2 && hrow < C::NQ);
+            if (wr) racc[hrow * p.rvp + 16 * nt + (l & 15)] = a[e];
+          }
+        }
+      }
+      if (w == 0 && kq == 0 && hvalid && !lo_part) {
+        rec[2 * hq] = st.m_run;
+        rec[2 * hq + 1] = st.l_run;
+      }
+      st.m_run = -INFINITY;
+      st.l_run = 0.f;
+#pragma unroll
+      for (int i = 0; i < C::NNTW; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // Each step: wait for this wave's DMA of tile n, barrier (everyone's data
+  // landed, everyone finished the previous tile), prefetch tile n + 2 into the
+  // buffer freed by tile n - 1, then compute tile n.
+  for (int n = n_begin; n < n_end; n += 3) {
+#pragma unroll
+    for (int ph = 0; ph < 3; ++ph) {
+      const int nn = n + ph;
+      if (nn < n_end) {
+        if (nn + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
+        barrier();
+        if (nn + 2 < n_end) {
+          if (ph == 0) issue_n(buf2, nn + 2);
+          else if (ph == 1) issue_n(buf0, nn + 2);
+          else issue_n(buf1, nn + 2);
+        }
+        const int parity = (nn - n_begin) & 1;
+        if (ph == 0) step(buf0, nn, parity);
+        else if (ph == 1) step(buf1, nn, parity);
+        else step(buf2, nn, parity);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ absorbed query
+// qabs[b][h][k] = qscale * sum_d B_k^g[k][c*DH + d] q[b][h][d]   (k < r_k, else 0)
+template <class LT, int DH>
+__global__ void __launch_bounds__(256) palu_qabs_kernel(const DecodeParams p, int nq, int qpk, int ng) {
+  const int b = blockIdx.y, h = blockIdx.x;
+  const int g = h / nq;
+  const int c = (h % nq) / qpk;
+  const int rk = p.rk[g];
+  __shared__ float qs[DH];
+  const LT* qb = (const LT*)p.q + ((int64_t)b * p.H + h) * DH;
+  for (int d = threadIdx.x; d < DH; d += blockDim.x) qs[d] = to_f32(qb[d]);
+  __syncthreads();
+  const LT* Bg = (const LT*)p.Bk + p.boff_k[g];
+  const int w = ng * DH;
+  float* out = (float*)p.qabs + ((int64_t)b * p.H + h) * p.qabs_stride;
+  for (int k = threadIdx.x; k < p.qabs_stride; k += blockDim.x) {
+    float s = 0.f;
+    if (k < rk) {
+      const LT* row = Bg + (int64_t)k * w + c * DH;
+#pragma unroll 8
+      for (int d = 0; d < DH; ++d) s = fmaf(to_f32(row[d]), qs[d], s);
+    }
+    out[k] = s * p.qscale;
+  }
+}
+
+// ------------------------------------------------------------------ merge + B_v
+// One block per (group, sequence): combine the split records of the sequence
+// (m* = max m_i, l* = sum l_i 2^(m_i - m*), a = sum acc_i 2^(m_i - m*) / l*)
+// and write out[b][h][:] = a_h . B_v^g[:, c(h)*DH : (c(h)+1)*DH].
+template <class LT, int DH>
+__global__ void __launch_bounds__(256) palu_merge_kernel(const DecodeParams p, int nq, int qpk, int ng) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int rv = p.rv[g];
+  extern __shared__ float smem[];
+  float* a = smem;                      // [nq][rvp]
+  float* wgt = smem + nq * p.rvp;       // [P][nq] record weights
+  LT* out = (LT*)p.out + (int64_t)b * p.H * DH + (int64_t)g * nq * DH;
+
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
+  const int ts = p.hdr[b], te = p.hdr[b + 1], total = p.hdr[p.batch];
+  if (L == 0 || te <= ts) {
+    for (int i = tid; i < nq * DH; i += blockDim.x) out[i] = from_f32<LT>(0.f);
+    return;
+  }
+  const int tpb = cdiv(total, p.P);
+  const int p0 = ts / tpb, p1 = (te - 1) / tpb;
+  const int nrec = p1 - p0 + 1;           // <= P
+  const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + p0 + b) * p.rec_stride;
+
+  for (int h = tid; h < nq; h += blockDim.x) {
+    float m = -INFINITY;
+    for (int i = 0; i < nrec; ++i) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * h]);
+    float ls = 0.f;
+    for (int i = 0; i < nrec; ++i) {
+      const float* r = recs + (int64_t)i * p.rec_stride;
+      ls += r[2 * h + 1] * exp2f(r[2 * h] - m);
+    }
+    const float inv = 1.f / ls;
+    for (int i = 0; i < nrec; ++i) {
+      const float* r = recs + (int64_t)i * p.rec_stride;
+      wgt[i * nq + h] = exp2f(r[2 * h] - m) * inv;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nq * rv; idx += blockDim.x) {
+    const int h = idx / rv, r = idx - h * rv;
+    float s = 0.f;
+    for (int i = 0; i < nrec; ++i)
+      s = fmaf(recs[(int64_t)i * p.rec_stride + 2 * nq + h * p.rvp + r], wgt[i * nq + h], s);
+    a[h * p.rvp + r] = s;
+  }
+  __syncthreads();
+  const LT* Bv = (const LT*)p.Bv + p.boff_v[g];
+  const int w = ng * DH;
+  for (int idx = tid; idx < nq * DH; idx += blockDim.x) {
+    const int h = idx / DH, d = idx - h * DH;
+    const int c = h / qpk;
+    const float* ah = a + h * p.rvp;
+    const LT* col = Bv + c * DH + d;
+    float s = 0.f;
+    for (int r = 0; r < rv; ++r) s = fmaf(ah[r], to_f32(col[(int64_t)r * w]), s);
+    out[idx] = from_f32<LT>(s);
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+template <class C>
+hipError_t launch_cfg(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(palu_decode_kernel<C>, dim3(p.G * p.P), dim3(C::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+struct Entry {
+  DecodeKey key;
+  hipError_t (*decode)(const DecodeParams&, hipStream_t);
+};
+
+#define PALU_DEC(LTT, ELT, DH, NG, QPK, NKC, RK, RV, ROPE) \
+  Entry{DecodeKey{ELT, DH, NG, QPK, RK, RV, ROPE}, &launch_cfg<DecCfg<LTT, DH, NG, QPK, NKC, RK, RV, ROPE>>}
+
+static const Entry kEntries[] = {
+    // fp32 latents: 16-k chunks (head_dim 64, groups of 4 kv heads)
+    PALU_DEC(float, Elt::F32, 64, 4, 1, 8, 128, 128, true),
+    PALU_DEC(float, Elt::F32, 64, 4, 1, 8, 128, 128, false),
+    // 16-bit latents, head_dim 128, groups of 4 kv heads, MHA
+    PALU_DEC(_Float16, Elt::F16, 128, 4, 1, 8, 256, 256, true),
+    PALU_DEC(_Float16, Elt::F16, 128, 4, 1, 8, 256, 256, false),
+    PALU_DEC(__bf16, Elt::BF16, 128, 4, 1, 8, 256, 256, true),
+    PALU_DEC(__bf16, Elt::BF16, 128, 4, 1, 8, 256, 256, false),
+    // GQA: groups of 2 kv heads, 4 query heads per kv head, ranks up to 320
+    PALU_DEC(__bf16, Elt::BF16, 128, 2, 4, 10, 320, 320, true),
+    PALU_DEC(__bf16, Elt::BF16, 128, 2, 4, 10, 320, 320, false),
+    PALU_DEC(_Float16, Elt::F16, 128, 2, 4, 10, 320, 320, true),
+    PALU_DEC(_Float16, Elt::F16, 128, 2, 4, 10, 320, 320, false),
+};
+
+static const Entry* find_entry(const DecodeKey& k) {
+  const Entry* best = nullptr;
+  for (const Entry& e : kEntries) {
+    const DecodeKey& c = e.key;
+    if (c.elt != k.elt || c.head_dim != k.head_dim || c.kv_per_group != k.kv_per_group ||
+        c.q_per_kv != k.q_per_kv || c.rope != k.rope)
+      continue;
+    if (c.rk_max < k.rk_max || c.rv_max < k.rv_max) continue;
+    if (!best || c.rk_max + c.rv_max < best->key.rk_max + best->key.rv_max) best = &e;
+  }
+  return best;
+}
+
+bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap) {
+  const Entry* e = find_entry(k);
+  if (!e) return false;
+  if (rk_cap) *rk_cap = e->key.rk_max;
+  if (rv_cap) *rv_cap = e->key.rv_max;
+  return true;
+}
+
+hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
+  const Entry* e = find_entry(k);
+  if (!e) return hipErrorInvalidValue;
+  return e->decode(p, stream);
+}
+
+template <class LT>
+static hipError_t launch_qabs_t(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
+  const int nq = k.kv_per_group * k.q_per_kv;
+  if (k.head_dim == 64)
+    hipLaunchKernelGGL((palu_qabs_kernel<LT, 64>), dim3(p.H, p.batch), dim3(256), 0, stream, p, nq, k.q_per_kv, k.kv_per_group);
+  else if (k.head_dim == 128)
+    hipLaunchKernelGGL((palu_qabs_kernel<LT, 128>), dim3(p.H, p.batch), dim3(256), 0, stream, p, nq, k.q_per_kv, k.kv_per_group);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_qabs(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
+  switch (k.elt) {
+    case Elt::F32: return launch_qabs_t<float>(k, p, stream);
+    case Elt::F16: return launch_qabs_t<_Float16>(k, p, stream);
+    case Elt::BF16: return launch_qabs_t<__bf16>(k, p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class LT>
+static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
+  const int nq = k.kv_per_group * k.q_per_kv;
+  const size_t smem = (size_t)(nq * p.rvp + p.P * nq) * sizeof(float);
+  if (k.head_dim == 64)
+    hipLaunchKernelGGL((palu_merge_kernel<LT, 64>), dim3(p.G, p.batch), dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
+  else if (k.head_dim == 128)
+    hipLaunchKernelGGL((palu_merge_kernel<LT, 128>), dim3(p.G, p.batch), dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
+  switch (k.elt) {
+    case Elt::F32: return launch_merge_t<float>(k, p, stream);
+    case Elt::F16: return launch_merge_t<_Float16>(k, p, stream);
+    case Elt::BF16: return launch_merge_t<__bf16>(k, p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace palu

@@ -1,0 +1,27 @@
+// Host interface of the prefill projection kernel (internal to the library).
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace palu {
+
+constexpr int kMaxLatentRows = 32;   // 2 * max groups
+
+struct ProjectParams {
+  const void* x;          // [n_tok][D]
+  const void* A;          // [n_lat][D]  (A transposed)
+  uint8_t* zk; uint8_t* zv; uint8_t* sk; uint8_t* sv;
+  int64_t n_tok, d_model, pos0;
+  int G, seq, quant;
+  int rank[kMaxLatentRows];       // keys of groups 0..G-1 then values
+  int64_t col_off[kMaxLatentRows];
+  int64_t seq_bytes_k, seq_bytes_v, seq_sbytes_k, seq_sbytes_v;
+  int64_t goff_k[kMaxLatentRows / 2], goff_v[kMaxLatentRows / 2];
+  int64_t soff_k[kMaxLatentRows / 2], soff_v[kMaxLatentRows / 2];
+  int pk[kMaxLatentRows / 2], pv[kMaxLatentRows / 2];
+};
+
+// dtype: 0 = fp32, 1 = fp16, 2 = bf16 (x, A and non-quantised latents)
+hipError_t launch_project(int dtype, const ProjectParams& p, int max_rank, hipStream_t stream);
+
+}  // namespace palu

@@ -1,0 +1,139 @@
+"""Shared helpers of the GPU parity tests: build device inputs for a workload
+from the seeded generators, run the library through its binding, build the
+matching fp64 oracle inputs, and compare.
+
+Tolerances (from the spec bar, stated in the design doc):
+  fp16 / bf16 outputs: max |gpu - ref| <= 2e-3 + half an ulp of the output
+  format at |ref| (the output is stored in that format), and
+  ||gpu - ref||_2 / ||ref||_2 <= 1e-2;
+  fp32 outputs: max-abs <= 1e-5 and relative <= 1e-5.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+import oracle
+import palu_inputs as PI
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+_ULP_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+
+
+def desc_of(wl: PI.Workload):
+    import rank_decode_attention_amd as R
+    r = PI.ranks(wl).tolist()
+    return R.AttnDesc(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_groups, r, r, use_rope=wl.use_rope,
+                      rope_base=wl.rope_base, latent_dtype=wl.latent, act_dtype=wl.act)
+
+
+def _torch_dtype(fmt: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[fmt]
+
+
+def to_device(arr: np.ndarray, fmt: str, device="cuda"):
+    """Upload an array in a stored format ('bf16' = uint16 bits) as a torch tensor."""
+    import torch
+    if fmt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def from_device(t) -> np.ndarray:
+    import torch
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype != torch.float32 else \
+        t.detach().cpu().numpy().astype(np.float64)
+
+
+def padded_rows(arr: np.ndarray, fmt: str, r: int) -> np.ndarray:
+    """[n][r] stored-format rows -> [n][pitch] bytes with zero row padding."""
+    import rank_decode_attention_amd as R
+    esz = 4 if fmt == "f32" else 2
+    pitch = R.row_pitch(fmt, r)
+    n = arr.shape[0]
+    out = np.zeros((n, pitch // esz), dtype=arr.dtype)
+    out[:, :r] = arr
+    return out.view(np.uint8)
+
+
+class LazyLatents:
+    """zk[j][b] / zv[j][b] in fp64 for the oracle, regenerated on demand."""
+
+    def __init__(self, wl: PI.Workload, which: str, j: int, lens: np.ndarray):
+        self.wl, self.which, self.j, self.lens = wl, which, j, lens
+
+    def __getitem__(self, b):
+        L = int(self.lens[b])
+        a = PI.latent(self.wl, self.which, b, self.j, n=max(L, 1))
+        return oracle.upcast(a, self.wl.latent)
+
+
+def build_decode_case(wl: PI.Workload, q_scale: float = 1.0, lens: Optional[np.ndarray] = None,
+                      device="cuda") -> Dict:
+    """Device inputs of one decode step of workload wl (fp16/bf16/fp32 latents)."""
+    import torch
+    import rank_decode_attention_amd as R
+    desc = desc_of(wl)
+    ranks = PI.ranks(wl)
+    lens = PI.lengths(wl) if lens is None else np.asarray(lens, dtype=np.int32)
+    q = PI.query(wl)
+    if q_scale != 1.0:
+        q = PI.to_format(oracle.upcast(q, wl.act).astype(np.float32) * np.float32(q_scale), wl.act)
+    Bk = [PI.factor(wl, "Bk", j) for j in range(wl.n_groups)]
+    Bv = [PI.factor(wl, "Bv", j) for j in range(wl.n_groups)]
+
+    def rows(which, b, j):
+        n = int(min(max(lens[b], 1), wl.max_len))
+        a = PI.latent(wl, "k" if which == 0 else "v", b, j, n=n)
+        return padded_rows(a, wl.latent, int(ranks[j]))
+
+    cache = R.fill_cache(desc, wl.batch, wl.max_len, rows, device=device)
+    catB = lambda Bs: to_device(np.concatenate([b.reshape(-1) for b in Bs]), wl.act, device)
+    ws = torch.empty(R.decode_workspace_bytes(desc, wl.batch, wl.max_len), dtype=torch.uint8, device=device)
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=_torch_dtype(wl.act), device=device)
+    return dict(wl=wl, desc=desc, cache=cache, q=to_device(q, wl.act, device), q_host=q, Bk=catB(Bk), Bv=catB(Bv),
+                Bk_host=Bk, Bv_host=Bv, lens=lens, seq_lens=torch.from_numpy(lens).to(device), ws=ws, out=out,
+                sm_scale=1.0 / math.sqrt(wl.head_dim))
+
+
+def run_decode(case: Dict, q_pos=None):
+    import torch
+    import rank_decode_attention_amd as R
+    R.palu_decode_attn(case["desc"], case["q"], case["cache"], case["Bk"], case["Bv"], case["seq_lens"], q_pos,
+                       case["sm_scale"], case["out"], case["ws"])
+    torch.cuda.synchronize()
+    return from_device(case["out"])
+
+
+def oracle_decode(case: Dict, heads: Optional[Sequence[Tuple[int, int]]] = None, q_pos=None) -> np.ndarray:
+    wl = case["wl"]
+    lens = case["lens"]
+    zk = [LazyLatents(wl, "k", j, lens) for j in range(wl.n_groups)]
+    zv = [LazyLatents(wl, "v", j, lens) for j in range(wl.n_groups)]
+    Bk = [oracle.upcast(b, wl.act) for b in case["Bk_host"]]
+    Bv = [oracle.upcast(b, wl.act) for b in case["Bv_host"]]
+    q = oracle.upcast(case["q_host"], wl.act)
+    return oracle.decode_attention(q, zk, zv, Bk, Bv, lens, q_pos, n_kv_heads=wl.n_kv_heads,
+                                   use_rope=wl.use_rope, rope_base=wl.rope_base, sm_scale=case["sm_scale"],
+                                   heads=heads)
+
+
+def half_ulp(ref: np.ndarray, fmt: str) -> np.ndarray:
+    mag = np.maximum(np.abs(ref), 2.0 ** -14)
+    return 0.5 * 2.0 ** (np.floor(np.log2(mag)) - _ULP_BITS[fmt])
+
+
+def compare(gpu: np.ndarray, ref: np.ndarray, fmt: str, what: str = "") -> Dict[str, float]:
+    atol, rtol = TOL[fmt]
+    err = np.abs(gpu - ref)
+    allow = atol + (half_ulp(ref, fmt) if fmt != "f32" else 0.0)
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+    stats = dict(max_abs=float(err.max()) if err.size else 0.0, rel=rel)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    bad = err > allow
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond tolerance, max_abs={stats['max_abs']:.3e}"
+    assert rel <= rtol, f"{what}: relative error {rel:.3e} > {rtol}"
+    return stats

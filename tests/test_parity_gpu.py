@@ -1,0 +1,108 @@
+"""GPU parity of palu_decode_attn against the fp64 oracle, through the C ABI.
+
+Small cases (the oracle computes every output): several 32-token tiles with
+ragged tails, empty and single-token histories, explicit query positions,
+peaked attention.  Full-size cases (the shapes the benchmark times, same
+launch configuration): sampled (sequence, head) outputs, each computed by the
+oracle on its own.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import palu_inputs as PI
+from palu_cases import build_decode_case, compare, oracle_decode, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(name, **over):
+    return PI.scaled(name, **over)
+
+
+SMALL = [
+    ("tiny", PI.workload("tiny"), None),
+    ("tiny_norope", PI.scaled("tiny", use_rope=False, name="tiny_norope"), None),
+    ("tiny_ragged", PI.scaled("tiny", batch=3, max_len=200, fixed_lengths=(200, 37, 1)), None),
+    ("7b_small", _small("llama2_7b", batch=3, max_len=320, fixed_lengths=(300, 1, 77)), None),
+    ("7b_small_norope", _small("llama2_7b", batch=2, max_len=256, fixed_lengths=(256, 45), use_rope=False), None),
+    ("long_small", _small("long_b4", batch=3, max_len=600, ragged=True), None),
+    ("gqa_rope_small", _small("gqa_rope", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
+    ("gqa_norope_small", _small("gqa_norope", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
+    ("7b_f16_gqa_shape", PI.scaled("gqa_rope", latent="f16", act="f16", batch=2, max_len=96,
+                                   fixed_lengths=(96, 50)), None),
+]
+
+
+@pytest.mark.parametrize("name,wl,_", SMALL, ids=[s[0] for s in SMALL])
+def test_small_full_compare(name, wl, _):
+    case = build_decode_case(wl)
+    gpu = run_decode(case)
+    ref = oracle_decode(case)
+    stats = compare(gpu, ref, wl.act, name)
+    print(name, stats)
+
+
+@pytest.mark.parametrize("q_scale", [8.0])
+def test_peaked_attention(q_scale):
+    wl = _small("llama2_7b", batch=2, max_len=160, fixed_lengths=(160, 99), name="7b_peaked")
+    case = build_decode_case(wl, q_scale=q_scale)
+    compare(run_decode(case), oracle_decode(case), wl.act, "peaked")
+    wl = _small("gqa_rope", batch=2, max_len=160, fixed_lengths=(160, 99), name="gqa_peaked")
+    case = build_decode_case(wl, q_scale=q_scale)
+    compare(run_decode(case), oracle_decode(case), wl.act, "gqa peaked")
+
+
+def test_empty_sequences_and_explicit_positions():
+    import torch
+    wl = _small("llama2_7b", batch=4, max_len=128, fixed_lengths=(0, 128, 0, 5), name="7b_empty")
+    case = build_decode_case(wl)
+    gpu = run_decode(case)
+    assert np.all(gpu[0] == 0) and np.all(gpu[2] == 0)
+    compare(gpu, oracle_decode(case), wl.act, "empty")
+    qpos = np.array([0, 1000, 3, 70000], dtype=np.int32)
+    gpu2 = run_decode(case, q_pos=torch.from_numpy(qpos).cuda())
+    compare(gpu2, oracle_decode(case, q_pos=qpos), wl.act, "q_pos")
+
+
+def test_batch_zero_is_noop():
+    import torch
+    import rank_decode_attention_amd as R
+    wl = _small("llama2_7b", batch=1, max_len=64, name="7b_b1")
+    case = build_decode_case(wl)
+    q0 = case["q"][:0]
+    out0 = case["out"][:0]
+    R.palu_decode_attn(case["desc"], q0, case["cache"], case["Bk"], case["Bv"], case["seq_lens"], None,
+                       case["sm_scale"], out0, case["ws"])
+    torch.cuda.synchronize()
+
+
+def test_deterministic():
+    wl = _small("long_b4", batch=2, max_len=2000, ragged=True, name="long_det")
+    case = build_decode_case(wl)
+    a = run_decode(case)
+    b = run_decode(case)
+    assert np.array_equal(a, b)
+
+
+FULL = [
+    ("llama2_7b", [(0, 0), (0, 31), (7, 13), (15, 22)]),
+    ("long_b1", [(0, 0), (0, 17)]),
+    ("long_b4", [(0, 3), (3, 28)]),
+    ("gqa_rope", [(0, 0), (5, 9), (31, 31)]),
+    ("gqa_norope", [(0, 1), (17, 20), (31, 30)]),
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, heads):
+    wl = PI.workload(name)
+    case = build_decode_case(wl)
+    gpu = run_decode(case)
+    ref = oracle_decode(case, heads=heads)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    stats = compare(gpu[bs, hs], ref[bs, hs], wl.act, name)
+    assert np.all(np.isfinite(gpu))
+    print(name, stats)
