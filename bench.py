@@ -1,0 +1,224 @@
+"""Benchmark of palu_decode_attn on one MI355X.
+
+Workload: one decode step of a Llama-2-7B-shaped attention layer over the
+low-rank latent cache (batch 16, history 4096, 32 heads x 128, 8 head-groups
+of 4 heads, rank 256 per group = 50% of the group width, fp16 latents and
+factors, RoPE base 10000), synthetic seeded inputs resident in HBM.
+
+A step is one palu_decode_attn call (every decode step of the method: query
+rotation, latent streaming, key rebuild, RoPE, scores, online softmax, the
+latent-space value accumulation, split merge and the B_v output projection).
+Before each timed step a 1 GiB buffer is overwritten so that no latent bytes
+are served from the 256 MB Infinity Cache or the L2s (cold-cache timing).
+
+Output (stdout, one JSON line): decode tokens/s (batch / step time), plus
+`roofline` for the dominant kernel (the fused split-attention kernel, timed
+with HIP events recorded around it by the library) and `cpu_baseline` (the
+fp64 oracle on the host cores on a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, AMD published
+METRIC = "decode attn tokens/s and latent GB/s (% of HBM peak) at Llama-2-7B shape"
+
+
+def _hip():
+    import torch  # noqa: F401  (torch's HIP runtime is the one in the process)
+    lib = ctypes.CDLL("libamdhip64.so.7")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def setup(wl):
+    import torch
+    import palu_inputs as PI
+    import rank_decode_attention_amd as R
+
+    ranks = PI.ranks(wl)
+    desc = R.AttnDesc(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_groups, ranks.tolist(), use_rope=wl.use_rope,
+                      rope_base=wl.rope_base, latent_dtype=wl.latent, act_dtype=wl.act)
+    lens = PI.lengths(wl)
+    esz = 4 if wl.latent == "f32" else 2
+
+    def rows(which, b, j):
+        a = PI.latent(wl, "k" if which == 0 else "v", b, j, n=int(lens[b]))
+        pitch = R.row_pitch(wl.latent, int(ranks[j]))
+        out = np.zeros((a.shape[0], pitch // esz), dtype=a.dtype)
+        out[:, :a.shape[1]] = a
+        return out.view(np.uint8)
+
+    cache = R.fill_cache(desc, wl.batch, wl.max_len, rows)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.act]
+
+    def dev(a):
+        if wl.act == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    Bk = dev(np.concatenate([PI.factor(wl, "Bk", j).reshape(-1) for j in range(wl.n_groups)]))
+    Bv = dev(np.concatenate([PI.factor(wl, "Bv", j).reshape(-1) for j in range(wl.n_groups)]))
+    q = dev(PI.query(wl))
+    seq_lens = torch.from_numpy(lens).cuda()
+    ws = torch.empty(R.decode_workspace_bytes(desc, wl.batch, wl.max_len), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=tdt, device="cuda")
+    latent_bytes = int(sum(int(lens[b]) * int(ranks.sum()) * 2 * esz for b in range(wl.batch)))
+    recon_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * sum(
+        2 * int(r) * wl.group_width for r in ranks)
+    pv_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * wl.n_q_heads * 2 * int(ranks.max())
+    return dict(desc=desc, cache=cache, Bk=Bk, Bv=Bv, q=q, seq_lens=seq_lens, ws=ws, out=out,
+                sm_scale=1.0 / math.sqrt(wl.head_dim), latent_bytes=latent_bytes,
+                flops=recon_flops + pv_flops, lens=lens)
+
+
+def run_steps(st, steps, scrub, hip, ev_main):
+    import torch
+    import rank_decode_attention_amd as R
+    t_call, t_main = [], []
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mains = []
+    for i in range(steps):
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
+        before, after = ctypes.c_void_p(), ctypes.c_void_p()
+        if ev_main:
+            hip.hipEventCreate(ctypes.byref(before))
+            hip.hipEventCreate(ctypes.byref(after))
+            R.palu_profile_events(before, after)
+            mains.append((before, after))
+        starts[i].record()
+        R.palu_decode_attn(st["desc"], st["q"], st["cache"], st["Bk"], st["Bv"], st["seq_lens"], None,
+                           st["sm_scale"], st["out"], st["ws"])
+        ends[i].record()
+    R.palu_profile_events(None, None)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        t_call.append(starts[i].elapsed_time(ends[i]))
+    for before, after in mains:
+        ms = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(ms), before, after)
+        t_main.append(ms.value)
+        hip.hipEventDestroy(before)
+        hip.hipEventDestroy(after)
+    return t_call, t_main
+
+
+def cpu_baseline(wl, n_seq: int, reps: int = 3):
+    """The fp64 oracle (as it stands) on the first n_seq sequences of the workload."""
+    import oracle
+    import palu_inputs as PI
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    lens = PI.lengths(wl)[:n_seq]
+    zk = [[oracle.upcast(PI.latent(wl, "k", b, j, n=int(lens[b])), wl.latent) for b in range(n_seq)]
+          for j in range(wl.n_groups)]
+    zv = [[oracle.upcast(PI.latent(wl, "v", b, j, n=int(lens[b])), wl.latent) for b in range(n_seq)]
+          for j in range(wl.n_groups)]
+    Bk = [oracle.upcast(PI.factor(wl, "Bk", j), wl.act) for j in range(wl.n_groups)]
+    Bv = [oracle.upcast(PI.factor(wl, "Bv", j), wl.act) for j in range(wl.n_groups)]
+    q = oracle.upcast(PI.query(wl), wl.act)[:n_seq]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, zk, zv, Bk, Bv, lens, n_kv_heads=wl.n_kv_heads, use_rope=wl.use_rope,
+                                rope_base=wl.rope_base, sm_scale=1.0 / math.sqrt(wl.head_dim))
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": n_seq / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences (history {int(lens[0])}, all {wl.n_q_heads} heads), "
+                      f"fp64 numpy, median of {reps} runs of {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--no-scrub", action="store_true", help="time with warm caches")
+    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--detail", default="", help="also write a detailed JSON record to this path")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the method's hot path here is "
+              f"single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import palu_inputs as PI
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = PI.workload(args.workload)
+    st = setup(wl)
+    hip = _hip()
+    scrub = None if args.no_scrub else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    run_steps(st, args.warmup, scrub, hip, ev_main=False)
+    torch.cuda.synchronize()
+    t_call, t_main = run_steps(st, args.steps, scrub, hip, ev_main=True)
+    torch.cuda.synchronize()
+
+    ms_step = statistics.mean(t_call)
+    ms_main = statistics.mean(t_main)
+    tokens_per_s = wl.batch / (ms_step * 1e-3)
+    achieved = st["latent_bytes"] / (ms_main * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.act,
+        "data": "synthetic (seeded N(0,1) latents and queries, Gaussian factors with std 1/sqrt(fan_in))",
+        "config": {
+            "workload": f"{wl.name}: decode step, batch {wl.batch}, history {wl.max_len}, {wl.n_q_heads} heads x "
+                        f"{wl.head_dim}, {wl.n_groups} head-groups of {wl.kv_per_group} kv heads, rank "
+                        f"{int(PI.ranks(wl)[0])} per group, {wl.latent} latents, RoPE {wl.use_rope}",
+            "global_batch": wl.batch, "seq_len": wl.max_len, "parallelism": "single GPU",
+            "cache": "cold (1 GiB scrub before each step)" if scrub is not None else "warm",
+        },
+        "latent_GBps": round(st["latent_bytes"] / (ms_step * 1e-3) / 1e9, 1),
+        "latent_frac_of_hbm_peak": round(st["latent_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "palu_decode_kernel (split attention)", "kernel_ms": round(ms_main, 4),
+            "algorithmic_bytes": st["latent_bytes"],
+            "mfma_frac_f16": round(st["flops"] / (ms_main * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        },
+    }
+    if args.cpu_seqs > 0:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seqs)
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"line": line, "t_call_ms": t_call, "t_main_ms": t_main,
+                       "t_call_p10_p50_p90": np.percentile(t_call, [10, 50, 90]).tolist()}, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -188,6 +188,7 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  *   out        device [batch][H][d_h] act_dtype
  *   workspace  device, at least palu_decode_workspace_bytes(desc, batch,
  *              cache->max_len) bytes, 256-byte aligned; contents are scratch
+ * batch == 0 is a no-op after the descriptor checks (pointers may be NULL).
  * Errors: INVALID_ARG for null pointers, batch < 0, head counts that do not
  * divide, odd head_dim, rank <= 0, max_len <= 0, non-finite sm_scale,
  * I4 scales missing; WORKSPACE_TOO_SMALL; UNSUPPORTED for shapes without a
@@ -197,6 +198,17 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
                              const void* B_k, const void* B_v, const int32_t* seq_lens,
                              const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * palu_profile_events - timing hook for benchmark harnesses (not part of the
+ * method).  When set (non-NULL), every later palu_decode_attn call on the
+ * calling thread records `before_main` immediately before and `after_main`
+ * immediately after its main split-attention kernel, on the call's stream,
+ * so that hipEventElapsedTime gives that kernel's duration.  The caller owns
+ * the events (hipEventCreate) and must keep them alive while set; pass NULL,
+ * NULL to stop.  Thread-local; never fails.
+ */
+palu_status palu_profile_events(hipEvent_t before_main, hipEvent_t after_main);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "PaluError", "AttnDesc", "LatentCache", "lib_path", "load",
     "latent_bytes", "latent_offset", "row_pitch", "scale_pitch", "alloc_cache", "fill_cache",
-    "decode_workspace_bytes", "palu_decode_attn", "palu_project", "palu_quant_latent",
+    "decode_workspace_bytes", "palu_decode_attn", "palu_project", "palu_quant_latent", "palu_profile_events",
 ]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +83,8 @@ def load():
     lib.palu_decode_workspace_bytes.restype = sz
     lib.palu_decode_attn.argtypes = [D, vp, C, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.palu_decode_attn.restype = ctypes.c_int
+    lib.palu_profile_events.argtypes = [vp, vp]
+    lib.palu_profile_events.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -205,6 +207,12 @@ def decode_workspace_bytes(desc: AttnDesc, batch: int, max_len: int) -> int:
         lib = load()
         raise PaluError(-1, "palu_decode_workspace_bytes", lib.palu_last_error().decode())
     return n
+
+
+def palu_profile_events(before_main, after_main):
+    """Set (or clear with None, None) HIP events that palu_decode_attn records
+    around its main kernel on the calling thread (palu_profile_events)."""
+    _check(load().palu_profile_events(before_main, after_main))
 
 
 def palu_decode_attn(desc: AttnDesc, q, cache: LatentCache, B_k, B_v, seq_lens, q_pos, sm_scale: float, out,

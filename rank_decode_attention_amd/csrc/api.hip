@@ -20,6 +20,7 @@ using namespace palu;
 namespace {
 
 thread_local char g_err[512];
+thread_local hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
 
 palu_status fail(palu_status s, const char* fmt, ...) {
   va_list ap;
@@ -183,6 +184,12 @@ const char* palu_status_string(palu_status s) {
 
 const char* palu_last_error(void) { return g_err; }
 
+palu_status palu_profile_events(hipEvent_t before_main, hipEvent_t after_main) {
+  g_prof_before = before_main;
+  g_prof_after = after_main;
+  return ok();
+}
+
 size_t palu_latent_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len, int32_t which,
                          int32_t scales) {
   if (check_desc(desc) != PALU_OK || batch < 0 || max_len <= 0 || (which != 0 && which != 1)) return 0;
@@ -279,12 +286,12 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   DecodePlan pl;
   palu_status s = plan_decode(desc, batch, cache->max_len, &pl);
   if (s != PALU_OK) return s;
+  if (batch == 0) return ok();   // nothing is read or written
   if (!q || !B_k || !B_v || !seq_lens || !out || !cache->zk || !cache->zv)
     return fail(PALU_ERR_INVALID_ARG, "null pointer");
   if (!std::isfinite(sm_scale)) return fail(PALU_ERR_INVALID_ARG, "sm_scale must be finite");
   if (!aligned16(cache->zk) || !aligned16(cache->zv))
     return fail(PALU_ERR_INVALID_ARG, "latent buffers must be 16-byte aligned");
-  if (batch == 0) return ok();
   if (!workspace) return fail(PALU_ERR_INVALID_ARG, "workspace is NULL");
   if (((uintptr_t)workspace & 255u) != 0) return fail(PALU_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < pl.total)
@@ -320,8 +327,16 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
     e = launch_qabs(pl.key, p, stream);
     if (e != hipSuccess) return hip_fail(e, "absorbed-query launch");
   }
+  if (g_prof_before) {
+    e = hipEventRecord(g_prof_before, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
   e = launch_decode(pl.key, p, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (g_prof_after) {
+    e = hipEventRecord(g_prof_after, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
   e = launch_merge(pl.key, p, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();

@@ -17,8 +17,8 @@ from palu_cases import build_decode_case, compare, oracle_decode, run_decode
 pytestmark = pytest.mark.gpu
 
 
-def _small(name, **over):
-    return PI.scaled(name, **over)
+def _small(base, **over):
+    return PI.scaled(base, **over)
 
 
 SMALL = [
