@@ -63,6 +63,61 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const void* lds_addr) {
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the
+// gfx950 row-swap permutes (VALU only).  permlane16_swap(a, b) exchanges the
+// odd rows of a with the even rows of b; permlane32_swap(a, b) exchanges the
+// upper half of a with the lower half of b.  With a == b == x the two
+// results of each swap hold the row pair, so every lane ends with the same
+// value, summed in the same order.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// Reductions over each half-wave (32 lanes): DPP butterflies inside a 16-lane
+// row (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror), then the row pair through permlane16_swap.  Every lane of the
+// half receives the result (sums may differ by rounding order between lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max32(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float sum32(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+// x + (value of lane l ^ 32)
+__device__ __forceinline__ float halves_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
 
 // Round-to-nearest-even conversions from binary32.

@@ -31,7 +31,7 @@
 
 namespace palu {
 
-template <class LT_, int DH_, int NG_, int QPK_, int NKC_, int RKMAX_, int RVMAX_, bool ROPE_>
+template <class LT_, int DH_, int NG_, int QPK_, int NKC_, int RKMAX_, int RVMAX_, bool ROPE_, int NW_>
 struct DecCfg {
   typedef LT_ LT;
   static constexpr bool F32 = std::is_same<LT, float>::value;
@@ -39,7 +39,7 @@ struct DecCfg {
   static constexpr int DH = DH_, NG = NG_, QPK = QPK_, NKC = NKC_;
   static constexpr int RKMAX = RKMAX_, RVMAX = RVMAX_;
   static constexpr bool ROPE = ROPE_;
-  static constexpr int TT = kDecTile, NW = kDecWaves, NT = 64 * kDecWaves;
+  static constexpr int TT = kDecTile, NW = NW_, NT = 64 * NW_;
   static constexpr int NJ = DH / 32;                    // 16-row frequency blocks per head half
   static constexpr int PPW = ROPE ? NG * NJ / NW : 0;   // kv heads per wave
   static constexpr int RT = 2 * PPW;                    // 16-row MFMA tiles per wave
@@ -60,7 +60,15 @@ struct DecCfg {
   static constexpr int BUFB = (SLK + SLV) * 16;         // bytes per pipeline buffer
   static constexpr int NNT = RVMAX / 16;                // value n-tiles
   static constexpr int NNTW = cdiv(NNT, NW);
-  static constexpr int NSP = ROPE ? NJ : NW;            // partial-score slots per head
+  // partial scores per (head, token): RoPE one per (frequency block, row
+  // group); absorbed query one per (wave, hi|lo part)
+  // (with several query heads per kv head the row groups are pre-summed in
+  // registers to keep the LDS footprint down)
+  static constexpr bool PRESUM = ROPE && QPK > 1;
+  static constexpr int NP = ROPE ? NJ * (PRESUM ? 1 : 4) : NW;
+  static constexpr int NPP = (NP % 8 == 0) ? NP + 4 : cdiv(NP, 4) * 4;   // padded, 16-byte rows
+  static constexpr int SMW = cdiv(NQ * TT, 64);         // waves computing the softmax
+  static constexpr int PTP = F32 ? TT + 4 : TT + 8;     // P tile row pitch (elements, 16 B padding)
   static constexpr int STG_ROWS = KC;                   // B_k rows staged per pass
   static constexpr int NSI = cdiv(STG_ROWS * W * ESZ / 16, 64 * NW);  // DMA instr per wave per pass
 
@@ -71,6 +79,7 @@ struct DecCfg {
   static_assert(F32 ? NQ <= 16 : NQ <= 8, "query heads per group");
   static_assert(STG_ROWS * W * ESZ <= BUFB, "B_k staging must fit one buffer");
   static_assert(DH % 32 == 0, "head_dim");
+  static_assert(SMW <= NW && TT == 32, "softmax lanes");
 };
 
 // Operand registers of one 16x16xK MFMA input: 8 x 16-bit or 4 x fp32.
@@ -107,9 +116,7 @@ struct DecState {
   typedef typename Op<LT>::type op_t;
   op_t breg[C::ROPE ? C::RT : 1][C::ROPE ? C::NKC : 1];   // B_k^T operand (RoPE path)
   op_t aq[C::ROPE ? 1 : C::NKC];                          // absorbed query operand (no-RoPE path)
-  float qr[C::ROPE ? C::PPW : 1][C::QPK][2][4];           // rotated, pre-scaled query values
   float cs[4], sn[4];                                     // angle at the current tile (u = 0)
-  float c16[4], s16[4];                                   // rotation by 16 tokens
   f32x4 acc[C::NNTW];                                     // P z_v accumulators
   float m_run, l_run;
   int L;                                                  // history length of the current sequence
@@ -123,23 +130,35 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
   __shared__ uint4 buf1[C::BUFB / 16];
   __shared__ uint4 buf2[C::BUFB / 16];
   __shared__ uint4 dummy[64];
-  __shared__ float spart[2 * C::NSP * C::NQ * C::TT];
+  __shared__ float spart[C::NQ * C::TT * C::NPP];
+  __shared__ uint4 ptile[(16 * C::PTP * (C::F32 ? 4 : 2) + 15) / 16];   // P operand: [16 rows][PTP]
+  __shared__ float arow[16];                                             // rescale factor per P row
   __shared__ int tstart[kMaxBatch + 1];
   __shared__ int slen[kMaxBatch];
   __shared__ int wsum[C::NW];
+  // rotated, pre-scaled query values of each wave: [wave][lane row group][x][qq][half] x 4 rows
+  __shared__ f32x4 qtab[C::ROPE ? C::NW * 4 * C::PPW * C::QPK * 2 : 1];
+  // cos / sin of the 16-token rotation of each wave's frequency rows: [wave][row group][cos|sin]
+  __shared__ f32x4 steptab[C::ROPE ? C::NW * 4 * 2 : 1];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g = blockIdx.x % p.G, pb = blockIdx.x / p.G;
   const int batch = p.batch;
+  LT* ptile_h = (LT*)ptile;          // 16-bit P operand rows (hi rows 0-7, lo rows 8-15)
+  float* ptile_f = (float*)ptile;    // fp32 P operand rows
+  // P rows of absent heads stay zero; their rescale factor stays one
+  for (int i = tid; i < (int)(sizeof(ptile) / 16); i += C::NT) ptile[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 16) arow[tid] = 1.f;
 
   // ---------------------------------------------------------------- tile prefix sums
   {
     // each thread scans up to 4 consecutive sequences, then a block scan
+    constexpr int MAXPER = kMaxBatch / C::NT;
     const int per = cdiv(batch, C::NT);
-    int loc[4];
+    int loc[MAXPER];
     int s = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MAXPER; ++i) {
       int bb = tid * per + i;
       int v = 0;
       if (i < per && bb < batch) {
@@ -164,7 +183,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
     for (int i = 0; i < w; ++i) wbase += wsum[i];
     int run = wbase + incl - s;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MAXPER; ++i) {
       int bb = tid * per + i;
       if (i < per && bb < batch) tstart[bb] = run;
       run += loc[i];
@@ -323,10 +342,18 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
     barrier();   // staging buffers free before tile DMA overwrites them
 
     // frequencies of this lane's 4 rows and the 16/32-token rotation steps
+    if ((l & 15) == 0) {
+      f32x4 c4, s4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int f = 16 * jf + 4 * (l >> 4) + e;
-      sincos_angle(16.0, rope_theta(f), &st.c16[e], &st.s16[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int f = 16 * jf + 4 * (l >> 4) + e;
+        float ce, se;
+        sincos_angle(16.0, rope_theta(f), &ce, &se);
+        c4[e] = ce;
+        s4[e] = se;
+      }
+      steptab[(w * 4 + (l >> 4)) * 2] = c4;
+      steptab[(w * 4 + (l >> 4)) * 2 + 1] = s4;
     }
   }
 
@@ -347,7 +374,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
 
   int bcur = seq_of(n_begin, 0);
 
-  auto step = [&](const uint4* bufp, int n, int parity) __attribute__((always_inline)) {
+  auto step = [&](const uint4* bufp, int n) __attribute__((always_inline)) {
     // ---- segment bookkeeping
     bcur = seq_of(n, bcur);
     const int b = bcur;
@@ -362,20 +389,27 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
         float qc[4], qs[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sincos_angle((double)pos, rope_theta(16 * jf + 4 * (l >> 4) + e), &qc[e], &qs[e]);
+        // lanes of one row group share their frequency rows: lane 16*kq writes them
+        if ((l & 15) == 0) {
 #pragma unroll
-        for (int x = 0; x < C::PPW; ++x)
+          for (int x = 0; x < C::PPW; ++x)
 #pragma unroll
-          for (int qq = 0; qq < C::QPK; ++qq) {
-            const int h = (g * C::NG + cbase + x) * C::QPK + qq;
+            for (int qq = 0; qq < C::QPK; ++qq) {
+              const int h = (g * C::NG + cbase + x) * C::QPK + qq;
+              f32x4 lo4, hi4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int f = 16 * jf + 4 * (l >> 4) + e;
-              float qlo = to_f32(qb[h * C::DH + f]);
-              float qhi = to_f32(qb[h * C::DH + f + C::DH / 2]);
-              st.qr[x][qq][0][e] = (qlo * qc[e] - qhi * qs[e]) * p.qscale;
-              st.qr[x][qq][1][e] = (qlo * qs[e] + qhi * qc[e]) * p.qscale;
+              for (int e = 0; e < 4; ++e) {
+                const int f = 16 * jf + 4 * (l >> 4) + e;
+                float qlo = to_f32(qb[h * C::DH + f]);
+                float qhi = to_f32(qb[h * C::DH + f + C::DH / 2]);
+                lo4[e] = (qlo * qc[e] - qhi * qs[e]) * p.qscale;
+                hi4[e] = (qlo * qs[e] + qhi * qc[e]) * p.qscale;
+              }
+              f32x4* qt = qtab + ((w * 4 + (l >> 4)) * C::PPW * C::QPK + x * C::QPK + qq) * 2;
+              qt[0] = lo4;
+              qt[1] = hi4;
             }
-          }
+        }
       } else {
         const int kq = l >> 4, row = l & 15;
         const int hq = C::F32 ? row : (row & 7);
@@ -415,10 +449,9 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
 
     const uint8_t* zkt = (const uint8_t*)bufp;
     const uint8_t* zvt = (const uint8_t*)(bufp + C::SLK);
-    float* sp = spart + parity * (C::NSP * C::NQ * C::TT);
     const int kq = l >> 4, tl = l & 15;
 
-    // ---- scores
+    // ---- partial scores -> spart[hq][t][slot], one slot per (wave part, row group)
     if constexpr (C::ROPE) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -426,24 +459,25 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
 #pragma unroll
         for (int rt = 0; rt < C::RT; ++rt) cacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int t = 16 * u + tl;
-        __builtin_amdgcn_sched_barrier(0);
+        // All NKC chunks run: rows of B_k past the group's rank are zero in
+        // registers and the LDS slots they meet hold finite latent data.
 #pragma unroll
         for (int kc = 0; kc < C::NKC; ++kc) {
-          if (kc < nkc) {
-            // k >= r_k multiplies zero rows of B_k (row padding is finite)
-            op_t bop = *(const op_t*)(zkt + (t * C::PITK + 4 * kc + kq) * 16);
+          const op_t bop = *(const op_t*)(zkt + (t * C::PITK + 4 * kc + kq) * 16);
 #pragma unroll
-            for (int rt = 0; rt < C::RT; ++rt) cacc[rt] = mma<LT>(st.breg[rt][kc], bop, cacc[rt]);
-          }
+          for (int rt = 0; rt < C::RT; ++rt) cacc[rt] = mma<LT>(st.breg[rt][kc], bop, cacc[rt]);
         }
         // RoPE on the accumulator: lane holds token t, rows f_e of both halves
         float c[4], s[4];
+        if (u == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (u == 0) { c[e] = st.cs[e]; s[e] = st.sn[e]; }
-          else {
-            c[e] = st.cs[e] * st.c16[e] - st.sn[e] * st.s16[e];
-            s[e] = st.sn[e] * st.c16[e] + st.cs[e] * st.s16[e];
+          for (int e = 0; e < 4; ++e) { c[e] = st.cs[e]; s[e] = st.sn[e]; }
+        } else {
+          const f32x4 c16 = steptab[(w * 4 + kq) * 2], s16 = steptab[(w * 4 + kq) * 2 + 1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            c[e] = st.cs[e] * c16[e] - st.sn[e] * s16[e];
+            s[e] = st.sn[e] * c16[e] + st.cs[e] * s16[e];
           }
         }
 #pragma unroll
@@ -457,130 +491,141 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           }
 #pragma unroll
           for (int qq = 0; qq < C::QPK; ++qq) {
+            const f32x4* qt = qtab + ((w * 4 + kq) * C::PPW * C::QPK + x * C::QPK + qq) * 2;
+            const f32x4 qlo = qt[0], qhi = qt[1];
             float part = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              part = fmaf(st.qr[x][qq][0][e], klo[e], part);
-              part = fmaf(st.qr[x][qq][1][e], khi[e], part);
+              part = fmaf(qlo[e], klo[e], part);
+              part = fmaf(qhi[e], khi[e], part);
             }
-            part += shfl_xor(part, 16);
-            part += shfl_xor(part, 32);
             const int hq = (cbase + x) * C::QPK + qq;
-            if (kq == 0) sp[(jf * C::NQ + hq) * C::TT + t] = part;
+            if constexpr (C::PRESUM) {
+              part = rows4_sum(part);   // identical in the four row groups
+              spart[(hq * C::TT + t) * C::NPP + jf] = part;
+            } else {
+              spart[(hq * C::TT + t) * C::NPP + jf * 4 + kq] = part;
+            }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // advance the angle recurrence by one tile
+      const f32x4 c16 = steptab[(w * 4 + kq) * 2], s16 = steptab[(w * 4 + kq) * 2 + 1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // rotation by 32 tokens = the 16-token rotation applied twice
-        const float c32 = st.c16[e] * st.c16[e] - st.s16[e] * st.s16[e];
-        const float s32 = 2.f * st.c16[e] * st.s16[e];
+        const float c32 = c16[e] * c16[e] - s16[e] * s16[e];
+        const float s32 = 2.f * c16[e] * s16[e];
         float c2 = st.cs[e] * c32 - st.sn[e] * s32;
         float s2 = st.sn[e] * c32 + st.cs[e] * s32;
         st.cs[e] = c2; st.sn[e] = s2;
       }
     } else {
-      // absorbed query: wave w sums chunks w, w + NW, ...
+      // absorbed query: wave w sums chunks w, w + NW, ...; C rows are query
+      // heads (16-bit: rows 0-7 hi parts, 8-15 lo parts)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         f32x4 cacc = f32x4{0.f, 0.f, 0.f, 0.f};
         const int t = 16 * u + tl;
 #pragma unroll
         for (int kc = 0; kc < C::NKC; ++kc) {
-          if ((kc % C::NW) == w && kc < nkc) {
-            op_t bop = *(const op_t*)(zkt + (t * C::PITK + 4 * kc + kq) * 16);
+          if ((kc % C::NW) == w) {   // wave-uniform; chunks past the rank have zero query
+            const op_t bop = *(const op_t*)(zkt + (t * C::PITK + 4 * kc + kq) * 16);
             cacc = mma<LT>(st.aq[kc], bop, cacc);
           }
         }
         if constexpr (!C::F32) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) cacc[e] += shfl_xor(cacc[e], 32);   // hi + lo rows
+          for (int e = 0; e < 4; ++e) cacc[e] = halves_sum(cacc[e]);   // hi + lo rows
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int hq = 4 * kq + e;
           const bool wr = C::F32 ? (hq < C::NQ) : (kq < 2 && hq < C::NQ);
-          if (wr) sp[(w * C::NQ + hq) * C::TT + t] = cacc[e];
+          if (wr) spart[(hq * C::TT + t) * C::NPP + w] = cacc[e];
         }
       }
     }
     wait_lgkm0();
     barrier();
 
-    // ---- online softmax (every wave, redundantly) in the P-operand layout
-    const int row = l & 15;
-    const int hq = C::F32 ? row : (row & 7);
-    const bool lo_part = !C::F32 && row >= 8;
-    const bool hvalid = hq < C::NQ;
-    float sc[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int tt = C::F32 ? (kq + 4 * x) : (8 * kq + x);
-      float v = 0.f;
+    // ---- online softmax, once per tile: wave w < SMW, lane -> (head, token)
+    if (w < C::SMW) {
+      const int hq = (w * 64 + l) / C::TT, t = (w * 64 + l) % C::TT;
+      const bool hvalid = hq < C::NQ;
+      float sc = 0.f;
       if (hvalid) {
+        const float* sp = spart + (hq * C::TT + t) * C::NPP;
 #pragma unroll
-        for (int j = 0; j < C::NSP; ++j) v += sp[(j * C::NQ + hq) * C::TT + tt];
+        for (int j = 0; j < C::NP / 4; ++j) {
+          const f32x4 v = *(const f32x4*)(sp + 4 * j);
+          sc += (v[0] + v[1]) + (v[2] + v[3]);
+        }
+#pragma unroll
+        for (int j = (C::NP / 4) * 4; j < C::NP; ++j) sc += sp[j];
       }
-      const bool tvalid = hvalid && (t0 + tt < st.L);
-      sc[x] = tvalid ? v : -INFINITY;
+      sc = (hvalid && t0 + t < st.L) ? sc : -INFINITY;
+      const float tmax = max32(sc);
+      const float m_new = hvalid ? fmaxf(st.m_run, tmax) : 0.f;
+      const float alpha = hvalid ? __builtin_amdgcn_exp2f(st.m_run - m_new) : 1.f;
+      const float pr = hvalid ? __builtin_amdgcn_exp2f(sc - m_new) : 0.f;
+      const float psum = sum32(pr);
+      st.l_run = st.l_run * alpha + psum;
+      st.m_run = m_new;
+      if (hvalid) {
+        if constexpr (C::F32) {
+          ptile_f[hq * C::PTP + t] = pr;
+        } else {
+          const LT hi = from_f32<LT>(pr);
+          const LT lo = from_f32<LT>(pr - to_f32(hi));
+          ptile_h[hq * C::PTP + t] = hi;
+          ptile_h[(8 + hq) * C::PTP + t] = lo;
+        }
+        if (t == 0) {
+          arow[hq] = alpha;
+          if constexpr (!C::F32) arow[8 + hq] = alpha;
+          if (seg_end) {
+            float* rec = p.rec + ((int64_t)g * (p.P + batch) + pb + b) * p.rec_stride;
+            rec[2 * hq] = st.m_run;
+            rec[2 * hq + 1] = st.l_run;
+          }
+        }
+      }
+      if (seg_end) {
+        st.m_run = -INFINITY;
+        st.l_run = 0.f;
+      }
     }
-    float tmax = sc[0];
-#pragma unroll
-    for (int x = 1; x < 8; ++x) tmax = fmaxf(tmax, sc[x]);
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    float alpha = 1.f, m_new = st.m_run;
-    float pr[8];
-    if (hvalid) {
-      m_new = fmaxf(st.m_run, tmax);
-      alpha = exp2f(st.m_run - m_new);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pr[x] = exp2f(sc[x] - m_new);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pr[x] = 0.f;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) psum += pr[x];
-    psum += shfl_xor(psum, 16);
-    psum += shfl_xor(psum, 32);
-    st.l_run = st.l_run * alpha + psum;
-    st.m_run = m_new;
+    wait_lgkm0();
+    barrier();
 
-    // alpha of the accumulator rows held by this lane (rows 4*kq + e)
-    float arow[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) arow[e] = shfl(alpha, 4 * kq + e);
-
-    // ---- acc += P z_v
+    // ---- acc += P z_v (every wave, its value n-tiles)
+    const f32x4 ar = *(const f32x4*)(arow + 4 * kq);
+    const int row = l & 15;
     if constexpr (C::F32) {
+      float pf[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pf[x] = ptile_f[row * C::PTP + kq + 4 * x];
 #pragma unroll
       for (int i = 0; i < C::NNTW; ++i) {
         const int nt = w + i * C::NW;
         if (nt < nnt) {
           f32x4 a = st.acc[i];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] *= arow[e];
+          for (int e = 0; e < 4; ++e) a[e] *= ar[e];
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             const int tt = kq + 4 * x;
             const int col = 16 * nt + row;
             float zvv = *(const float*)(zvt + tt * C::PITV * 16 + col * 4);
-            a = mfma16x16x4(pr[x], zvv, a);
+            a = mfma16x16x4(pf[x], zvv, a);
           }
           st.acc[i] = a;
         }
       }
     } else {
-      op_t pop;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        LT hi = from_f32<LT>(pr[x]);
-        LT lo = from_f32<LT>(pr[x] - to_f32(hi));
-        pop[x] = lo_part ? lo : hi;
-      }
+      const op_t pop = *(const op_t*)(ptile_h + row * C::PTP + 8 * kq);
       const int s = l & 15;
 #pragma unroll
       for (int i = 0; i < C::NNTW; ++i) {
@@ -588,7 +633,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
         if (nt < nnt) {
           f32x4 a = st.acc[i];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] *= arow[e];
+          for (int e = 0; e < 4; ++e) a[e] *= ar[e];
           // rows (tokens) 8kq + s/4 (+4), columns 16 nt + 4 (s%4) .. +3
           const int ta = 8 * kq + (s >> 2), tb = ta + 4;
           const int colb = (16 * nt + 4 * (s & 3)) * 2;
@@ -605,8 +650,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
     // ---- close the split record at the end of a segment
     if (seg_end) {
       const int k = pb + b;
-      float* rec = p.rec + ((int64_t)g * (p.P + batch) + k) * p.rec_stride;
-      float* racc = rec + 2 * C::NQ;
+      float* racc = p.rec + ((int64_t)g * (p.P + batch) + k) * p.rec_stride + 2 * C::NQ;
 #pragma unroll
       for (int i = 0; i < C::NNTW; ++i) {
         const int nt = w + i * C::NW;
@@ -614,7 +658,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           f32x4 a = st.acc[i];
           if constexpr (!C::F32) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] += shfl_xor(a[e], 32);
+            for (int e = 0; e < 4; ++e) a[e] = halves_sum(a[e]);   // hi + lo rows
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -624,12 +668,6 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           }
         }
       }
-      if (w == 0 && kq == 0 && hvalid && !lo_part) {
-        rec[2 * hq] = st.m_run;
-        rec[2 * hq + 1] = st.l_run;
-      }
-      st.m_run = -INFINITY;
-      st.l_run = 0.f;
 #pragma unroll
       for (int i = 0; i < C::NNTW; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -650,10 +688,9 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           else if (ph == 1) issue_n(buf0, nn + 2);
           else issue_n(buf1, nn + 2);
         }
-        const int parity = (nn - n_begin) & 1;
-        if (ph == 0) step(buf0, nn, parity);
-        else if (ph == 1) step(buf1, nn, parity);
-        else step(buf2, nn, parity);
+        if (ph == 0) step(buf0, nn);
+        else if (ph == 1) step(buf1, nn);
+        else step(buf2, nn);
       }
     }
   }
@@ -686,64 +723,131 @@ __global__ void __launch_bounds__(256) palu_qabs_kernel(const DecodeParams p, in
 }
 
 // ------------------------------------------------------------------ merge + B_v
-// One block per (group, sequence): combine the split records of the sequence
-// (m* = max m_i, l* = sum l_i 2^(m_i - m*), a = sum acc_i 2^(m_i - m*) / l*)
-// and write out[b][h][:] = a_h . B_v^g[:, c(h)*DH : (c(h)+1)*DH].
+// Block = (group g, kv head c of the group, chunk of sequences); its 16 rows
+// are (sequence, query head of kv head c) pairs.  For every row the split
+// records of the sequence are combined,
+//   m* = max m_i, l* = sum l_i 2^(m_i - m*), a = sum acc_i 2^(m_i - m*) / l*,
+// and out[b][h][:] = a . B_v^g[:, c*DH : (c+1)*DH] (16-bit: MFMA with a split
+// into hi + lo parts, B_v staged once in LDS; fp32: VALU).
+constexpr int kMergeRows = 16;
+
 template <class LT, int DH>
 __global__ void __launch_bounds__(256) palu_merge_kernel(const DecodeParams p, int nq, int qpk, int ng) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  constexpr bool F32 = std::is_same<LT, float>::value;
+  const int g = blockIdx.x / ng, c = blockIdx.x % ng;
+  const int bpc = kMergeRows / qpk;                  // sequences per block
+  const int b0 = blockIdx.y * bpc;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int rv = p.rv[g];
+  const int rvk = (rv + 31) / 32 * 32;               // rank padded to whole k-steps
+  const int w_grp = ng * DH;
   extern __shared__ float smem[];
-  float* a = smem;                      // [nq][rvp]
-  float* wgt = smem + nq * p.rvp;       // [P][nq] record weights
-  LT* out = (LT*)p.out + (int64_t)b * p.H * DH + (int64_t)g * nq * DH;
+  float* a = smem;                                   // [16][rvk + 4]
+  const int apitch = rvk + 4;
+  LT* bs = (LT*)(smem + kMergeRows * apitch);        // [rvk][DH + 8]
+  constexpr int BP = DH + (F32 ? 4 : 16);   // row pitch: consecutive rows 8 banks apart
 
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
-  const int ts = p.hdr[b], te = p.hdr[b + 1], total = p.hdr[p.batch];
-  if (L == 0 || te <= ts) {
-    for (int i = tid; i < nq * DH; i += blockDim.x) out[i] = from_f32<LT>(0.f);
-    return;
+  // stage B_v^g[:, c*DH : (c+1)*DH], zero rows past the rank
+  const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH;
+  constexpr int EPC = 16 / sizeof(LT);              // elements per 16-byte chunk
+  for (int i = tid; i < rvk * (DH / EPC); i += 256) {
+    const int r = i / (DH / EPC), cc = i - r * (DH / EPC);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rv) v = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
+    *(uint4*)(bs + r * BP + cc * EPC) = v;
   }
+
+  // merge the records of each row into a[row][r]
+  const int total = p.hdr[p.batch];
   const int tpb = cdiv(total, p.P);
-  const int p0 = ts / tpb, p1 = (te - 1) / tpb;
-  const int nrec = p1 - p0 + 1;           // <= P
-  const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + p0 + b) * p.rec_stride;
+  {
+    const int row = tid >> 4, sub = tid & 15;        // 16 threads per row
+    const int b = b0 + row / qpk, qq = row % qpk;
+    const int hq = c * qpk + qq;
+    float* ar = a + row * apitch;
+    int L = 0;
+    if (b < p.batch) {
+      L = p.seq_lens[b];
+      L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
+    }
+    const int ts = b < p.batch ? p.hdr[b] : 0, te = b < p.batch ? p.hdr[b + 1] : 0;
+    if (L == 0 || te <= ts) {
+      for (int r = sub; r < rvk; r += 16) ar[r] = 0.f;
+    } else {
+      const int p0 = ts / tpb, p1 = (te - 1) / tpb;
+      const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + p0 + b) * p.rec_stride;
+      const int nrec = p1 - p0 + 1;
+      float m = -INFINITY;
+      for (int i = 0; i < nrec; ++i) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * hq]);
+      float ls = 0.f;
+      for (int i = 0; i < nrec; ++i) {
+        const float* rr = recs + (int64_t)i * p.rec_stride;
+        ls += rr[2 * hq + 1] * exp2f(rr[2 * hq] - m);
+      }
+      const float inv = 1.f / ls;
+      for (int r = sub; r < rvk; r += 16) {
+        float sacc = 0.f;
+        if (r < rv) {
+          for (int i = 0; i < nrec; ++i) {
+            const float* rr = recs + (int64_t)i * p.rec_stride;
+            sacc = fmaf(rr[2 * nq + hq * p.rvp + r], exp2f(rr[2 * hq] - m), sacc);
+          }
+        }
+        ar[r] = sacc * inv;
+      }
+    }
+  }
+  __syncthreads();
 
-  for (int h = tid; h < nq; h += blockDim.x) {
-    float m = -INFINITY;
-    for (int i = 0; i < nrec; ++i) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * h]);
-    float ls = 0.f;
-    for (int i = 0; i < nrec; ++i) {
-      const float* r = recs + (int64_t)i * p.rec_stride;
-      ls += r[2 * h + 1] * exp2f(r[2 * h] - m);
+  LT* out = (LT*)p.out;
+  if constexpr (F32) {
+    // 16 rows x DH outputs, one per thread per pass
+    for (int o = tid; o < kMergeRows * DH; o += 256) {
+      const int row = o / DH, d = o - row * DH;
+      const int b = b0 + row / qpk, qq = row % qpk;
+      if (b >= p.batch) continue;
+      const float* ar = a + row * apitch;
+      float sacc = 0.f;
+      for (int r = 0; r < rv; ++r) sacc = fmaf(ar[r], to_f32(bs[r * BP + d]), sacc);
+      const int h = (g * ng + c) * qpk + qq;
+      out[((int64_t)b * p.H + h) * DH + d] = from_f32<LT>(sacc);
     }
-    const float inv = 1.f / ls;
-    for (int i = 0; i < nrec; ++i) {
-      const float* r = recs + (int64_t)i * p.rec_stride;
-      wgt[i * nq + h] = exp2f(r[2 * h] - m) * inv;
+  } else {
+    typedef typename Vec8<LT>::type op_t;
+    const int kq = l >> 4, s = l & 15;
+    for (int nt = w; nt < DH / 16; nt += 4) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < rvk / 32; ++ks) {
+        const float* ap = a + s * apitch + 32 * ks + 8 * kq;     // A: row s, k = 8 kq .. +7
+        op_t ahi, alo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = ap[e];
+          const LT hi = from_f32<LT>(v);
+          ahi[e] = hi;
+          alo[e] = from_f32<LT>(v - to_f32(hi));
+        }
+        // B: rows (ranks) 32 ks + 8 kq + s/4 (+4), columns 16 nt + 4 (s%4) .. +3
+        const int ra = 32 * ks + 8 * kq + (s >> 2), rb = ra + 4;
+        const int col = 16 * nt + 4 * (s & 3);
+        i16x4 va = ds_read_tr16(bs + ra * BP + col);
+        i16x4 vb = ds_read_tr16(bs + rb * BP + col);
+        typedef short s8 __attribute__((ext_vector_type(8)));
+        s8 both = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        const op_t bop = __builtin_bit_cast(op_t, both);
+        acc = mfma16x16x32(ahi, bop, acc);
+        acc = mfma16x16x32(alo, bop, acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * kq + e;
+        const int b = b0 + row / qpk, qq = row % qpk;
+        if (b < p.batch) {
+          const int h = (g * ng + c) * qpk + qq;
+          out[((int64_t)b * p.H + h) * DH + 16 * nt + s] = from_f32<LT>(acc[e]);
+        }
+      }
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nq * rv; idx += blockDim.x) {
-    const int h = idx / rv, r = idx - h * rv;
-    float s = 0.f;
-    for (int i = 0; i < nrec; ++i)
-      s = fmaf(recs[(int64_t)i * p.rec_stride + 2 * nq + h * p.rvp + r], wgt[i * nq + h], s);
-    a[h * p.rvp + r] = s;
-  }
-  __syncthreads();
-  const LT* Bv = (const LT*)p.Bv + p.boff_v[g];
-  const int w = ng * DH;
-  for (int idx = tid; idx < nq * DH; idx += blockDim.x) {
-    const int h = idx / DH, d = idx - h * DH;
-    const int c = h / qpk;
-    const float* ah = a + h * p.rvp;
-    const LT* col = Bv + c * DH + d;
-    float s = 0.f;
-    for (int r = 0; r < rv; ++r) s = fmaf(ah[r], to_f32(col[(int64_t)r * w]), s);
-    out[idx] = from_f32<LT>(s);
   }
 }
 
@@ -760,7 +864,7 @@ struct Entry {
 };
 
 #define PALU_DEC(LTT, ELT, DH, NG, QPK, NKC, RK, RV, ROPE) \
-  Entry{DecodeKey{ELT, DH, NG, QPK, RK, RV, ROPE}, &launch_cfg<DecCfg<LTT, DH, NG, QPK, NKC, RK, RV, ROPE>>}
+  Entry{DecodeKey{ELT, DH, NG, QPK, RK, RV, ROPE}, &launch_cfg<DecCfg<LTT, DH, NG, QPK, NKC, RK, RV, ROPE, kDecWaves>>}
 
 static const Entry kEntries[] = {
     // fp32 latents: 16-k chunks (head_dim 64, groups of 4 kv heads)
@@ -829,13 +933,19 @@ hipError_t launch_qabs(const DecodeKey& k, const DecodeParams& p, hipStream_t st
 template <class LT>
 static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
   const int nq = k.kv_per_group * k.q_per_kv;
-  const size_t smem = (size_t)(nq * p.rvp + p.P * nq) * sizeof(float);
-  if (k.head_dim == 64)
-    hipLaunchKernelGGL((palu_merge_kernel<LT, 64>), dim3(p.G, p.batch), dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
-  else if (k.head_dim == 128)
-    hipLaunchKernelGGL((palu_merge_kernel<LT, 128>), dim3(p.G, p.batch), dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
-  else
-    return hipErrorInvalidValue;
+  if (kMergeRows % k.q_per_kv != 0) return hipErrorInvalidValue;
+  const int bpc = kMergeRows / k.q_per_kv;
+  const int rvk = (k.rv_max + 31) / 32 * 32;
+  const size_t smem = (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
+                      (size_t)rvk * (k.head_dim + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT);
+  dim3 grid(p.G * k.kv_per_group, (p.batch + bpc - 1) / bpc);
+  auto kern = k.head_dim == 64 ? palu_merge_kernel<LT, 64> : palu_merge_kernel<LT, 128>;
+  if (k.head_dim != 64 && k.head_dim != 128) return hipErrorInvalidValue;
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
   return hipGetLastError();
 }
 
