@@ -38,9 +38,20 @@ __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
 }
 
 // 16-byte global -> LDS copy; `lds_wave_base` must be wave-uniform, lane l
-// writes bytes [16*l, 16*l+16) after it.
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (PALU_LDS void*)lds_wave_base, 16, 0, 0);
+// writes bytes [16*l, 16*l+16) after it.  Issued from an asm block (M0 is set
+// in the same block; there are no register outputs) so that the compiler
+// does not order later LDS reads of other buffers behind it: callers wait
+// with wait_vmcnt<N>() and a barrier before reading the destination.
+__device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_wave_base) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(gsrc)
+               : "memory", "m0");
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const PALU_LDS void*)p;
 }
 
 // s_waitcnt vmcnt(N) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding).

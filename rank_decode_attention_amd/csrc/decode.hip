@@ -27,6 +27,7 @@
 #include "common.h"
 #include "decode.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace palu {
@@ -57,7 +58,11 @@ struct DecCfg {
   static constexpr int SLV = cdiv(TT * PITV, 64) * 64;
   static constexpr int NIK = cdiv(SLK, 64 * NW), NIV = cdiv(SLV, 64 * NW);
   static constexpr int NDMA = NIK + NIV;                // DMA instructions per wave per tile
-  static constexpr int BUFB = (SLK + SLV) * 16;         // bytes per pipeline buffer
+  // each buffer ends with one instruction's worth of overflow slots: DMA
+  // instructions of waves past a region's end land there (never read), so
+  // every DMA destination stays inside its own buffer object
+  static constexpr int PADS = 64;
+  static constexpr int BUFB = (SLK + SLV + PADS) * 16;  // bytes per pipeline buffer
   static constexpr int NNT = RVMAX / 16;                // value n-tiles
   static constexpr int NNTW = cdiv(NNT, NW);
   // partial scores per (head, token): RoPE one per (frequency block, row
@@ -129,7 +134,6 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
   __shared__ uint4 buf0[C::BUFB / 16];
   __shared__ uint4 buf1[C::BUFB / 16];
   __shared__ uint4 buf2[C::BUFB / 16];
-  __shared__ uint4 dummy[64];
   __shared__ float spart[C::NQ * C::TT * C::NPP];
   __shared__ uint4 ptile[(16 * C::PTP * (C::F32 ? 4 : 2) + 15) / 16];   // P operand: [16 rows][PTP]
   __shared__ float arow[16];                                             // rescale factor per P row
@@ -141,7 +145,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
   // cos / sin of the 16-token rotation of each wave's frequency rows: [wave][row group][cos|sin]
   __shared__ f32x4 steptab[C::ROPE ? C::NW * 4 * 2 : 1];
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lane = l;
   const int g = blockIdx.x % p.G, pb = blockIdx.x / p.G;
   const int batch = p.batch;
   LT* ptile_h = (LT*)ptile;          // 16-bit P operand rows (hi rows 0-7, lo rows 8-15)
@@ -243,21 +247,24 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
   auto seq_len = [&](int b) { return slen[b]; };
 
   auto issue_tile = [&](uint4* bufp, int b, int t0, int L) __attribute__((always_inline)) {
-    const uint8_t* kb = zk_seq + (int64_t)b * sbk;
-    const uint8_t* vb = zv_seq + (int64_t)b * sbv;
+    // wave-uniform 64-bit bases, per-lane 32-bit offsets (rows past the
+    // history are clamped to its last row: valid memory, masked later)
+    const uint8_t* kb = zk_seq + (int64_t)b * sbk + (uint32_t)t0 * (uint32_t)pk;
+    const uint8_t* vb = zv_seq + (int64_t)b * sbv + (uint32_t)t0 * (uint32_t)pv;
+    const int lim = L - 1 - t0;
 #pragma unroll
     for (int m = 0; m < C::NIK; ++m) {
-      int sbase = (m * C::NW + w) * 64;
-      int tg = min(t0 + (dk_geo[m] >> 16), L - 1);
-      void* dst = sbase < C::SLK ? (void*)(bufp + sbase) : (void*)dummy;
-      dma16(kb + (int64_t)tg * pk + (dk_geo[m] & 0xFFFF), dst);
+      const int sbase = (m * C::NW + w) * 64;
+      const uint32_t off = (uint32_t)min(dk_geo[m] >> 16, lim) * (uint32_t)pk + (uint32_t)(dk_geo[m] & 0xFFFF);
+      const unsigned dst = lds_addr(bufp) + 16u * (sbase < C::SLK ? sbase : C::SLK + C::SLV);
+      dma16(kb + off, dst);
     }
 #pragma unroll
     for (int m = 0; m < C::NIV; ++m) {
-      int sbase = (m * C::NW + w) * 64;
-      int tg = min(t0 + (dv_geo[m] >> 16), L - 1);
-      void* dst = sbase < C::SLV ? (void*)(bufp + C::SLK + sbase) : (void*)dummy;
-      dma16(vb + (int64_t)tg * pv + (dv_geo[m] & 0xFFFF), dst);
+      const int sbase = (m * C::NW + w) * 64;
+      const uint32_t off = (uint32_t)min(dv_geo[m] >> 16, lim) * (uint32_t)pv + (uint32_t)(dv_geo[m] & 0xFFFF);
+      const unsigned dst = lds_addr(bufp) + 16u * (sbase < C::SLV ? C::SLK + sbase : C::SLK + C::SLV);
+      dma16(vb + off, dst);
     }
   };
 
@@ -283,7 +290,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
         int row = e0 / C::W, col = e0 - row * C::W;
         int kr = kc * C::KC + row;
         kr = kr < rk ? kr : rk - 1;
-        void* dst = sbase < STG_SLOTS ? (void*)(bufp + sbase) : (void*)dummy;
+        const unsigned dst = lds_addr(bufp) + 16u * (sbase < STG_SLOTS ? sbase : C::SLK + C::SLV);
         dma16(Bg + (int64_t)kr * C::W + col, dst);
       }
     };
@@ -375,6 +382,11 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
   int bcur = seq_of(n_begin, 0);
 
   auto step = [&](const uint4* bufp, int n) __attribute__((always_inline)) {
+    // Lane-derived offsets are recomputed from an opaque copy of the lane id
+    // every tile: cheaper than keeping dozens of hoisted addresses alive in
+    // registers across the tile loop.
+    int l = lane;
+    asm volatile("" : "+v"(l));
     // ---- segment bookkeeping
     bcur = seq_of(n, bcur);
     const int b = bcur;
@@ -438,6 +450,10 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           st.aq[kc] = v;
         }
       }
+      // The segment's global loads finish here (a pipeline drain once per
+      // segment); otherwise the compiler keeps them pending and drains the
+      // whole prefetch pipeline at later register reuses in every tile.
+      wait_vmcnt<0>();
     }
     if constexpr (C::ROPE) {
       if (seg_start || ((n - n_begin) & 63) == 0) {
@@ -650,7 +666,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
     // ---- close the split record at the end of a segment
     if (seg_end) {
       const int k = pb + b;
-      float* racc = p.rec + ((int64_t)g * (p.P + batch) + k) * p.rec_stride + 2 * C::NQ;
+      float* racc = p.rec + ((int64_t)g * (p.P + batch) + k) * p.rec_stride + 2 * C::NQ;   // wave-uniform
 #pragma unroll
       for (int i = 0; i < C::NNTW; ++i) {
         const int nt = w + i * C::NW;
@@ -664,7 +680,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           for (int e = 0; e < 4; ++e) {
             const int hrow = 4 * kq + e;
             const bool wr = C::F32 ? (hrow < C::NQ) : (kq < 2 && hrow < C::NQ);
-            if (wr) racc[hrow * p.rvp + 16 * nt + (l & 15)] = a[e];
+            if (wr) racc[(uint32_t)(hrow * p.rvp + 16 * nt + (l & 15))] = a[e];
           }
         }
       }
@@ -942,7 +958,16 @@ static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipS
   auto kern = k.head_dim == 64 ? palu_merge_kernel<LT, 64> : palu_merge_kernel<LT, 128>;
   if (k.head_dim != 64 && k.head_dim != 128) return hipErrorInvalidValue;
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    // raise the dynamic-LDS limit once per instantiation (to the largest size
+    // this kernel can ask for)
+    static std::once_flag once64, once128;
+    static hipError_t err64 = hipSuccess, err128 = hipSuccess;
+    const int lim = 160 * 1024;
+    if (k.head_dim == 64)
+      std::call_once(once64, [&] { err64 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lim); });
+    else
+      std::call_once(once128, [&] { err128 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lim); });
+    const hipError_t e = k.head_dim == 64 ? err64 : err128;
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);

@@ -82,12 +82,12 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
 #pragma unroll
     for (int m = 0; m < C::NIX; ++m) {
       const T* src = X + (m0 + (gx[m] >> 8)) * D + k0 + (gx[m] & 0xFF) * (16 / C::ESZ);
-      dma16(src, buf + (m * C::NW + w) * 64);
+      dma16(src, lds_addr(buf) + 16u * ((m * C::NW + w) * 64));
     }
 #pragma unroll
     for (int m = 0; m < C::NIA; ++m) {
       const T* src = A + (col0 + (ga[m] >> 8)) * D + k0 + (ga[m] & 0xFF) * (16 / C::ESZ);
-      dma16(src, buf + C::SX + (m * C::NW + w) * 64);
+      dma16(src, lds_addr(buf) + 16u * (C::SX + (m * C::NW + w) * 64));
     }
   };
 
