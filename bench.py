@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -33,6 +34,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+# HBM bytes per launch of the main kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, calibrated against a plain copy of known size; valid only for the
+# kernel sources it was measured on (their hash is stored beside the figures).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "palu_decode_kernel_llama2_7b_traffic.json")
+KERNEL_SOURCES = ["decode.hip", "decode.h", "common.h"]
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, AMD published
 METRIC = "decode attn tokens/s and latent GB/s (% of HBM peak) at Llama-2-7B shape"
 
@@ -120,6 +126,69 @@ def run_steps(st, steps, scrub, hip, ev_main):
     return t_call, t_main
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rank_decode_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the stored counter passes, or None when they
+    were taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return int(t["read_bytes_per_launch"] + t["write_bytes_per_launch"])
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counter readings give the scale from counter units to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "reps": reps}),
+          flush=True)
+
+
+def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str = TRAFFIC_FILE):
+    """Derive HBM bytes per main-kernel launch from four rocprofv3 --pmc runs
+    under prof_dir (FETCH_SIZE / WRITE_SIZE of this benchmark, and of the
+    copy calibration) and store them with the kernel sources' hash."""
+    import csv
+    import glob
+
+    def values(sub, name_part):
+        f = glob.glob(os.path.join(prof_dir, sub, "*counter_collection.csv"))[0]
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(f)) if name_part in r["Kernel_Name"]]
+
+    def med(v):
+        return statistics.median(v)
+
+    scale_r = copy_bytes / (1024 * med([v for v in values("copy_FETCH_SIZE", "copyBuffer") if v > 1024]))
+    scale_w = copy_bytes / (1024 * med([v for v in values("copy_WRITE_SIZE", "copyBuffer") if v > 1024]))
+    rd = med(values("FETCH_SIZE", "palu_decode_kernel")) * 1024 * scale_r
+    wr = med(values("WRITE_SIZE", "palu_decode_kernel")) * 1024 * scale_w
+    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "kernel": "palu_decode_kernel",
+           "read_bytes_per_launch": int(round(rd)), "write_bytes_per_launch": int(round(wr)),
+           "fetch_scale": round(scale_r, 5), "write_scale": round(scale_w, 5),
+           "how": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches), "
+                  "each times the bytes-per-counted-byte of a plain copy of known size"}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, n_seq: int, reps: int = 3):
     """The fp64 oracle (as it stands) on the first n_seq sequences of the workload."""
     import oracle
@@ -158,7 +227,15 @@ def main():
     ap.add_argument("--no-scrub", action="store_true", help="time with warm caches")
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--detail", default="", help="also write a detailed JSON record to this path")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--record-traffic", default="", metavar="DIR",
+                    help="derive the main kernel's HBM bytes from the counter runs under DIR and store them")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE, help="where --record-traffic writes")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.workload, 1 << 30, args.traffic_out)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the method's hot path here is "
               f"single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
@@ -167,6 +244,9 @@ def main():
     import torch
     import palu_inputs as PI
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
     wl = PI.workload(args.workload)
     st = setup(wl)
     hip = _hip()
@@ -181,6 +261,7 @@ def main():
     ms_main = statistics.mean(t_main)
     tokens_per_s = wl.batch / (ms_step * 1e-3)
     achieved = st["latent_bytes"] / (ms_main * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -205,7 +286,7 @@ def main():
         "latent_frac_of_hbm_peak": round(st["latent_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "palu_decode_kernel (split attention)", "kernel_ms": round(ms_main, 4),
             "algorithmic_bytes": st["latent_bytes"],
             "mfma_frac_f16": round(st["flops"] / (ms_main * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),

@@ -134,8 +134,9 @@ int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t 
  * Per 32-element chunk: s = fp16(amax / 7) (binary32 divide, round to
  * nearest even), code = clamp(rint(z / s), -7, 7) in binary32 with ties to
  * even, code = 0 where s == 0.  Pad nibbles are written as zero.
- * Errors: INVALID_ARG for null pointers, n_rows < 0, r <= 0, z_row_stride < r;
- * UNSUPPORTED for z_dtype == I4.
+ * n_rows == 0 is a no-op after the argument checks (pointers may be NULL).
+ * Errors: INVALID_ARG for null pointers, n_rows < 0, r <= 0, z_row_stride < r,
+ * codes not 16-byte aligned; UNSUPPORTED for z_dtype == I4.
  */
 palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r,
                               int64_t z_row_stride, void* codes, void* scales, hipStream_t stream);
@@ -201,12 +202,12 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
 
 /*
  * palu_profile_events - timing hook for benchmark harnesses (not part of the
- * method).  When set (non-NULL), every later palu_decode_attn call on the
- * calling thread records `before_main` immediately before and `after_main`
- * immediately after its main split-attention kernel, on the call's stream,
- * so that hipEventElapsedTime gives that kernel's duration.  The caller owns
- * the events (hipEventCreate) and must keep them alive while set; pass NULL,
- * NULL to stop.  Thread-local; never fails.
+ * method).  When both are set (non-NULL), every later palu_decode_attn call
+ * on the calling thread launches its main split-attention kernel with
+ * hipExtLaunchKernel, which stamps `before_main` at the kernel's start and
+ * `after_main` at its end, so that hipEventElapsedTime gives that kernel's
+ * duration.  The caller owns the events (hipEventCreate) and must keep them
+ * alive while set; pass NULL, NULL to stop.  Thread-local; never fails.
  */
 palu_status palu_profile_events(hipEvent_t before_main, hipEvent_t after_main);
 

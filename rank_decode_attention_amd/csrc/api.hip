@@ -214,12 +214,12 @@ int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t 
 
 palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r, int64_t z_row_stride,
                               void* codes, void* scales, hipStream_t stream) {
-  if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
   if (n_rows < 0 || r <= 0 || z_row_stride < r) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r / z_row_stride");
   if (z_dtype == PALU_I4) return fail(PALU_ERR_UNSUPPORTED, "input must be F32, F16 or BF16");
   if (!valid_dtype(z_dtype)) return fail(PALU_ERR_INVALID_ARG, "invalid dtype");
-  if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
   if (n_rows == 0) return ok();
+  if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
   hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream);
   if (e != hipSuccess) return hip_fail(e, "quantiser launch");
   return ok();
@@ -327,16 +327,9 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
     e = launch_qabs(pl.key, p, stream);
     if (e != hipSuccess) return hip_fail(e, "absorbed-query launch");
   }
-  if (g_prof_before) {
-    e = hipEventRecord(g_prof_before, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  e = launch_decode(pl.key, p, stream);
+  const bool prof = g_prof_before && g_prof_after;
+  e = launch_decode(pl.key, p, stream, prof ? g_prof_before : nullptr, prof ? g_prof_after : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (g_prof_after) {
-    e = hipEventRecord(g_prof_after, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
   e = launch_merge(pl.key, p, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();

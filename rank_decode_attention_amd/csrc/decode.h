@@ -46,7 +46,9 @@ struct DecodeKey {
 // Returns false if no compiled instantiation covers the key (rk_max / rv_max
 // are upper bounds that the chosen kernel must reach).
 bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap);
-hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
+// With both events set, the dispatch itself stamps them at the kernel's start and end.
+hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream,
+                         hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_qabs(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
 

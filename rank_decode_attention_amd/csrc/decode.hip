@@ -27,6 +27,7 @@
 #include "common.h"
 #include "decode.h"
 
+#include <hip/hip_ext.h>
 #include <mutex>
 #include <type_traits>
 
@@ -869,14 +870,17 @@ __global__ void __launch_bounds__(256) palu_merge_kernel(const DecodeParams p, i
 
 // ------------------------------------------------------------------ dispatch
 template <class C>
-hipError_t launch_cfg(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(palu_decode_kernel<C>, dim3(p.G * p.P), dim3(C::NT), 0, stream, p);
+hipError_t launch_cfg(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (t0 && t1)  // events stamped by the dispatch itself: the kernel's own start and end
+    hipExtLaunchKernelGGL(palu_decode_kernel<C>, dim3(p.G * p.P), dim3(C::NT), 0, stream, t0, t1, 0, p);
+  else
+    hipLaunchKernelGGL(palu_decode_kernel<C>, dim3(p.G * p.P), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 struct Entry {
   DecodeKey key;
-  hipError_t (*decode)(const DecodeParams&, hipStream_t);
+  hipError_t (*decode)(const DecodeParams&, hipStream_t, hipEvent_t, hipEvent_t);
 };
 
 #define PALU_DEC(LTT, ELT, DH, NG, QPK, NKC, RK, RV, ROPE) \
@@ -919,10 +923,11 @@ bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap) {
   return true;
 }
 
-hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
+                         hipEvent_t t1) {
   const Entry* e = find_entry(k);
   if (!e) return hipErrorInvalidValue;
-  return e->decode(p, stream);
+  return e->decode(p, stream, t0, t1);
 }
 
 template <class LT>

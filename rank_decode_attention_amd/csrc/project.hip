@@ -44,7 +44,6 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   typedef typename std::conditional<C::F32, f32x4, typename Vec8<typename std::conditional<C::F32, _Float16, T>::type>::type>::type op_t;
   __shared__ uint4 st0[C::BUF];
   __shared__ uint4 st1[C::BUF];
-  __shared__ uint4 dummy[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int64_t m0 = (int64_t)blockIdx.x * C::BM;
@@ -186,53 +185,51 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
         }
       }
   } else {
-    // stage fp32 rows in LDS (reusing a stage buffer), 64 tokens per round,
-    // then quantise per (token, 32-element chunk) exactly as palu_quant_latent
-    float* zs = (float*)st0;          // [64 tokens][BN]
+    // Quantise per (token, 32-element chunk) exactly as palu_quant_latent.
+    // Each wave stages one 16-token m-tile at a time in its own LDS region,
+    // transposed ([column][token], 16-byte vector writes of the lane's four
+    // consecutive tokens), then its lanes take one (token, chunk) each.
+    // The region reuses a stage buffer: every wave has passed the main
+    // loop's final barrier, so no stage data is read any more.
+    constexpr int TP = 20;                                  // floats per staged column (16 tokens + pad)
+    static_assert(C::NW * C::BN * TP * 4 <= C::BUF * 16, "staging");
+    float* zs = (float*)st0 + w * (C::BN * TP);
     uint8_t* sb = (is_v ? p.sv : p.sk) + (int64_t)p.seq * (is_v ? p.seq_sbytes_v : p.seq_sbytes_k) +
                   (is_v ? p.soff_v[gj] : p.soff_k[gj]);
     const int nc_row = cdiv(r, 32);
     const int nchunk = cdiv(nvalid, 32);
-    static_assert(64 * C::BN * 4 <= C::BUF * 16, "staging");
-    for (int round = 0; round < C::NW; ++round) {
-      barrier();
-      if (w == round) {
 #pragma unroll
-        for (int a = 0; a < C::MT; ++a)
+    for (int a = 0; a < C::MT; ++a) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int trow = 16 * a + 4 * kq + e;
-#pragma unroll
-            for (int b = 0; b < C::NTL; ++b) zs[trow * C::BN + 16 * b + rr] = acc[a][b][e];
-          }
-      }
+      for (int b = 0; b < C::NTL; ++b) *(f32x4*)(zs + (16 * b + rr) * TP + 4 * kq) = acc[a][b];
       wait_lgkm0();
-      barrier();
-      for (int it = tid; it < 64 * nchunk; it += C::NT) {
-        const int trow = it / nchunk, c = it - trow * nchunk;
-        const int64_t tok = m0 + 64 * round + trow;
-        if (tok >= p.n_tok) continue;
+      for (int it = l; it < 16 * nchunk; it += 64) {
+        const int trow = it & 15, c = it >> 4;
+        const int64_t tok = m0 + 64 * w + 16 * a + trow;
         const int cg = n0 / 32 + c;                // chunk index within the latent row
         const int n = min(32, r - cg * 32);
-        const float* v = zs + trow * C::BN + 32 * c;
-        float amax = 0.f;
-        for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i]));
-        const float s32 = __fdiv_rn(amax, 7.0f);
-        const _Float16 s16 = (_Float16)s32;
-        const float sf = (float)s16;
-        unsigned int words[4] = {0u, 0u, 0u, 0u};
-        for (int i = 0; i < n; ++i) {
-          int q = 0;
-          if (sf != 0.f) {
-            float qf = rintf(__fdiv_rn(v[i], sf));
-            qf = fminf(fmaxf(qf, -7.f), 7.f);
-            q = (int)qf;
+        if (tok < p.n_tok) {
+          const float* v = zs + (32 * c) * TP + trow;
+          float amax = 0.f;
+          for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i * TP]));
+          const float s32 = __fdiv_rn(amax, 7.0f);
+          const _Float16 s16 = (_Float16)s32;
+          const float sf = (float)s16;
+          unsigned int words[4] = {0u, 0u, 0u, 0u};
+          for (int i = 0; i < n; ++i) {
+            int q = 0;
+            if (sf != 0.f) {
+              float qf = rintf(__fdiv_rn(v[i * TP], sf));
+              qf = fminf(fmaxf(qf, -7.f), 7.f);
+              q = (int)qf;
+            }
+            words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
           }
-          words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
+          *(uint4*)(zb + (p.pos0 + tok) * pitch + 16 * cg) = make_uint4(words[0], words[1], words[2], words[3]);
+          ((_Float16*)(sb + (p.pos0 + tok) * 2 * nc_row))[cg] = s16;
         }
-        *(uint4*)(zb + (p.pos0 + tok) * pitch + 16 * cg) = make_uint4(words[0], words[1], words[2], words[3]);
-        ((_Float16*)(sb + (p.pos0 + tok) * 2 * nc_row))[cg] = s16;
       }
+      wait_lgkm0();   // this m-tile's reads are done before the next one is staged
     }
   }
 }
