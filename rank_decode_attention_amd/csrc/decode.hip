@@ -740,77 +740,149 @@ __global__ void __launch_bounds__(256) palu_qabs_kernel(const DecodeParams p, in
 }
 
 // ------------------------------------------------------------------ merge + B_v
-// Block = (group g, kv head c of the group, chunk of sequences); its 16 rows
-// are (sequence, query head of kv head c) pairs.  For every row the split
-// records of the sequence are combined,
+// Block = (group g, kv head c of the group, 32 output columns of that head,
+// 16 rows of (sequence, query head of kv head c)).  For every row the split
+// records of its sequence are combined,
 //   m* = max m_i, l* = sum l_i 2^(m_i - m*), a = sum acc_i 2^(m_i - m*) / l*,
-// and out[b][h][:] = a . B_v^g[:, c*DH : (c+1)*DH] (16-bit: MFMA with a split
-// into hi + lo parts, B_v staged once in LDS; fp32: VALU).
+// with the per-record weights 2^(m_i - m*) / l* formed once per row, then
+// out[b][h][cols] = a . B_v^g[:, c*DH + cols] (16-bit: MFMA with a split into
+// hi + lo parts, one wave per 16 columns; fp32: VALU).  The kernel is
+// latency-bound: every phase issues all of a thread's global loads before
+// using any of them.
 constexpr int kMergeRows = 16;
+constexpr int kMergeCols = 32;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxRank = 320;
 
 template <class LT, int DH>
-__global__ void __launch_bounds__(256) palu_merge_kernel(const DecodeParams p, int nq, int qpk, int ng) {
+__global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeParams p, int nq, int qpk, int ng) {
   constexpr bool F32 = std::is_same<LT, float>::value;
-  const int g = blockIdx.x / ng, c = blockIdx.x % ng;
+  constexpr int NCB = DH / kMergeCols;
+  constexpr int NT = kMergeThreads;
+  const int g = blockIdx.x / (ng * NCB), c = (blockIdx.x / NCB) % ng, cb = blockIdx.x % NCB;
   const int bpc = kMergeRows / qpk;                  // sequences per block
   const int b0 = blockIdx.y * bpc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int rv = p.rv[g];
   const int rvk = (rv + 31) / 32 * 32;               // rank padded to whole k-steps
   const int w_grp = ng * DH;
-  extern __shared__ float smem[];
-  float* a = smem;                                   // [16][rvk + 4]
+  const int wpitch = p.P + 1;
+  // (uint4-typed so that the dynamic region starts 16-byte aligned after the
+  // static arrays below: the a rows and the B_v slice take 16-byte accesses)
+  extern __shared__ uint4 smem_u4[];
+  float* smem = (float*)smem_u4;
+  float* wts = smem;                                 // [16][P + 1] record weights
+  float* a = wts + kMergeRows * wpitch;              // [16][rvk + 4]
   const int apitch = rvk + 4;
-  LT* bs = (LT*)(smem + kMergeRows * apitch);        // [rvk][DH + 8]
-  constexpr int BP = DH + (F32 ? 4 : 16);   // row pitch: consecutive rows 8 banks apart
+  constexpr int BP = kMergeCols + (F32 ? 4 : 16);    // B_v slice row pitch (elements)
+  LT* bs = (LT*)(a + kMergeRows * apitch);           // [rvk][BP]
+  __shared__ int rinfo[kMergeRows][2];               // first record index, record count (0: empty row)
+  __shared__ int maxrec;
 
-  // stage B_v^g[:, c*DH : (c+1)*DH], zero rows past the rank
-  const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH;
-  constexpr int EPC = 16 / sizeof(LT);              // elements per 16-byte chunk
-  for (int i = tid; i < rvk * (DH / EPC); i += 256) {
-    const int r = i / (DH / EPC), cc = i - r * (DH / EPC);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rv) v = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
-    *(uint4*)(bs + r * BP + cc * EPC) = v;
+  // stage B_v^g[:, c*DH + cb*32 .. +32], zero rows past the rank
+  {
+    const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH + cb * kMergeCols;
+    constexpr int EPC = 16 / sizeof(LT);             // elements per 16-byte chunk
+    constexpr int CPRW = kMergeCols / EPC;           // chunks per staged row
+    constexpr int SPT = cdiv(kMergeMaxRank * CPRW, NT);
+    uint4 v[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
+      v[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rv) v[k] = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
+    }
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
+      if (r < rvk) *(uint4*)(bs + r * BP + cc * EPC) = v[k];
+    }
   }
 
-  // merge the records of each row into a[row][r]
+  // per-row record weights: 16 lanes per row
   const int total = p.hdr[p.batch];
   const int tpb = cdiv(total, p.P);
+  if (tid == 0) maxrec = 0;
+  __syncthreads();
   {
-    const int row = tid >> 4, sub = tid & 15;        // 16 threads per row
+    const int row = tid >> 4, sub = tid & 15;
     const int b = b0 + row / qpk, qq = row % qpk;
     const int hq = c * qpk + qq;
-    float* ar = a + row * apitch;
-    int L = 0;
+    int nrec = 0, k0 = 0;
     if (b < p.batch) {
-      L = p.seq_lens[b];
+      int L = p.seq_lens[b];
       L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
-    }
-    const int ts = b < p.batch ? p.hdr[b] : 0, te = b < p.batch ? p.hdr[b + 1] : 0;
-    if (L == 0 || te <= ts) {
-      for (int r = sub; r < rvk; r += 16) ar[r] = 0.f;
-    } else {
-      const int p0 = ts / tpb, p1 = (te - 1) / tpb;
-      const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + p0 + b) * p.rec_stride;
-      const int nrec = p1 - p0 + 1;
-      float m = -INFINITY;
-      for (int i = 0; i < nrec; ++i) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * hq]);
-      float ls = 0.f;
-      for (int i = 0; i < nrec; ++i) {
-        const float* rr = recs + (int64_t)i * p.rec_stride;
-        ls += rr[2 * hq + 1] * exp2f(rr[2 * hq] - m);
+      const int ts = p.hdr[b], te = p.hdr[b + 1];
+      if (L > 0 && te > ts) {
+        const int p0 = ts / tpb, p1 = (te - 1) / tpb;
+        nrec = p1 - p0 + 1;
+        k0 = p0 + b;
       }
-      const float inv = 1.f / ls;
-      for (int r = sub; r < rvk; r += 16) {
-        float sacc = 0.f;
-        if (r < rv) {
-          for (int i = 0; i < nrec; ++i) {
-            const float* rr = recs + (int64_t)i * p.rec_stride;
-            sacc = fmaf(rr[2 * nq + hq * p.rvp + r], exp2f(rr[2 * hq] - m), sacc);
-          }
-        }
-        ar[r] = sacc * inv;
+    }
+    const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + k0) * p.rec_stride;
+    float m = -INFINITY;
+    for (int i = sub; i < nrec; i += 16) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * hq]);
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+    float ls = 0.f;
+    for (int i = sub; i < nrec; i += 16) {
+      const float* rr = recs + (int64_t)i * p.rec_stride;
+      const float e = exp2f(rr[2 * hq] - m);
+      wts[row * wpitch + i] = e;
+      ls = fmaf(rr[2 * hq + 1], e, ls);
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) ls += __shfl_xor(ls, d, 64);
+    const float inv = nrec > 0 ? 1.f / ls : 0.f;
+    for (int i = sub; i < nrec; i += 16) wts[row * wpitch + i] *= inv;
+    if (sub == 0) {
+      rinfo[row][0] = k0;
+      rinfo[row][1] = nrec;
+      atomicMax(&maxrec, nrec);
+    }
+  }
+  __syncthreads();
+
+  // a[row][r] = sum_i w_i acc_i[r]: 4 consecutive ranks per item, consecutive
+  // threads on consecutive items; per record all of a thread's loads go out
+  // before any is used
+  {
+    constexpr int IPT = cdiv(kMergeRows * kMergeMaxRank / 4, NT);
+    const int rq = rvk / 4;                          // items per row
+    const int ni = kMergeRows * rq;
+    const int nmax = maxrec;
+    f32x4 acc4[IPT];
+    const float* base[IPT];
+    int nr[IPT];
+    int rowi[IPT];
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int q = tid + NT * k;
+      const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
+      const int qq = row % qpk, hq = c * qpk + qq;
+      rowi[k] = row;
+      nr[k] = (q < ni && 4 * r4 < rv) ? rinfo[row][1] : 0;
+      base[k] = p.rec + ((int64_t)g * (p.P + p.batch) + rinfo[row][0]) * p.rec_stride + 2 * nq + hq * p.rvp + 4 * r4;
+      acc4[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int i = 0; i < nmax; ++i) {
+      f32x4 v[IPT];
+#pragma unroll
+      for (int k = 0; k < IPT; ++k)
+        v[k] = i < nr[k] ? *(const f32x4*)(base[k] + (int64_t)i * p.rec_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const float wi = i < nr[k] ? wts[rowi[k] * wpitch + i] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc4[k][e] = fmaf(v[k][e], wi, acc4[k][e]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int q = tid + NT * k;
+      if (q < ni) {
+        const int row = q / rq, r4 = q - row * rq;
+        *(f32x4*)(a + row * apitch + 4 * r4) = acc4[k];
       }
     }
   }
@@ -818,51 +890,50 @@ __global__ void __launch_bounds__(256) palu_merge_kernel(const DecodeParams p, i
 
   LT* out = (LT*)p.out;
   if constexpr (F32) {
-    // 16 rows x DH outputs, one per thread per pass
-    for (int o = tid; o < kMergeRows * DH; o += 256) {
-      const int row = o / DH, d = o - row * DH;
+    for (int o = tid; o < kMergeRows * kMergeCols; o += NT) {
+      const int row = o / kMergeCols, d = o - row * kMergeCols;
       const int b = b0 + row / qpk, qq = row % qpk;
       if (b >= p.batch) continue;
       const float* ar = a + row * apitch;
       float sacc = 0.f;
       for (int r = 0; r < rv; ++r) sacc = fmaf(ar[r], to_f32(bs[r * BP + d]), sacc);
       const int h = (g * ng + c) * qpk + qq;
-      out[((int64_t)b * p.H + h) * DH + d] = from_f32<LT>(sacc);
+      out[((int64_t)b * p.H + h) * DH + cb * kMergeCols + d] = from_f32<LT>(sacc);
     }
   } else {
     typedef typename Vec8<LT>::type op_t;
+    if (w >= kMergeCols / 16) return;                 // one wave per 16 columns
     const int kq = l >> 4, s = l & 15;
-    for (int nt = w; nt < DH / 16; nt += 4) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < rvk / 32; ++ks) {
-        const float* ap = a + s * apitch + 32 * ks + 8 * kq;     // A: row s, k = 8 kq .. +7
-        op_t ahi, alo;
+    const int nt = w;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < rvk / 32; ++ks) {
+      const float* ap = a + s * apitch + 32 * ks + 8 * kq;     // A: row s, k = 8 kq .. +7
+      op_t ahi, alo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = ap[e];
-          const LT hi = from_f32<LT>(v);
-          ahi[e] = hi;
-          alo[e] = from_f32<LT>(v - to_f32(hi));
-        }
-        // B: rows (ranks) 32 ks + 8 kq + s/4 (+4), columns 16 nt + 4 (s%4) .. +3
-        const int ra = 32 * ks + 8 * kq + (s >> 2), rb = ra + 4;
-        const int col = 16 * nt + 4 * (s & 3);
-        i16x4 va = ds_read_tr16(bs + ra * BP + col);
-        i16x4 vb = ds_read_tr16(bs + rb * BP + col);
-        typedef short s8 __attribute__((ext_vector_type(8)));
-        s8 both = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-        const op_t bop = __builtin_bit_cast(op_t, both);
-        acc = mfma16x16x32(ahi, bop, acc);
-        acc = mfma16x16x32(alo, bop, acc);
+      for (int e = 0; e < 8; ++e) {
+        const float v = ap[e];
+        const LT hi = from_f32<LT>(v);
+        ahi[e] = hi;
+        alo[e] = from_f32<LT>(v - to_f32(hi));
       }
+      // B: rows (ranks) 32 ks + 8 kq + s/4 (+4), columns 16 nt + 4 (s%4) .. +3
+      const int ra = 32 * ks + 8 * kq + (s >> 2), rb = ra + 4;
+      const int col = 16 * nt + 4 * (s & 3);
+      i16x4 va = ds_read_tr16(bs + ra * BP + col);
+      i16x4 vb = ds_read_tr16(bs + rb * BP + col);
+      typedef short s8 __attribute__((ext_vector_type(8)));
+      s8 both = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+      const op_t bop = __builtin_bit_cast(op_t, both);
+      acc = mfma16x16x32(ahi, bop, acc);
+      acc = mfma16x16x32(alo, bop, acc);
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * kq + e;
-        const int b = b0 + row / qpk, qq = row % qpk;
-        if (b < p.batch) {
-          const int h = (g * ng + c) * qpk + qq;
-          out[((int64_t)b * p.H + h) * DH + 16 * nt + s] = from_f32<LT>(acc[e]);
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * kq + e;
+      const int b = b0 + row / qpk, qq = row % qpk;
+      if (b < p.batch) {
+        const int h = (g * ng + c) * qpk + qq;
+        out[((int64_t)b * p.H + h) * DH + cb * kMergeCols + 16 * nt + s] = from_f32<LT>(acc[e]);
       }
     }
   }
@@ -955,13 +1026,18 @@ template <class LT>
 static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
   const int nq = k.kv_per_group * k.q_per_kv;
   if (kMergeRows % k.q_per_kv != 0) return hipErrorInvalidValue;
+  if (k.head_dim != 64 && k.head_dim != 128) return hipErrorInvalidValue;
+  // 16-byte record loads: the value part of a record starts at 2 * nq floats
+  // and records are nq * (2 + rvp) floats apart (rvp is a multiple of 16)
+  if (nq % 2 != 0 || k.rv_max > kMergeMaxRank) return hipErrorInvalidValue;
   const int bpc = kMergeRows / k.q_per_kv;
   const int rvk = (k.rv_max + 31) / 32 * 32;
-  const size_t smem = (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
-                      (size_t)rvk * (k.head_dim + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT);
-  dim3 grid(p.G * k.kv_per_group, (p.batch + bpc - 1) / bpc);
+  const size_t smem = (size_t)kMergeRows * (p.P + 1) * sizeof(float) +
+                      (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
+                      (size_t)rvk * (kMergeCols + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT);
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
+  dim3 grid(p.G * k.kv_per_group * (k.head_dim / kMergeCols), (p.batch + bpc - 1) / bpc);
   auto kern = k.head_dim == 64 ? palu_merge_kernel<LT, 64> : palu_merge_kernel<LT, 128>;
-  if (k.head_dim != 64 && k.head_dim != 128) return hipErrorInvalidValue;
   if (smem > 64 * 1024) {
     // raise the dynamic-LDS limit once per instantiation (to the largest size
     // this kernel can ask for)
@@ -975,7 +1051,7 @@ static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipS
     const hipError_t e = k.head_dim == 64 ? err64 : err128;
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(256), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
+  hipLaunchKernelGGL(kern, grid, dim3(kMergeThreads), smem, stream, p, nq, k.q_per_kv, k.kv_per_group);
   return hipGetLastError();
 }
 
