@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # passes, calibrated against a plain copy of known size; valid only for the
 # kernel sources it was measured on (their hash is stored beside the figures).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "palu_decode_kernel_llama2_7b_traffic.json")
-KERNEL_SOURCES = ["decode.hip", "decode.h", "common.h"]
+KERNEL_SOURCES = ["decode.hip", "decode_mha.hip", "decode.h", "common.h"]
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, AMD published
 METRIC = "decode attn tokens/s and latent GB/s (% of HBM peak) at Llama-2-7B shape"
 

@@ -44,9 +44,17 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpalu.so)")
 
 
+# per-file code-generation options
+FILE_FLAGS = {
+    # MFMA accumulators in VGPRs: the one-wave-per-kv-head kernel keeps its
+    # B_k^T operands (256 registers) in the AGPR file
+    "decode_mha.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")
