@@ -1,33 +1,35 @@
-// Fused decode attention for MHA head-groups on gfx950: one wave per kv head.
+// Fused decode attention for MHA head-groups on gfx950: two waves per kv head.
 //
 // Method: PALU page, section "Low-rank projection decomposition" (K = z_k B_k,
 // V = z_v B_v) and section "Inference flow" (decode: read the latents,
 // rebuild, attend); arXiv 2407.21118v2 abstract (keys rebuilt on the fly,
 // RoPE-based attention, fused kernels).  Same results and split records as
 // palu_decode_kernel; this instantiation covers head-groups of 4 kv heads with
-// one query head each, head_dim 128, ranks <= 256, 16-bit latents, RoPE.
+// one query head each, head_dim 128, ranks <= 256 (multiples of 32), 16-bit
+// latents, RoPE.
 //
 // Design (ours):
-//  * Block = the 4 kv heads of a head-group = 4 waves, one per SIMD, so each
-//    wave has 512 registers: wave c keeps B_k^T of kv head c (128 dims x 256
-//    ranks, 256 registers) for the whole block.  A wave owns whole heads, so
-//    its scores are complete in registers and the online softmax runs inside
-//    the wave: one block barrier per tile.
-//  * 32-token tiles stream HBM -> LDS through LDS DMA, two tiles ahead, into
-//    unpadded XOR-swizzled rows (keys: 16-byte chunk index ^ (row & 15);
-//    values: ^ ((row & 3) << 1)), so MFMA operand reads and transpose reads
-//    are bank-conflict-free and every DMA instruction is fully used.  Key
-//    tiles use a ring of 3 buffers, value tiles a ring of 4: the value tile
-//    of step n is consumed in step n + 1.
-//  * The RoPE angles of a tile (64 frequencies x 32 positions) are formed
-//    once per block into a shared table (each lane advances 8 of them by a
-//    32-token rotation, re-seeded exactly in fp64 at every segment start and
-//    every 64 tiles) one step ahead of use.
-//  * Step n: softmax of tile n-1 (scores kept in registers), P . z_v of tile
-//    n-1 on MFMA, then the key rebuild of tile n (64 MFMA per 16 tokens) with
-//    RoPE and the query dot on the fp32 accumulators.  The running maximum is
-//    raised only when a tile's maximum exceeds it by more than 2^8, so the
-//    accumulator rescale is rare; P <= 2^8 is split into hi + lo 16-bit parts.
+//  * Block = 8 waves, two per SIMD; wave w owns kv head c = w % 4 and the
+//    frequency half w / 4 (32 rotation frequencies, both RoPE halves: 64 of
+//    the head's 128 dims).  Its B_k^T rows (64 dims x 256 ranks) stay in 128
+//    AGPRs for the whole block, feeding the MFMA A operand directly.
+//  * 32-token tiles stream HBM -> LDS through LDS DMA, two tiles ahead (key
+//    tiles XOR-swizzled per row for conflict-free MFMA operand reads; value
+//    tiles unswizzled).  Key tiles use a ring of 3 buffers, value tiles a
+//    ring of 4: the value tile of step n is consumed in step n + 1.
+//  * Per step n (one barrier): the online softmax of tile n-1 from the two
+//    half-head partial scores both waves of the head left in LDS before the
+//    barrier (summed in a fixed order, so both waves hold identical P);
+//    P z_v of tile n-1 on the VALU (each wave half of the ranks) beside the
+//    key rebuild of tokens 0-15 of tile n on MFMA; the rebuild of tokens
+//    16-31 beside RoPE and the query dot of tokens 0-15; then RoPE and the
+//    dot of tokens 16-31, and the partial scores go to LDS.
+//  * RoPE angles (64 frequencies x 32 positions per tile) are formed once
+//    per block into a shared table, one step ahead, by rotating the previous
+//    tile's entries by 32 positions (re-seeded exactly in fp64 at every
+//    segment start and every 64 tiles).
+//  * The running maximum is raised only when a tile's maximum exceeds it by
+//    more than 2^8, so the accumulator rescale is rare.
 #include "common.h"
 #include "decode.h"
 
@@ -40,23 +42,29 @@ namespace {
 template <class LT_>
 struct MhaCfg {
   typedef LT_ LT;
-  static constexpr int DH = 128, NW = 4, NT = 256, TT = 32;
+  static constexpr int DH = 128, NH = 4, NW = 8, NT = 512, TT = 32;
   static constexpr int RK = 256, RV = 256;
   static constexpr int NKC = RK / 32;          // 32-deep k-chunks of the key rebuild
-  static constexpr int NMT = DH / 16;          // 16-row M-tiles per wave (one kv head)
-  static constexpr int NNT = RV / 16;          // value n-tiles
+  static constexpr int NMT = DH / 32;          // 16-row M-tiles per wave (half a head: 4)
   static constexpr int ROWB = RK * 2;          // bytes per LDS latent row (512)
   static constexpr int TILEB = TT * ROWB;      // 16 KB per latent tile
-  static constexpr int NDT = TILEB / (16 * NT);   // DMA instructions per wave per latent tile (4)
-  static constexpr int NDMA = 2 * NDT + 1;     // per tile step: keys, values, query
+  static constexpr int NDT = TILEB / (16 * NT);   // DMA instructions per wave per latent tile (2)
+  static constexpr int NDMA = 2 * NDT;         // per tile step: keys, values (+ a query at segment starts)
   static constexpr int NKB = 3, NVB = 4;       // key / value buffer rings
   static constexpr int AP = 17;                // angle-table row pitch in 16-byte units (68 floats)
-  static constexpr int STGB = 32 * DH * NW * 2;   // bytes of one staged B_k chunk (32 ranks x 512 columns)
+  static constexpr int STGB = 32 * DH * NH * 2;   // bytes of one staged B_k chunk (32 ranks x 512 columns)
   static_assert(NDT * 16 * NT == TILEB, "tile DMA");
+  static_assert(NT / 32 == 16, "one DMA instruction covers 16 rows");
   static_assert(STGB <= NKB * TILEB && 2 * STGB <= NVB * TILEB, "B_k staging");
 };
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 domain)
+
+// Value-tile swizzle (in 32-byte pairs): a transposed operand read touches
+// rows 8 kq + e (e < 4, plus the +4 rows in a second read), half a wave
+// covering kq = 0, 1; the pair index is XORed with bits 0, 1 and 3 of the row
+// so that those eight rows land in eight distinct 32-byte bank groups.
+__device__ __forceinline__ int vswz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 
 __device__ __forceinline__ void sincos_turns(double t, double theta_turns, float* c, float* s) {
   double rev = t * theta_turns;
@@ -113,7 +121,7 @@ __device__ __forceinline__ float sum16(float x) {
 }  // namespace
 
 template <class LT>
-__global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodeParams p) {
   typedef MhaCfg<LT> C;
   typedef typename Vec8<LT>::type op_t;
   typedef short s8 __attribute__((ext_vector_type(8)));
@@ -122,19 +130,25 @@ __global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodePar
   __shared__ f32x4 angc[2 * C::TT * C::AP];       // [table][position][frequency / 4]
   __shared__ f32x4 angs[2 * C::TT * C::AP];
   __shared__ uint4 qst[3][C::NW][16];             // raw query of each wave, one per tile step in flight
+  __shared__ float sp[2][C::NH][2][C::TT];        // partial scores [tile parity][head][frequency half][token]
+  __shared__ uint4 pst[C::NW][2 * C::NH * C::TT * 2 / 16];   // per wave: P (hi, lo) of the previous tile, [part][head][token]
+  __shared__ uint4 pzero[C::TT * 2 / 16];          // zero rows of the P operand
   __shared__ double theta[C::DH / 2];             // rotation frequencies in turns per token
   __shared__ f32x4 stpc[C::DH / 8], stps[C::DH / 8];   // rotation by 32 tokens per frequency
-  __shared__ int tstart[kMaxBatch + 1];
   __shared__ int wsum[C::NW];
-  __shared__ f32x4 pbc[C::NW][C::TT / 4];          // per wave: P of the previous tile, broadcast to all lanes
+  __shared__ int start_info[2];                   // sequence and first token of the block's first tile
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = w & 3, hf = w >> 2;               // kv head, frequency half
   const int kq = l >> 4, s = l & 15;
   const int g = blockIdx.x % p.G, pb = blockIdx.x / p.G;
   const int batch = p.batch;
 
   // ---------------------------------------------------------------- tile prefix sums
+  // (no table is kept: block (0, 0) writes the tile starts of every sequence
+  // to the workspace header, every block notes where its first tile lies)
+  int total;
   {
     constexpr int MAXPER = kMaxBatch / C::NT;
     const int per = cdiv(batch, C::NT);
@@ -159,29 +173,41 @@ __global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodePar
       if (l >= d) incl += o;
     }
     if (l == 63) wsum[w] = incl;
-    __syncthreads();
-    int run = incl - sacc;
-    for (int i = 0; i < w; ++i) run += wsum[i];
-#pragma unroll
-    for (int i = 0; i < MAXPER; ++i) {
-      const int bb = tid * per + i;
-      if (i < per && bb < batch) tstart[bb] = run;
-      run += loc[i];
-    }
-    if (tid == C::NT - 1) tstart[batch] = run;
+    if (tid < C::TT * 2 / 16) pzero[tid] = uint4{0u, 0u, 0u, 0u};
     if (tid < C::DH / 2) {
       const double th = exp2(-(2.0 * tid / C::DH) * log2(p.rope_base)) * 0.15915494309189535;
       theta[tid] = th;
-      float c, sn;
-      sincos_turns(32.0, th, &c, &sn);
-      ((float*)stpc)[tid] = c;
-      ((float*)stps)[tid] = sn;
+      float cv, sv;
+      sincos_turns(32.0, th, &cv, &sv);
+      ((float*)stpc)[tid] = cv;
+      ((float*)stps)[tid] = sv;
     }
     __syncthreads();
-  }
-  const int total = tstart[batch];
-  if (g == 0 && pb == 0) {
-    for (int i = tid; i <= batch; i += C::NT) p.hdr[i] = tstart[i];
+    int all = 0, before = 0;
+    for (int i = 0; i < C::NW; ++i) {
+      all += wsum[i];
+      before += i < w ? wsum[i] : 0;
+    }
+    total = all;
+    const int tpb0 = cdiv(total, p.P);
+    const int nb0 = pb * tpb0;
+    int run = before + incl - sacc;
+    const bool hdr = (g == 0 && pb == 0);
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      const int bb = tid * per + i;
+      if (i < per && bb < batch) {
+        if (hdr) p.hdr[bb] = run;
+        // the sequence holding tile nb0 (non-empty: it owns tiles [run, run + loc))
+        if (nb0 >= run && nb0 < run + loc[i]) {
+          start_info[0] = bb;
+          start_info[1] = (nb0 - run) * C::TT;
+        }
+      }
+      run += loc[i];
+    }
+    if (hdr && tid == C::NT - 1) p.hdr[batch] = total;
+    __syncthreads();
   }
   const int tpb = cdiv(total, p.P);
   const int n_begin = pb * tpb;
@@ -194,14 +220,16 @@ __global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodePar
   const uint8_t* zk_seq = p.zk + p.goff_k[g];
   const uint8_t* zv_seq = p.zv + p.goff_v[g];
   const int64_t sbk = p.seq_bytes_k, sbv = p.seq_bytes_v;
-  const int h = g * C::NW + w;                    // query head of this wave (one per kv head)
+  const int h = g * C::NH + c;                    // query head of this wave (one per kv head)
 
-  // ---------------------------------------------------------------- B_k^T of kv head w into registers
-  op_t breg[C::NKC][C::NMT];   // [k-chunk][M-tile]
+  // ---------------------------------------------------------------- B_k^T rows of this wave into AGPRs
+  // M-tile mt = 2j + half: dims half*64 + 32*hf + 16j + (0..15), i.e. rotation
+  // frequencies 32*hf + 16j + (0..15) in both RoPE halves
+  op_t breg[C::NKC][C::NMT];
   {
     const LT* Bg = (const LT*)p.Bk + p.boff_k[g];   // [rk][4 * DH]
-    constexpr int W = C::NW * C::DH;
-    constexpr int NSI = C::STGB / (16 * C::NT);     // DMA instructions per wave per staged chunk (8)
+    constexpr int W = C::NH * C::DH;
+    constexpr int NSI = C::STGB / (16 * C::NT);     // DMA instructions per wave per staged chunk (4)
     uint8_t* const slots[3] = {(uint8_t*)zkb, (uint8_t*)zvb, (uint8_t*)zvb + C::STGB};
     auto stage = [&](int slot, int kc) __attribute__((always_inline)) {
 #pragma unroll
@@ -216,8 +244,8 @@ __global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodePar
       const LT* sb = (const LT*)slots[slot];
 #pragma unroll
       for (int mt = 0; mt < C::NMT; ++mt) {
-        const int j = mt >> 1, hh = mt & 1;
-        const int i0 = w * C::DH + hh * (C::DH / 2) + 16 * j;
+        const int j = mt >> 1, half = mt & 1;
+        const int i0 = c * C::DH + half * (C::DH / 2) + 32 * hf + 16 * j;
         // (the rank is a multiple of 32: every staged row is a real row of B_k)
         const i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * W + i0 + 4 * (s & 3));
         const i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * W + i0 + 4 * (s & 3));
@@ -253,217 +281,272 @@ __global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodePar
 
   // ---------------------------------------------------------------- per-lane constants
   // DMA slots: instruction m of wave w fills 16-byte slots (m*NW + w)*64 + l of
-  // a tile = row q >> 5, physical chunk q & 31, holding the logical chunk
-  // given by the swizzle; chunks past a row's data load chunk 0 (finite, and
-  // multiplied by zero rows of B_k or ignored by the merge).
-  // (row, key chunk byte, value chunk byte) of DMA slot m of this lane
-  auto dslot = [&](int m, int& row, int& ck, int& cv) __attribute__((always_inline)) {
-    const int q = (m * C::NW + w) * 64 + l;
+  // a tile = row q >> 5, physical chunk q & 31.  Key rows hold logical chunk
+  // (physical ^ (row & 15)), so that the 16 token rows of an MFMA operand
+  // read fall in distinct banks; value rows hold logical chunk
+  // (physical ^ 2 vswz(row)), so that the 16 rows of a transposed read do.
+  // Chunks past a row's data load chunk 0 (finite, and multiplied by zero
+  // rows of B_k or ignored by the merge).
+  auto dslot = [&](int m, int ln, int& row, int& ck, int& cv) __attribute__((always_inline)) {
+    const int q = (m * C::NW + w) * 64 + ln;
     const int pc = q & 31;
     row = q >> 5;
-    const int lck = pc ^ (row & 15), lcv = pc ^ ((row & 3) << 1);
+    const int lck = pc ^ (row & 15);
+    const int lcv = pc ^ (2 * vswz(row));
     ck = 16 * (lck < cprk ? lck : 0);
     cv = 16 * (lcv < cprv ? lcv : 0);
   };
-  unsigned koff[C::NDT], voff[C::NDT];          // byte offsets inside a full tile
-#pragma unroll
-  for (int m = 0; m < C::NDT; ++m) {
-    int row, ck, cv;
-    dslot(m, row, ck, cv);
-    koff[m] = (unsigned)(row * pk + ck);
-    voff[m] = (unsigned)(row * pv + cv);
-  }
-  // key operand reads: token row 16u + s, logical chunk 4 kc + kq
-  const int sh = s >> 2, sl = s & 3;
-  int kaddr[4];
-#pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) kaddr[b4] = s * C::ROWB + 16 * (kq ^ sl) + 64 * (b4 ^ sh);
-  // value reads: lane l accumulates ranks 4l .. 4l+3 (logical chunk l/2, half l%2)
-  int vofs[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) vofs[r] = 16 * ((l >> 1) ^ (2 * r)) + 8 * (l & 1);
-  // angle-table writer: position tau, frequency quads f4a and f4a + 8
-  const int tau = tid & 31, f4a = tid >> 5;
+  // Per-lane indices and LDS addresses are re-derived inside the tile loop
+  // from an opaque copy of the thread index, where they are used: kept alive
+  // across the loop, a dozen of them would not fit beside the MFMA
+  // accumulators, and a spilled one costs a scratch reload whose wait would
+  // also drain the tile DMA in flight.
+  struct Lane { int t, l, s, kq; };
+  auto lane = [&]() __attribute__((always_inline)) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    Lane r;
+    r.t = t;
+    r.l = t & 63;
+    r.s = t & 15;
+    r.kq = (t >> 4) & 3;
+    return r;
+  };
+  // key operand reads: token row 16u + s, logical chunk 4 kc + kq; chunk quad
+  // b4 of the row sits at 64 * (b4 ^ (s >> 2)): one base, XORed per use
+  auto kbase_of = [&](const Lane& ln) __attribute__((always_inline)) {
+    return ln.s * C::ROWB + 16 * (ln.kq ^ (ln.s & 3)) + 64 * (ln.s >> 2);
+  };
 
   // ---------------------------------------------------------------- tile cursors (wave-uniform)
-  // A cursor walks the block's tiles in order: tile n of sequence b starts at
-  // token t0 of a history of L tokens; empty sequences hold no tiles.
+  // The DMA cursor names tile m of the block's range: sequence b, first
+  // token t0 of a history of L tokens (empty sequences hold no tiles), and
+  // the HBM addresses of its latent rows.  It runs two tiles ahead of the
+  // tile being rebuilt.  The tiles behind it are carried as info words
+  // (sequence, valid tokens, segment flags), shifted along each step, so
+  // that the per-step scalar work stays small: the scalar unit is shared by
+  // all waves of a compute unit, and every wave runs this control.
+  constexpr int F_START = 1 << 24, F_END = 1 << 25;
   auto len_of = [&](int b) __attribute__((always_inline)) {
     int L = sload_i32(p.seq_lens + b);
     return L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
   };
-  struct Cur { int n, b, t0, L; };
-  Cur c0;
-  {
-    int b = 0;
-    while (tstart[b + 1] <= n_begin) ++b;
-    b = __builtin_amdgcn_readfirstlane(b);
-    c0.n = n_begin;
-    c0.b = b;
-    c0.t0 = __builtin_amdgcn_readfirstlane((n_begin - tstart[b]) * C::TT);
-    c0.L = len_of(b);
-  }
-  auto advance = [&](Cur& c) __attribute__((always_inline)) {
-    ++c.n;
-    c.t0 += C::TT;
-    if (c.t0 >= c.L && c.n < n_end) {
-      int b = c.b + 1, L = len_of(b);
+  struct DCur { int b, t0, L, st; const uint8_t* kb; const uint8_t* vb; };
+  auto dma_addr = [&](DCur& d) __attribute__((always_inline)) {
+    d.kb = zk_seq + (int64_t)d.b * sbk + (int64_t)d.t0 * pk;
+    d.vb = zv_seq + (int64_t)d.b * sbv + (int64_t)d.t0 * pv;
+  };
+  DCur cd;
+  cd.b = __builtin_amdgcn_readfirstlane(start_info[0]);
+  cd.t0 = __builtin_amdgcn_readfirstlane(start_info[1]);
+  cd.L = len_of(cd.b);
+  cd.st = F_START;   // (the block's first tile starts a segment)
+  dma_addr(cd);
+  // info word of the cursor's tile: b | valid tokens << 16 | F_START (the
+  // first tile of a segment: its query is loaded) | F_END (the last tile of
+  // its history: its record is written; the block's last tile, handled by
+  // the drain step, is the other segment end)
+  auto info_of = [&](const DCur& d) __attribute__((always_inline)) {
+    const int rem = d.L - d.t0;
+    return d.b | (min(rem, C::TT) << 16) | d.st | (rem <= C::TT ? F_END : 0);
+  };
+  // to the next tile (only called while there is one in the range)
+  auto advance = [&](DCur& d) __attribute__((always_inline)) {
+    d.t0 += C::TT;
+    d.kb += C::TT * pk;
+    d.vb += C::TT * pv;
+    d.st = 0;
+    if (d.t0 >= d.L) {
+      int b = d.b + 1, L = len_of(b);
       while (L == 0) L = len_of(++b);
-      c.b = b;
-      c.L = L;
-      c.t0 = 0;
+      d.b = b;
+      d.L = L;
+      d.t0 = 0;
+      d.st = F_START;
+      dma_addr(d);
     }
-  };
-  auto seg_start = [&](const Cur& c) __attribute__((always_inline)) { return c.t0 == 0 || c.n == n_begin; };
-  auto seg_end = [&](const Cur& c) __attribute__((always_inline)) { return c.t0 + C::TT >= c.L || c.n == n_end - 1; };
-
-  auto issue = [&](const Cur& c) __attribute__((always_inline)) {
-    const uint8_t* kb = zk_seq + (int64_t)c.b * sbk + (int64_t)c.t0 * pk;
-    const uint8_t* vb = zv_seq + (int64_t)c.b * sbv + (int64_t)c.t0 * pv;
-    const unsigned kdst = lds_addr(zkb) + (unsigned)((c.n % C::NKB) * C::TILEB);
-    const unsigned vdst = lds_addr(zvb) + (unsigned)((c.n % C::NVB) * C::TILEB);
-    const int lim = c.L - 1 - c.t0;
-    if (lim >= C::TT - 1) {
-#pragma unroll
-      for (int m = 0; m < C::NDT; ++m) dma16s(kb, koff[m], kdst + 16u * ((m * C::NW + w) * 64));
-#pragma unroll
-      for (int m = 0; m < C::NDT; ++m) dma16s(vb, voff[m], vdst + 16u * ((m * C::NW + w) * 64));
-    } else {
-      // last tile of a history: rows past it repeat its last row
-#pragma unroll
-      for (int m = 0; m < C::NDT; ++m) {
-        int row, ck, cv;
-        dslot(m, row, ck, cv);
-        dma16s(kb, (unsigned)(min(row, lim) * pk + ck), kdst + 16u * ((m * C::NW + w) * 64));
-      }
-#pragma unroll
-      for (int m = 0; m < C::NDT; ++m) {
-        int row, ck, cv;
-        dslot(m, row, ck, cv);
-        dma16s(vb, (unsigned)(min(row, lim) * pv + cv), vdst + 16u * ((m * C::NW + w) * 64));
-      }
-    }
-    // this wave's query (256 bytes, lanes 0-15; loaded at every step so that
-    // every step issues the same number of DMA instructions)
-    const uint8_t* qb = (const uint8_t*)p.q + ((int64_t)c.b * p.H + h) * (C::DH * 2);
-    if (l < 16) dma16s(qb, 16u * l, lds_addr(&qst[c.n % 3][w][0]));
   };
 
-  // Angle table of tile c.n from the table of tile c.n - 1 (same entries of
-  // this lane, rotated by 32 positions), or seeded exactly.  The previous
-  // entries and the rotation are read first (ang_fetch) so that their LDS
-  // latency passes while other work runs.
-  struct AngIn { f32x4 pc0, pc1, ps0, ps1, rc0, rc1, rs0, rs1; };
-  auto ang_fetch = [&](const Cur& c, AngIn& in) __attribute__((always_inline)) {
-    const f32x4* pc = angc + ((c.n - 1) & 1) * (C::TT * C::AP) + tau * C::AP;
-    const f32x4* ps = angs + ((c.n - 1) & 1) * (C::TT * C::AP) + tau * C::AP;
-    in.pc0 = pc[f4a];
-    in.pc1 = pc[f4a + 8];
-    in.ps0 = ps[f4a];
-    in.ps1 = ps[f4a + 8];
-    in.rc0 = stpc[f4a];
-    in.rc1 = stpc[f4a + 8];
-    in.rs0 = stps[f4a];
-    in.rs1 = stps[f4a + 8];
-  };
-  auto angles = [&](const Cur& c, const AngIn& in, bool have_prev) __attribute__((always_inline)) {
-    f32x4 oc0, oc1, os0, os1;
-    if (!have_prev || seg_start(c) || ((c.n - n_begin) & 63) == 0) {
-      // exact seed at this tile's first position
+  // Tile and value tile m of the DMA cursor into their ring slots: four DMA
+  // instructions per wave (keys, values; two each), issued one at a time
+  // between the MFMAs of a window so that the eight waves do not queue them
+  // all at once.  Instruction i covers rows 16i + (2w + l/32); in the last
+  // tile of a history, rows past it repeat its last row.
+  struct DmaPlan { const uint8_t* kb; const uint8_t* vb; unsigned kdst, vdst, koff[2], voff[2]; };
+  auto dma_plan = [&](const DCur& d, int m, const Lane& ln) __attribute__((always_inline)) {
+    DmaPlan q;
+    q.kb = d.kb;
+    q.vb = d.vb;
+    q.kdst = lds_addr(zkb) + (unsigned)((m % C::NKB) * C::TILEB) + 16u * (w * 64);
+    q.vdst = lds_addr(zvb) + (unsigned)((m % C::NVB) * C::TILEB) + 16u * (w * 64);
+    const int lim = d.L - 1 - d.t0;
+    int row, ck, cv;
+    dslot(0, ln.l, row, ck, cv);   // (the swizzles of row + 16 are those of row)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float cv, sv;
-        sincos_turns((double)(c.t0 + tau), theta[4 * f4a + i], &cv, &sv);
-        oc0[i] = cv;
-        os0[i] = sv;
-        sincos_turns((double)(c.t0 + tau), theta[4 * (f4a + 8) + i], &cv, &sv);
-        oc1[i] = cv;
-        os1[i] = sv;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        oc0[i] = in.pc0[i] * in.rc0[i] - in.ps0[i] * in.rs0[i];
-        os0[i] = in.ps0[i] * in.rc0[i] + in.pc0[i] * in.rs0[i];
-        oc1[i] = in.pc1[i] * in.rc1[i] - in.ps1[i] * in.rs1[i];
-        os1[i] = in.ps1[i] * in.rc1[i] + in.pc1[i] * in.rs1[i];
-      }
+    for (int i = 0; i < C::NDT; ++i) {
+      const int r = min(row + 16 * i, lim);
+      q.koff[i] = (unsigned)(r * pk + ck);
+      q.voff[i] = (unsigned)(r * pv + cv);
     }
-    f32x4* tc = angc + (c.n & 1) * (C::TT * C::AP) + tau * C::AP;
-    f32x4* ts = angs + (c.n & 1) * (C::TT * C::AP) + tau * C::AP;
-    tc[f4a] = oc0;
-    tc[f4a + 8] = oc1;
-    ts[f4a] = os0;
-    ts[f4a + 8] = os1;
+    return q;
+  };
+  auto dma_piece = [&](const DmaPlan& q, int i) __attribute__((always_inline)) {
+    if (i < C::NDT) dma16s(q.kb, q.koff[i], q.kdst + 16u * (i * C::NW * 64));
+    else dma16s(q.vb, q.voff[i - C::NDT], q.vdst + 16u * ((i - C::NDT) * C::NW * 64));
+  };
+  // the query of a segment's first tile m (256 bytes, lanes 0-15), with its tile
+  auto dma_query = [&](const DCur& d, int m, const Lane& ln) __attribute__((always_inline)) {
+    const uint8_t* qb = (const uint8_t*)p.q + ((int64_t)d.b * p.H + h) * (C::DH * 2);
+    if (ln.l < 16) dma16s(qb, 16u * ln.l, lds_addr(&qst[m % 3][w][0]));
+  };
+  auto issue = [&](const DCur& d, int m, int info) __attribute__((always_inline)) {
+    const Lane ln = lane();
+    if (info & F_START) dma_query(d, m, ln);
+    const DmaPlan q = dma_plan(d, m, ln);
+#pragma unroll
+    for (int i = 0; i < 2 * C::NDT; ++i) dma_piece(q, i);
+  };
+
+  // Angle table of tile cr.n: entries (position t & 31, frequencies
+  // 4 (t >> 5) .. +3) rotated by 32 positions from the same entries of the
+  // previous table, or seeded exactly in fp64.
+  auto ang_rotate = [&](int m, const Lane& ln) __attribute__((always_inline)) {
+    const int e = (ln.t & 31) * C::AP + (ln.t >> 5);
+    const f32x4 pc = angc[((m - 1) & 1) * (C::TT * C::AP) + e];
+    const f32x4 ps = angs[((m - 1) & 1) * (C::TT * C::AP) + e];
+    const f32x4 rc = stpc[ln.t >> 5], rs = stps[ln.t >> 5];
+    f32x4 oc, os;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      oc[i] = pc[i] * rc[i] - ps[i] * rs[i];
+      os[i] = ps[i] * rc[i] + pc[i] * rs[i];
+    }
+    angc[(m & 1) * (C::TT * C::AP) + e] = oc;
+    angs[(m & 1) * (C::TT * C::AP) + e] = os;
+  };
+  auto ang_seed = [&](int m, int t0) __attribute__((always_inline)) {
+    const Lane ln = lane();
+    const int tau = ln.t & 31, f4 = ln.t >> 5;
+    const int e = tau * C::AP + f4;
+    f32x4 oc, os;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float cv, sv;
+      sincos_turns((double)(t0 + tau), theta[4 * f4 + i], &cv, &sv);
+      oc[i] = cv;
+      os[i] = sv;
+    }
+    angc[(m & 1) * (C::TT * C::AP) + e] = oc;
+    angs[(m & 1) * (C::TT * C::AP) + e] = os;
   };
 
   // ---------------------------------------------------------------- running state
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};         // ranks 4l .. 4l+3 of sum_t P_t z_v[t]
-  float m_run = -INFINITY, l_run = 0.f;
-  float qlo[4][4], qhi[4][4];
-  float sc0 = 0.f, sc1 = 0.f;                     // scores of the previous tile
-  Cur prev = c0;
-  float* const pb_w = (float*)&pbc[w][0];         // this wave's P of the previous tile
+  // Softmax state and the P z_v accumulators cover all four heads in every
+  // wave: the softmax lane layout is (head l / 16, tokens l % 16 and
+  // 16 + l % 16); the P z_v accumulators hold D[head][rank] of the 16x16 MFMA
+  // tiles of ranks 32 w + 16 nt + (0..15), rows 0-3 (lanes 0-15) being the
+  // heads.  The softmax denominator is kept as per-lane partial sums, reduced
+  // over the head's 16 lanes when a record is written.
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float m_run = -INFINITY, l_lane = 0.f;
+  float qlo[2][4], qhi[2][4];
+  uint8_t* const pw = (uint8_t*)&pst[w][0];       // this wave's P (hi, lo) of the previous tile
 
-  // online softmax of the previous tile; its P goes to pb_w
-  auto softmax_prev = [&]() __attribute__((always_inline)) {
-    const float x0 = (prev.t0 + s < prev.L) ? sc0 : -INFINITY;
-    const float x1 = (prev.t0 + 16 + s < prev.L) ? sc1 : -INFINITY;
-    // every row of the wave holds the same 16 token pairs: the maximum is uniform
-    const float tmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(max16(fmaxf(x0, x1)))));
-    if (tmax > m_run + kTau) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);
-      l_run *= alpha;
+  // P as a 16-bit (hi, lo) pair for the MFMA: hi + lo carries P to about 2^-17
+  auto store_p = [&](const Lane& ln, float p0, float p1) __attribute__((always_inline)) {
+    const LT h0 = (LT)p0, h1 = (LT)p1;
+    const LT g0 = (LT)(p0 - (float)h0), g1 = (LT)(p1 - (float)h1);
+    LT* pt = (LT*)pw + ln.kq * C::TT;
+    pt[ln.s] = h0;
+    pt[16 + ln.s] = h1;
+    pt[C::NH * C::TT + ln.s] = g0;
+    pt[C::NH * C::TT + 16 + ln.s] = g1;
+  };
+  // Online softmax of the previous tile for the four heads.  A head's score
+  // is the sum of both half-head partials (fixed order).  The running maximum
+  // of a head is raised only when the tile holds a score above it by more
+  // than kTau: the common path forms P with the current maximum and flags
+  // such lanes; softmax_fix (rare) then raises the maxima, rescales and forms
+  // P again.
+  struct Sm { float x0, x1, p0, p1; bool up; };
+  auto softmax_fast = [&](int m, int info, Sm& sm, const Lane& ln) __attribute__((always_inline)) {
+    const int s = ln.s;
+    const float* sq = &sp[m & 1][ln.kq][0][0];
+    const float x0 = sq[s] + sq[C::TT + s];
+    const float x1 = sq[16 + s] + sq[C::TT + 16 + s];
+    const int nv = (info >> 16) & 63;              // valid tokens of the tile (1..32)
+    sm.x0 = s < nv ? x0 : -INFINITY;
+    sm.x1 = 16 + s < nv ? x1 : -INFINITY;
+    sm.up = fmaxf(sm.x0, sm.x1) > m_run + kTau;
+    sm.p0 = __builtin_amdgcn_exp2f(sm.x0 - m_run);
+    sm.p1 = __builtin_amdgcn_exp2f(sm.x1 - m_run);
+    store_p(ln, sm.p0, sm.p1);
+  };
+  auto softmax_fix = [&](Sm& sm, const Lane& ln) __attribute__((always_inline)) {
+    const float tmax = max16(fmaxf(sm.x0, sm.x1));
+    const float mnew = tmax > m_run + kTau ? tmax : m_run;
+    // (alpha is exactly 1 for a head whose maximum stays; 0 on a segment's first tile)
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+    m_run = mnew;
+    l_lane *= alpha;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] *= alpha;
-      m_run = tmax;
+    for (int e = 0; e < 4; ++e) {
+      const float ae = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alpha), 16 * e));
+      acc[0][e] *= ae;
+      acc[1][e] *= ae;
     }
-    const float p0 = __builtin_amdgcn_exp2f(x0 - m_run);
-    const float p1 = __builtin_amdgcn_exp2f(x1 - m_run);
-    l_run += sum16(p0 + p1);
-    if (kq == 0) {
-      pb_w[s] = p0;
-      pb_w[16 + s] = p1;
+    sm.p0 = __builtin_amdgcn_exp2f(sm.x0 - mnew);
+    sm.p1 = __builtin_amdgcn_exp2f(sm.x1 - mnew);
+    store_p(ln, sm.p0, sm.p1);
+  };
+
+  // P z_v of the previous tile on MFMA: A = P (rows 0-3 = heads, rows 4-15
+  // zero), B = value tile columns 32 w + 16 nt + (0..15) read transposed.
+  auto pv_mfma = [&](const uint8_t* zv, const Lane& ln) __attribute__((always_inline)) {
+    const int r = ln.s;
+    const uint8_t* ah = r < C::NH ? pw + r * (2 * C::TT) + 16 * ln.kq : (const uint8_t*)pzero + 16 * ln.kq;
+    const uint8_t* al = r < C::NH ? ah + C::NH * C::TT * 2 : ah;
+    const op_t phi = *(const op_t*)ah;
+    const op_t plo = *(const op_t*)al;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      // rows 8 kq + r / 4 (+ 4), ranks 32 w + 16 nt + 4 (r & 3) .. +3: the
+      // 32-byte pair 2 w + nt of the row, swizzled
+      const int r0 = 8 * ln.kq + (r >> 2);
+      const int pair = 2 * w + nt;
+      const uint8_t* zb0 = zv + r0 * C::ROWB + 32 * (pair ^ vswz(r0)) + 8 * (r & 3);
+      const uint8_t* zb1 = zv + (r0 + 4) * C::ROWB + 32 * (pair ^ vswz(r0 + 4)) + 8 * (r & 3);
+      const i16x4 lo = ds_read_tr16(zb0);
+      const i16x4 hi = ds_read_tr16(zb1);
+      const s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const op_t bz = __builtin_bit_cast(op_t, both);
+      acc[nt] = mfma16x16x32(phi, bz, acc[nt]);
+      acc[nt] = mfma16x16x32(plo, bz, acc[nt]);
     }
   };
 
-  // P z_v of the previous tile for tokens 4k .. 4k+3 (P broadcast from LDS)
-  auto pv_part = [&](const uint8_t* zv, const f32x4& pq, int k) __attribute__((always_inline)) {
+  auto record_prev = [&](int info) __attribute__((always_inline)) {
+    const Lane ln = lane();
+    const float lsum = sum16(l_lane);
+    float* rec = p.rec + ((int64_t)g * (p.P + batch) + pb + (info & 0xFFFF)) * p.rec_stride;
+    if (ln.l < 16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * k + i;
-      const float pt = pq[i];
-      const uint2 z = *(const uint2*)(zv + t * C::ROWB + vofs[t & 3]);
-      if constexpr (std::is_same<LT, _Float16>::value) {
-        const _Float16* zh = (const _Float16*)&z;
-        acc[0] = fmaf(pt, (float)zh[0], acc[0]);
-        acc[1] = fmaf(pt, (float)zh[1], acc[1]);
-        acc[2] = fmaf(pt, (float)zh[2], acc[2]);
-        acc[3] = fmaf(pt, (float)zh[3], acc[3]);
-      } else {
-        acc[0] = fmaf(pt, __uint_as_float(z.x << 16), acc[0]);
-        acc[1] = fmaf(pt, __uint_as_float(z.x & 0xFFFF0000u), acc[1]);
-        acc[2] = fmaf(pt, __uint_as_float(z.y << 16), acc[2]);
-        acc[3] = fmaf(pt, __uint_as_float(z.y & 0xFFFF0000u), acc[3]);
-      }
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < C::NH; ++e) rec[2 * C::NH + e * p.rvp + 32 * w + 16 * nt + ln.s] = acc[nt][e];
     }
-  };
-
-  auto record_prev = [&]() __attribute__((always_inline)) {
-    float* rec = p.rec + ((int64_t)g * (p.P + batch) + pb + prev.b) * p.rec_stride;
-    *(f32x4*)(rec + 2 * C::NW + w * p.rvp + 4 * l) = acc;
-    if (l == 0) {
-      rec[2 * w] = m_run;
-      rec[2 * w + 1] = l_run;
+    if (w == 0 && ln.s == 0) {
+      rec[2 * ln.kq] = m_run;
+      rec[2 * ln.kq + 1] = lsum;
     }
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
-    l_run = 0.f;
+    l_lane = 0.f;
   };
 
-  // RoPE on the rebuilt keys of one 16-token half and the query dot (pairs of
-  // frequency blocks j0 .. j1-1)
-  auto rope_part = [&](const f32x4 (&kt)[C::NMT], const f32x4 (&cj)[4], const f32x4 (&sj)[4], int j0, int j1,
+  // RoPE on the rebuilt keys of one 16-token half and the query dot
+  auto rope_part = [&](const f32x4 (&kt)[C::NMT], const f32x4 (&cj)[2], const f32x4 (&sj)[2], int j0, int j1,
                        float part) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
@@ -480,124 +563,228 @@ __global__ void __launch_bounds__(256, 1) palu_decode_mha_kernel(const DecodePar
     return part;
   };
 
-  // ---------------------------------------------------------------- pipeline
-  Cur cd = c0;                 // next tile to load
-  issue(cd);
-  advance(cd);
-  if (cd.n < n_end) { issue(cd); advance(cd); }
-  Cur ca = c0;                 // next angle table
-  {
-    AngIn in0;
-    angles(ca, in0, false);
-  }
-  advance(ca);
-  Cur cc = c0;                 // tile to rebuild
+  // segment start: rotate this wave's query to its position, pre-scaled
+  auto load_query = [&](int m, int info) __attribute__((always_inline)) {
+    const int b = info & 0xFFFF;
+    const int pos = p.q_pos ? sload_i32(p.q_pos + b) : len_of(b) - 1;
+    const LT* qr = (const LT*)&qst[m % 3][w][0];
+    const Lane ln = lane();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = 32 * hf + 16 * j + 4 * ln.kq + e;
+        float cs, sn;
+        sincos_turns((double)pos, theta[f], &cs, &sn);
+        const float a = to_f32(qr[f]), bq = to_f32(qr[f + C::DH / 2]);
+        qlo[j][e] = (a * cs - bq * sn) * p.qscale;
+        qhi[j][e] = (a * sn + bq * cs) * p.qscale;
+      }
+    }
+  };
 
-  for (int n = n_begin; n <= n_end; ++n) {
-    if (n < n_end) {
+  // ---------------------------------------------------------------- pipeline
+  // Step n: tile n's keys are rebuilt and scored, tile n - 1 goes through
+  // the softmax and P z_v, tile n + 1's angle table is formed and tile n + 2
+  // is loaded.  One barrier per step.  Within a step: window A = keys of
+  // tokens 0-15 on MFMA beside the softmax and the next angle table; window
+  // B = keys of tokens 16-31 beside RoPE + dot of tokens 0-15; then P z_v on
+  // MFMA beside RoPE + dot of tokens 16-31.
+  // tiles n_begin and n_begin + 1 (info words of the current and next tile)
+  int i_c = info_of(cd), i_a = 0, i_p = 0, t0_a = 0;
+  issue(cd, n_begin, i_c);
+  ang_seed(n_begin, cd.t0);
+  if (n_begin + 1 < n_end) {
+    advance(cd);
+    i_a = info_of(cd);
+    t0_a = cd.t0;
+    issue(cd, n_begin + 1, i_a);
+    if (n_begin + 2 < n_end) advance(cd);
+  }
+
+  // lane indices of the tile loop (the addresses derived from them stay in
+  // registers across it)
+  const Lane lnk = {tid, l, s, kq};
+  // (ALL2: tile n + 2 exists, known at compile time in the steady state)
+  auto step = [&](int n, auto have_t, auto had_t, auto all2_t) __attribute__((always_inline)) {
+    constexpr bool HAVE = decltype(have_t)::value, HAD = decltype(had_t)::value, ALL2 = decltype(all2_t)::value;
+    if (HAVE) {
       if (n + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
     }
-    barrier();   // tile n and angle table n visible; every wave finished step n - 1
-    const bool have = n < n_end, had = n > n_begin;
-    AngIn ain;
-    const bool do_ang = ca.n < n_end;
-    if (do_ang) ang_fetch(ca, ain);
-    if (have && seg_start(cc)) {
-      // segment start: rotate this wave's query to its position, pre-scaled
-      const int pos = p.q_pos ? sload_i32(p.q_pos + cc.b) : cc.L - 1;
-      const LT* qr = (const LT*)&qst[cc.n % 3][w][0];
+    barrier();   // tile n, angle table n and the partial scores of tile n - 1 are visible
+    // tile n + 1 (if any) gets an exact angle table at a segment start and
+    // every 64 tiles
+    const bool seed = n + 1 < n_end && ((i_a & F_START) || ((n + 1 - n_begin) & 63) == 0);
+    if (HAVE && (i_c & F_START)) load_query(n, i_c);
+    const Lane ln = lnk;
+    // tile n + 2: its DMA instructions go out between the MFMAs of window A
+    // (where there is no window A, here); a waiting count of NDMA at the next
+    // step stays safe with a query load in front of them
+    const bool load2 = ALL2 || n + 2 < n_end;
+    DmaPlan dq;
+    int i_d = 0, t0_d = 0;
+    if (load2) {
+      i_d = info_of(cd);
+      t0_d = cd.t0;
+      if (i_d & F_START) dma_query(cd, n + 2, ln);
+      dq = dma_plan(cd, n + 2, ln);
+      if (n + 3 < n_end) advance(cd);   // (the cursor never walks past the range)
+      if (!HAVE) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int i = 0; i < 2 * C::NDT; ++i) dma_piece(dq, i);
+      }
+    }
+    Sm sm;
+    f32x4 k0[C::NMT], k1[C::NMT];
+    const uint8_t* zk = (const uint8_t*)zkb + (n % C::NKB) * C::TILEB;
+    const int kbase = kbase_of(ln);
+    // key operand of chunk kc of token half u (read two chunks ahead)
+    auto bload = [&](int u, int kc) __attribute__((always_inline)) {
+      return *(const op_t*)(zk + (kbase ^ (64 * (kc & 3))) + 256 * (kc >> 2) + u * 16 * C::ROWB);
+    };
+    // angle entries of this lane's token, frequency quads 8 hf + kq + 4 j
+    const f32x4* tc = angc + (n & 1) * (C::TT * C::AP) + ln.s * C::AP + 8 * hf + ln.kq;
+    const f32x4* ts = angs + (n & 1) * (C::TT * C::AP) + ln.s * C::AP + 8 * hf + ln.kq;
+    f32x4 ca0[2], sa0[2], ca1[2], sa1[2];
+    // The windows are laid out by hand: after every MFMA a small, fixed
+    // piece of the other work, with scheduling fences between the pieces so
+    // that the VALU and LDS work stays spread between the MFMAs of its wave.
+    if (HAVE) {
+      // window A: keys of tokens 0-15 beside the softmax of the previous tile
+      // and the angle table of the next one
+      float ra0, rb0, ra1, rb1;
+      f32x4 apc, aps, arc, ars, oc, os;
+      LT h0, h1, g0, g1;
+      const float* sq = &sp[(n - 1) & 1][ln.kq][0][0];
+      const int nv = (i_p >> 16) & 63;                 // valid tokens of the previous tile
+      const int ae = (ln.t & 31) * C::AP + (ln.t >> 5);
+      LT* pt = (LT*)pw + ln.kq * C::TT;
+      auto work = [&](int slot) __attribute__((always_inline)) {
+        if (HAD) {
+          if (slot == 0) {
+            ra0 = sq[ln.s];
+            rb0 = sq[C::TT + ln.s];
+            ra1 = sq[16 + ln.s];
+            rb1 = sq[C::TT + 16 + ln.s];
+          }
+          if (slot == 8) { sm.x0 = ra0 + rb0; sm.x1 = ra1 + rb1; }
+          if (slot == 9) {
+            sm.x0 = ln.s < nv ? sm.x0 : -INFINITY;
+            sm.x1 = 16 + ln.s < nv ? sm.x1 : -INFINITY;
+          }
+          if (slot == 10) sm.up = fmaxf(sm.x0, sm.x1) > m_run + kTau;
+          if (slot == 11) sm.p0 = __builtin_amdgcn_exp2f(sm.x0 - m_run);
+          if (slot == 12) sm.p1 = __builtin_amdgcn_exp2f(sm.x1 - m_run);
+          if (slot == 13) { h0 = (LT)sm.p0; h1 = (LT)sm.p1; }
+          if (slot == 14) g0 = (LT)(sm.p0 - (float)h0);
+          if (slot == 15) g1 = (LT)(sm.p1 - (float)h1);
+          if (slot == 16) {
+            pt[ln.s] = h0;
+            pt[16 + ln.s] = h1;
+            pt[C::NH * C::TT + ln.s] = g0;
+            pt[C::NH * C::TT + 16 + ln.s] = g1;
+          }
+        }
+        // angle table of tile n + 1 by rotation (where that tile is seeded or
+        // does not exist, the seed overwrites these entries or nobody reads
+        // them: table (n + 1) & 1 is not read in this step)
+        if (slot == 1) {
+          apc = angc[(n & 1) * (C::TT * C::AP) + ae];
+          aps = angs[(n & 1) * (C::TT * C::AP) + ae];
+          arc = stpc[ln.t >> 5];
+          ars = stps[ln.t >> 5];
+        }
+        if (slot >= 18 && slot < 22) {
+          const int i = slot - 18;
+          oc[i] = apc[i] * arc[i] - aps[i] * ars[i];
+          os[i] = aps[i] * arc[i] + apc[i] * ars[i];
+        }
+        if (slot == 22) {
+          angc[((n + 1) & 1) * (C::TT * C::AP) + ae] = oc;
+          angs[((n + 1) & 1) * (C::TT * C::AP) + ae] = os;
+        }
+        // angles of tokens 0-15 for window B
+        if (slot % 6 == 3 && slot / 6 < 2 * C::NDT && load2) dma_piece(dq, slot / 6);
+        if (slot == 24) ca0[0] = tc[0];
+        if (slot == 25) sa0[0] = ts[0];
+        if (slot == 26) ca0[1] = tc[4];
+        if (slot == 27) sa0[1] = ts[4];
+      };
+      op_t bq[3];
+      bq[0] = bload(0, 0);
+      bq[1] = bload(0, 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int f = 16 * j + 4 * kq + e;
-          float cs, sn;
-          sincos_turns((double)pos, theta[f], &cs, &sn);
-          const float a = to_f32(qr[f]), bq = to_f32(qr[f + C::DH / 2]);
-          qlo[j][e] = (a * cs - bq * sn) * p.qscale;
-          qhi[j][e] = (a * sn + bq * cs) * p.qscale;
+      for (int kc = 0; kc < C::NKC; ++kc) {
+#pragma unroll
+        for (int mt = 0; mt < C::NMT; ++mt) {
+          k0[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k0[mt]);
+          if (mt == 0 && kc + 2 < C::NKC) bq[(kc + 2) % 3] = bload(0, kc + 2);
+          work(4 * kc + mt);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    } else if (HAD) {
+      softmax_fast(n - 1, i_p, sm, ln);
     }
-    if (had) softmax_prev();
-    if (cd.n < n_end) { issue(cd); advance(cd); }
-    if (do_ang) { angles(ca, ain, true); advance(ca); }
-
-    const uint8_t* zk = (const uint8_t*)zkb + (cc.n % C::NKB) * C::TILEB;
-    const uint8_t* zv = (const uint8_t*)zvb + (prev.n % C::NVB) * C::TILEB;
-    const f32x4* tc = angc + (cc.n & 1) * (C::TT * C::AP) + s * C::AP + kq;
-    const f32x4* ts = angs + (cc.n & 1) * (C::TT * C::AP) + s * C::AP + kq;
-    f32x4 k0[C::NMT], k1[C::NMT];
-    // window A: keys of tokens 0-15 on MFMA beside P z_v of the previous tile;
-    // the operands of window B and the angles of tokens 0-15 are fetched here
-    op_t bopb[C::NKC];
-    auto prefetch_b = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int kc = 0; kc < C::NKC; ++kc)
-        bopb[kc] = *(const op_t*)(zk + kaddr[kc & 3] + 256 * (kc >> 2) + 16 * C::ROWB);
-    };
-    auto window_a = [&](bool with_pv) __attribute__((always_inline)) {
-      op_t bop[C::NKC];
-#pragma unroll
-      for (int kc = 0; kc < C::NKC; ++kc) bop[kc] = *(const op_t*)(zk + kaddr[kc & 3] + 256 * (kc >> 2));
-      prefetch_b();
-#pragma unroll
-      for (int kc = 0; kc < C::NKC; ++kc) {
-#pragma unroll
-        for (int mt = 0; mt < C::NMT; ++mt)
-          k0[mt] = mfma16x16x32(breg[kc][mt], bop[kc], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k0[mt]);
-        if (with_pv) pv_part(zv, *(const f32x4*)(pb_w + 4 * kc), kc);
-      }
-      // issue pattern: every MFMA followed by two VALU (the P z_v FMAs)
-#pragma unroll
-      for (int i = 0; i < C::NKC * C::NMT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-    };
-    if (have && had) {
-      window_a(true);
-    } else if (have) {
-      window_a(false);
-    } else if (had) {
-#pragma unroll
-      for (int kc = 0; kc < C::NKC; ++kc) pv_part(zv, *(const f32x4*)(pb_w + 4 * kc), kc);
+    if (HAD) {
+      if (__builtin_amdgcn_ballot_w64(sm.up)) softmax_fix(sm, ln);
+      l_lane += sm.p0 + sm.p1;
     }
-    if (had && seg_end(prev)) record_prev();
-    if (have) {
-      // window B: keys of tokens 16-31 on MFMA beside RoPE + dot of tokens 0-15;
-      // the angles of tokens 16-31 are fetched here
-      f32x4 ca0[4], sa0[4], ca1[4], sa1[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ca0[j] = tc[4 * j];
-        sa0[j] = ts[4 * j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ca1[j] = tc[16 * C::AP + 4 * j];
-        sa1[j] = ts[16 * C::AP + 4 * j];
-      }
+    if (HAVE) {
+      // window B: keys of tokens 16-31 beside RoPE + dot of tokens 0-15
       float part = 0.f;
+      float klo, khi;
+      op_t bq[3];
+      bq[0] = bload(1, 0);
+      bq[1] = bload(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kc = 0; kc < C::NKC; ++kc) {
+        const int j = kc >> 2, e = kc & 3;
+        const float ka = k0[2 * j][e], kb = k0[2 * j + 1][e];
 #pragma unroll
-        for (int mt = 0; mt < C::NMT; ++mt)
-          k1[mt] = mfma16x16x32(breg[kc][mt], bopb[kc], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k1[mt]);
-        if (kc % 2 == 1) part = rope_part(k0, ca0, sa0, kc / 2, kc / 2 + 1, part);
+        for (int mt = 0; mt < C::NMT; ++mt) {
+          k1[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k1[mt]);
+          if (mt == 0) klo = ka * ca0[j][e] - kb * sa0[j][e];
+          if (mt == 1) khi = ka * sa0[j][e] + kb * ca0[j][e];
+          if (mt == 2) part = fmaf(qhi[j][e], khi, fmaf(qlo[j][e], klo, part));
+          if (mt == 3 && kc + 2 < C::NKC) bq[(kc + 2) % 3] = bload(1, kc + 2);
+          if (mt == 3 && kc >= 4) {
+            // angles of tokens 16-31 for the tail
+            if (kc == 4) ca1[0] = tc[16 * C::AP];
+            if (kc == 5) sa1[0] = ts[16 * C::AP];
+            if (kc == 6) ca1[1] = tc[16 * C::AP + 4];
+            if (kc == 7) sa1[1] = ts[16 * C::AP + 4];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      // issue pattern: every MFMA followed by two VALU (RoPE and dot of tokens 0-15)
-#pragma unroll
-      for (int i = 0; i < C::NKC * C::NMT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      const float sc0 = rows4_sum(part);
+      if (HAD) pv_mfma((const uint8_t*)zvb + ((n - 1) % C::NVB) * C::TILEB, ln);
+      const float sc1 = rows4_sum(rope_part(k1, ca1, sa1, 0, 2, 0.f));
+      if (ln.kq == 0) {
+        sp[n & 1][c][hf][ln.s] = sc0;
+        sp[n & 1][c][hf][16 + ln.s] = sc1;
       }
-      sc0 = rows4_sum(part);
-      sc1 = rows4_sum(rope_part(k1, ca1, sa1, 0, 4, 0.f));
-      prev = cc;
-      advance(cc);
+    } else if (HAD) {
+      pv_mfma((const uint8_t*)zvb + ((n - 1) % C::NVB) * C::TILEB, ln);
     }
-  }
+    if (HAD && (!HAVE || (i_p & F_END))) record_prev(i_p);
+    if (seed) ang_seed(n + 1, t0_a);
+    i_p = i_c;
+    i_c = i_a;
+    i_a = i_d;
+    t0_a = t0_d;
+  };
+
+  const std::true_type yes{};
+  const std::false_type no{};
+  step(n_begin, yes, no, no);
+  int n = n_begin + 1;
+  for (; n + 2 < n_end; ++n) step(n, yes, yes, yes);
+  for (; n < n_end; ++n) step(n, yes, yes, no);
+  step(n_end, no, yes, no);
 }
 
 bool mha_supported(const DecodeKey& k, const DecodeParams& p) {
@@ -606,12 +793,12 @@ bool mha_supported(const DecodeKey& k, const DecodeParams& p) {
     return false;
   for (int j = 0; j < p.G; ++j)
     if (p.rk[j] % 32 != 0) return false;   // B_k is staged in whole 32-row chunks
-  return true;
+  return p.rvp >= 256;                     // every wave writes its 32 value ranks of the record
 }
 
 hipError_t launch_decode_mha(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
                              hipEvent_t t1) {
-  const dim3 grid(p.G * p.P), block(256);
+  const dim3 grid(p.G * p.P), block(512);
   if (k.elt == Elt::F16) {
     if (t0 && t1)
       hipExtLaunchKernelGGL(palu_decode_mha_kernel<_Float16>, grid, block, 0, stream, t0, t1, 0, p);
