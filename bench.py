@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # HBM bytes per launch of the main kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes, calibrated against a plain copy of known size; valid only for the
 # kernel sources it was measured on (their hash is stored beside the figures).
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "palu_decode_kernel_llama2_7b_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "palu_decode_mha_kernel_llama2_7b_traffic.json")
 KERNEL_SOURCES = ["decode.hip", "decode_mha.hip", "decode.h", "common.h"]
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, AMD published
 METRIC = "decode attn tokens/s and latent GB/s (% of HBM peak) at Llama-2-7B shape"
@@ -160,6 +160,19 @@ def copy_calibration(nbytes: int, reps: int):
           flush=True)
 
 
+def main_kernel_name(wl) -> str:
+    """Name of the decode kernel the library runs for a workload: the fused
+    MHA-group kernel where it applies (16-bit latents, head_dim 128, groups of
+    4 kv heads with one query head each, RoPE, ranks multiples of 32 up to 256),
+    the general split-attention kernel otherwise."""
+    import palu_inputs as PI
+    r = PI.ranks(wl)
+    mha = (wl.latent in ("f16", "bf16") and wl.head_dim == 128 and wl.kv_per_group == 4
+           and wl.n_q_heads == wl.n_kv_heads and wl.use_rope
+           and all(int(x) % 32 == 0 and int(x) <= 256 for x in r))
+    return "palu_decode_mha_kernel (fused, MHA head-groups)" if mha else "palu_decode_kernel (split attention)"
+
+
 def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str = TRAFFIC_FILE):
     """Derive HBM bytes per main-kernel launch from four rocprofv3 --pmc runs
     under prof_dir (FETCH_SIZE / WRITE_SIZE of this benchmark, and of the
@@ -176,9 +189,10 @@ def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str 
 
     scale_r = copy_bytes / (1024 * med([v for v in values("copy_FETCH_SIZE", "copyBuffer") if v > 1024]))
     scale_w = copy_bytes / (1024 * med([v for v in values("copy_WRITE_SIZE", "copyBuffer") if v > 1024]))
-    rd = med(values("FETCH_SIZE", "palu_decode_kernel")) * 1024 * scale_r
-    wr = med(values("WRITE_SIZE", "palu_decode_kernel")) * 1024 * scale_w
-    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "kernel": "palu_decode_kernel",
+    # (both decode kernels carry "palu_decode" in their names; the merge kernel does not)
+    rd = med(values("FETCH_SIZE", "palu_decode")) * 1024 * scale_r
+    wr = med(values("WRITE_SIZE", "palu_decode")) * 1024 * scale_w
+    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "kernel": "palu_decode",
            "read_bytes_per_launch": int(round(rd)), "write_bytes_per_launch": int(round(wr)),
            "fetch_scale": round(scale_r, 5), "write_scale": round(scale_w, 5),
            "how": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches), "
@@ -287,7 +301,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "palu_decode_kernel (split attention)", "kernel_ms": round(ms_main, 4),
+            "kernel": main_kernel_name(wl), "kernel_ms": round(ms_main, 4),
             "algorithmic_bytes": st["latent_bytes"],
             "mfma_frac_f16": round(st["flops"] / (ms_main * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
         },
