@@ -64,6 +64,8 @@ def setup(wl):
     esz = 4 if wl.latent == "f32" else 2
 
     def rows(which, b, j):
+        if wl.latent == "i4":
+            return PI.latent_int4(wl, "k" if which == 0 else "v", b, j, n=max(int(lens[b]), 1))
         a = PI.latent(wl, "k" if which == 0 else "v", b, j, n=int(lens[b]))
         pitch = R.row_pitch(wl.latent, int(ranks[j]))
         out = np.zeros((a.shape[0], pitch // esz), dtype=a.dtype)
@@ -84,7 +86,12 @@ def setup(wl):
     seq_lens = torch.from_numpy(lens).cuda()
     ws = torch.empty(R.decode_workspace_bytes(desc, wl.batch, wl.max_len), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=tdt, device="cuda")
-    latent_bytes = int(sum(int(lens[b]) * int(ranks.sum()) * 2 * esz for b in range(wl.batch)))
+    if wl.latent == "i4":
+        # half a byte per code plus one binary16 scale per 32 elements, keys and values
+        row_bytes = sum(int(r) / 2 + 2 * ((int(r) + 31) // 32) for r in ranks) * 2
+        latent_bytes = int(sum(int(lens[b]) for b in range(wl.batch)) * row_bytes)
+    else:
+        latent_bytes = int(sum(int(lens[b]) * int(ranks.sum()) * 2 * esz for b in range(wl.batch)))
     recon_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * sum(
         2 * int(r) * wl.group_width for r in ranks)
     pv_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * wl.n_q_heads * 2 * int(ranks.max())
@@ -167,10 +174,12 @@ def main_kernel_name(wl) -> str:
     the general split-attention kernel otherwise."""
     import palu_inputs as PI
     r = PI.ranks(wl)
-    mha = (wl.latent in ("f16", "bf16") and wl.head_dim == 128 and wl.kv_per_group == 4
+    q4 = wl.latent == "i4"   # (int4 caches are expanded to 16-bit rows of the rank rounded up to 32 first)
+    mha = ((wl.latent in ("f16", "bf16") or q4) and wl.head_dim == 128 and wl.kv_per_group == 4
            and wl.n_q_heads == wl.n_kv_heads and wl.use_rope
-           and all(int(x) % 32 == 0 and int(x) <= 256 for x in r))
-    return "palu_decode_mha_kernel (fused, MHA head-groups)" if mha else "palu_decode_kernel (split attention)"
+           and all((q4 or int(x) % 32 == 0) and int(x) <= 256 for x in r))
+    name = "palu_decode_mha_kernel (fused, MHA head-groups)" if mha else "palu_decode_kernel (split attention)"
+    return ("palu_dequant_kernel, then " + name) if q4 else name
 
 
 def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str = TRAFFIC_FILE):
@@ -213,10 +222,14 @@ def cpu_baseline(wl, n_seq: int, reps: int = 3):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     lens = PI.lengths(wl)[:n_seq]
-    zk = [[oracle.upcast(PI.latent(wl, "k", b, j, n=int(lens[b])), wl.latent) for b in range(n_seq)]
-          for j in range(wl.n_groups)]
-    zv = [[oracle.upcast(PI.latent(wl, "v", b, j, n=int(lens[b])), wl.latent) for b in range(n_seq)]
-          for j in range(wl.n_groups)]
+
+    def lat(which, b, j):
+        if wl.latent == "i4":
+            packed, scales = PI.latent_int4(wl, which, b, j, n=int(lens[b]))
+            return oracle.int4_latent(packed, scales, int(PI.ranks(wl)[j]), wl.act)
+        return oracle.upcast(PI.latent(wl, which, b, j, n=int(lens[b])), wl.latent)
+    zk = [[lat("k", b, j) for b in range(n_seq)] for j in range(wl.n_groups)]
+    zv = [[lat("v", b, j) for b in range(n_seq)] for j in range(wl.n_groups)]
     Bk = [oracle.upcast(PI.factor(wl, "Bk", j), wl.act) for j in range(wl.n_groups)]
     Bv = [oracle.upcast(PI.factor(wl, "Bv", j), wl.act) for j in range(wl.n_groups)]
     q = oracle.upcast(PI.query(wl), wl.act)[:n_seq]
@@ -274,7 +287,10 @@ def main():
     ms_step = statistics.mean(t_call)
     ms_main = statistics.mean(t_main)
     tokens_per_s = wl.batch / (ms_step * 1e-3)
-    achieved = st["latent_bytes"] / (ms_main * 1e-3) / 1e9
+    # int4 caches: the step is two kernels (expansion, then the decode), so the
+    # rate is taken over the whole call
+    ms_roof = ms_step if wl.latent == "i4" else ms_main
+    achieved = st["latent_bytes"] / (ms_roof * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
     line = {
         "metric": METRIC,
@@ -301,9 +317,10 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": main_kernel_name(wl), "kernel_ms": round(ms_main, 4),
+            "kernel": main_kernel_name(wl), "kernel_ms": round(ms_roof, 4),
+            "decode_kernel_ms": round(ms_main, 4),
             "algorithmic_bytes": st["latent_bytes"],
-            "mfma_frac_f16": round(st["flops"] / (ms_main * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "mfma_frac_f16": round(st["flops"] / (ms_roof * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
         },
     }
     if args.cpu_seqs > 0:

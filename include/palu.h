@@ -178,6 +178,12 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  * Without RoPE the score uses the absorbed query (q_h B_k^T) against z_k and,
  * in all cases, values enter as (softmax . z_v) . B_v; both equal the formula
  * up to rounding.  Arithmetic is binary32 throughout.
+ * I4 latents (act_dtype F16 or BF16): the decode consumes the
+ * dequantised latent code * scale (PALU page, section "Rollout", route C:
+ * quantization on top of the low-rank cache), formed exactly in binary32 and
+ * rounded to nearest even into act_dtype; the rows [0, L_b) of every
+ * sequence are first expanded into the workspace (16-bit rows of the rank
+ * rounded up to 32, zero past the rank), then attended as above.
  *   q          device [batch][H][d_h] act_dtype
  *   cache      latent buffers; rows [0, L_b) of each (b, j) are read
  *   B_k, B_v   device, layout above, act_dtype
@@ -189,10 +195,12 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  *   out        device [batch][H][d_h] act_dtype
  *   workspace  device, at least palu_decode_workspace_bytes(desc, batch,
  *              cache->max_len) bytes, 256-byte aligned; contents are scratch
+ *              (for I4 it includes batch * max_len * sum_j 2 * (ceil32(r_k^j)
+ *              + ceil32(r_v^j)) bytes of expanded latents)
  * batch == 0 is a no-op after the descriptor checks (pointers may be NULL).
  * Errors: INVALID_ARG for null pointers, batch < 0, head counts that do not
  * divide, odd head_dim, rank <= 0, max_len <= 0, non-finite sm_scale,
- * I4 scales missing; WORKSPACE_TOO_SMALL; UNSUPPORTED for shapes without a
+ * I4 scales missing or not 2-byte aligned; WORKSPACE_TOO_SMALL; UNSUPPORTED for shapes without a
  * compiled kernel (palu_last_error names the reason).
  */
 palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,

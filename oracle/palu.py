@@ -36,6 +36,10 @@ Readings where the pages are silent (each is listed in the design doc):
   s16 == 0; the last chunk of a row whose rank is not a multiple of 32 is
   short; codes are 4-bit two's complement, element 2i in the low nibble of
   byte i, rows padded with zero nibbles to a 16-byte multiple.
+* int4 decode: the attention consumes the dequantised latent code * scale
+  rounded once, to nearest even, into the activation format (fp16 or
+  bf16), as the GPU's matrix units take it; everything after that is the
+  plain definition above.
 
 Pins (tests/test_oracle_pins.py): standard attention through
 torch.nn.functional.scaled_dot_product_attention (float64, CPU) in the
@@ -55,7 +59,7 @@ import numpy as np
 __all__ = [
     "upcast", "rope_theta", "rope", "reconstruct", "attend", "attend_partial", "merge_partials",
     "decode_attention", "project", "quant_int4", "pack_int4", "unpack_int4", "dequant_int4",
-    "chunks_per_row",
+    "chunks_per_row", "round_to", "int4_latent",
 ]
 
 QUANT_GROUP = 32
@@ -69,6 +73,32 @@ def upcast(a: np.ndarray, fmt: str) -> np.ndarray:
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
     return np.asarray(a).astype(np.float64)
+
+
+_SIG_BITS = {"f16": 11, "bf16": 8}
+
+
+def round_to(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round fp64 values to nearest (ties to even) at the precision of 'f16'
+    or 'bf16', returned in fp64.  Written from the definition: with
+    x = m * 2^e (0.5 <= |m| < 1), keep rint(m * 2^p) * 2^(e - p) for p
+    significant bits.  Only normal-range values (and zero) are accepted,
+    which holds for every value it is used on here."""
+    x = np.asarray(x, dtype=np.float64)
+    p = _SIG_BITS[fmt]
+    nz = x != 0
+    lo, hi = (2.0 ** -14, 65504.0) if fmt == "f16" else (2.0 ** -126, 3.0e38)
+    assert np.all(np.abs(x[nz]) >= lo) and np.all(np.abs(x) <= hi), "round_to: value outside the normal range"
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, p)), e - p)
+
+
+def int4_latent(packed: np.ndarray, scales: np.ndarray, r: int, act: str) -> np.ndarray:
+    """Latent rows a decode step attends over when the cache holds int4
+    codes: unpack, z_hat = code * scale (exact), rounded to the activation
+    format (the reading stated in the module docstring)."""
+    z = dequant_int4(unpack_int4(packed, r), scales)
+    return round_to(z, act) if act in _SIG_BITS else z
 
 
 # ------------------------------------------------------------------ RoPE

@@ -16,7 +16,14 @@ prefill chunk.  Distributions (one reading, stated in the design doc):
   and A as above every entry of x.A is a sum of d_model products with
   variance 1/d_model each, so N(0, 1) is its distribution; drawing it
   directly keeps multi-terabyte-flop fp64 projections out of the test budget;
-* queries q ~ N(0, 1); prefill activations x ~ N(0, 1).
+* queries q ~ N(0, 1); prefill activations x ~ N(0, 1);
+* stored int4 latents (the decode's input for 'i4' workloads) are drawn as
+  codes and scales directly: codes binomial(14, 1/2) - 7 (integers in
+  [-7, 7] peaked at 0, the shape that quantising normal rows to amax/7
+  steps gives), one binary16 scale per 32 elements uniform in [0.28, 0.45]
+  (amax/7 of 32 standard normal draws lies there in most chunks); pad
+  nibbles past the rank are zero.  Packing them into the documented byte
+  layout is data placement, not quantisation.
 
 Every array comes from its own counter-style stream
 ``PCG64(SeedSequence([seed, stream_tag, *indices]))`` so that any (sequence,
@@ -32,12 +39,12 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "scaled",
     "to_f16", "to_bf16_bits", "to_format",
-    "ranks", "lengths", "factor", "latent", "latent_f32", "query", "prefill_x",
+    "ranks", "lengths", "factor", "latent", "latent_f32", "latent_int4", "query", "prefill_x",
     "prefill_A",
 ]
 
 # stream tags (stable: changing them changes every generated array)
-_T_RANK, _T_LEN, _T_BK, _T_BV, _T_AK, _T_AV, _T_ZK, _T_ZV, _T_Q, _T_X = range(1, 11)
+_T_RANK, _T_LEN, _T_BK, _T_BV, _T_AK, _T_AV, _T_ZK, _T_ZV, _T_Q, _T_X, _T_QK4, _T_QV4 = range(1, 13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -189,6 +196,24 @@ def latent(wl: Workload, which: str, b: int, g: int, n: Optional[int] = None) ->
     """Cached latent of (b, g) in its stored format ('i4' workloads return the
     fp32 values that are to be quantised)."""
     return to_format(latent_f32(wl, which, b, g, n), wl.latent)
+
+
+def latent_int4(wl: Workload, which: str, b: int, g: int, n: Optional[int] = None):
+    """Stored int4 latent of (sequence b, group g): (codes, scales) with codes
+    uint8 [n][16 * ceil(r_g/32)] (4-bit two's complement, element 2i in the
+    low nibble of byte i, zero nibbles past the rank) and scales float16
+    [n][ceil(r_g/32)]; n = max_len by default.  Drawn directly (no
+    quantisation): see the module docstring."""
+    r = int(ranks(wl)[g])
+    n = wl.max_len if n is None else n
+    nc = (r + 31) // 32
+    rng = _rng(wl, _T_QK4 if which == "k" else _T_QV4, b, g)
+    codes = rng.binomial(14, 0.5, size=(n, r)).astype(np.int16) - 7
+    scales = to_f16(rng.uniform(0.28, 0.45, size=(n, nc)).astype(np.float32))
+    nib = np.zeros((n, 32 * nc), dtype=np.uint8)
+    nib[:, :r] = (codes & 0xF).astype(np.uint8)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales
 
 
 def query(wl: Workload) -> np.ndarray:

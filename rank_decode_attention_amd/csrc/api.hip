@@ -122,6 +122,12 @@ struct DecodePlan {
   DecodeKey key;
   int P, rvp, qabs_stride, nq;
   size_t hdr_bytes, rec_bytes, qabs_bytes, total;
+  // int4 latents: the decode runs on a 16-bit copy of the cache in the
+  // workspace (ranks rounded up to 32, rows zero-padded), expanded first
+  bool q4;
+  size_t dense_k_bytes, dense_v_bytes;
+  int64_t dk_pitch[kMaxGroups], dv_pitch[kMaxGroups], dk_goff[kMaxGroups], dv_goff[kMaxGroups];
+  int64_t dk_seq, dv_seq;
 };
 
 Elt elt_of(palu_dtype d) { return d == PALU_F32 ? Elt::F32 : d == PALU_F16 ? Elt::F16 : Elt::BF16; }
@@ -132,17 +138,21 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   if (batch < 0) return fail(PALU_ERR_INVALID_ARG, "batch must be >= 0");
   if (max_len <= 0) return fail(PALU_ERR_INVALID_ARG, "max_len must be positive");
   if (batch > kMaxBatch) return fail(PALU_ERR_UNSUPPORTED, "batch above %d", kMaxBatch);
-  if (d->latent_dtype == PALU_I4)
-    return fail(PALU_ERR_UNSUPPORTED, "int4 latents are not supported by palu_decode_attn yet");
-  if (d->latent_dtype != d->act_dtype)
+  pl->q4 = d->latent_dtype == PALU_I4;
+  if (pl->q4 && d->act_dtype == PALU_F32)
+    return fail(PALU_ERR_UNSUPPORTED, "int4 latents need act_dtype F16 or BF16");
+  if (!pl->q4 && d->latent_dtype != d->act_dtype)
     return fail(PALU_ERR_UNSUPPORTED, "latent_dtype must equal act_dtype for float latents");
+  // (int4: the kernels see 16-bit rows of 32-rounded rank, zero past the rank)
+  auto dense_rank = [&](int r) { return pl->q4 ? (int)roundup(r, 32) : r; };
   int rk_max = 0, rv_max = 0;
   for (int j = 0; j < d->n_groups; ++j) {
-    rk_max = d->rank_k[j] > rk_max ? d->rank_k[j] : rk_max;
-    rv_max = d->rank_v[j] > rv_max ? d->rank_v[j] : rv_max;
+    rk_max = dense_rank(d->rank_k[j]) > rk_max ? dense_rank(d->rank_k[j]) : rk_max;
+    rv_max = dense_rank(d->rank_v[j]) > rv_max ? dense_rank(d->rank_v[j]) : rv_max;
   }
+  if (pl->q4 && (rk_max > 1024 || rv_max > 1024)) return fail(PALU_ERR_UNSUPPORTED, "int4 latents: rank above 1024");
   const int ng = d->n_kv_heads / d->n_groups, qpk = d->n_q_heads / d->n_kv_heads;
-  pl->key = DecodeKey{elt_of(d->latent_dtype), d->head_dim, ng, qpk, rk_max, rv_max, d->use_rope != 0};
+  pl->key = DecodeKey{elt_of(d->act_dtype), d->head_dim, ng, qpk, rk_max, rv_max, d->use_rope != 0};
   int rk_cap = 0, rv_cap = 0;
   if (!decode_supported(pl->key, &rk_cap, &rv_cap))
     return fail(PALU_ERR_UNSUPPORTED,
@@ -163,7 +173,21 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   pl->hdr_bytes = (size_t)roundup((int64_t)(batch + 1) * 4, 256);
   pl->rec_bytes = (size_t)roundup((int64_t)d->n_groups * (P + batch) * pl->nq * (2 + pl->rvp) * 4, 256);
   pl->qabs_bytes = d->use_rope ? 0 : (size_t)roundup((int64_t)batch * d->n_q_heads * pl->qabs_stride * 4, 256);
-  pl->total = pl->hdr_bytes + pl->rec_bytes + pl->qabs_bytes;
+  pl->dense_k_bytes = pl->dense_v_bytes = 0;
+  pl->dk_seq = pl->dv_seq = 0;
+  if (pl->q4) {
+    for (int j = 0; j < d->n_groups; ++j) {
+      pl->dk_pitch[j] = 2 * roundup(d->rank_k[j], 32);
+      pl->dv_pitch[j] = 2 * roundup(d->rank_v[j], 32);
+      pl->dk_goff[j] = pl->dk_seq;
+      pl->dv_goff[j] = pl->dv_seq;
+      pl->dk_seq += (int64_t)max_len * pl->dk_pitch[j];
+      pl->dv_seq += (int64_t)max_len * pl->dv_pitch[j];
+    }
+    pl->dense_k_bytes = (size_t)roundup((int64_t)batch * pl->dk_seq, 256);
+    pl->dense_v_bytes = (size_t)roundup((int64_t)batch * pl->dv_seq, 256);
+  }
+  pl->total = pl->hdr_bytes + pl->rec_bytes + pl->qabs_bytes + pl->dense_k_bytes + pl->dense_v_bytes;
   return PALU_OK;
 }
 
@@ -297,8 +321,41 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   if (workspace_bytes < pl.total)
     return fail(PALU_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
 
+  if (pl.q4) {
+    if (!cache->sk || !cache->sv) return fail(PALU_ERR_INVALID_ARG, "I4 scales are NULL");
+    if (((uintptr_t)cache->sk & 1u) != 0 || ((uintptr_t)cache->sv & 1u) != 0)
+      return fail(PALU_ERR_INVALID_ARG, "I4 scale buffers must be 2-byte aligned");
+  }
   Layout L;
   make_layout(desc, cache->max_len, &L);
+  uint8_t* const dense_k = (uint8_t*)workspace + pl.hdr_bytes + pl.rec_bytes + pl.qabs_bytes;
+  uint8_t* const dense_v = dense_k + pl.dense_k_bytes;
+  if (pl.q4) {
+    // int4 latents -> 16-bit rows (the history of every sequence, keys then values)
+    static_assert(kDqMaxGroups >= kMaxGroups, "group arrays");
+    for (int which = 0; which < 2; ++which) {
+      DequantParams dp;
+      memset(&dp, 0, sizeof(dp));
+      dp.codes = (const uint8_t*)(which ? cache->zv : cache->zk);
+      dp.scales = (const uint8_t*)(which ? cache->sv : cache->sk);
+      dp.out = which ? dense_v : dense_k;
+      dp.seq_lens = seq_lens;
+      dp.batch = batch; dp.G = desc->n_groups; dp.max_len = cache->max_len;
+      dp.seq_c = which ? L.seq_v : L.seq_k;
+      dp.seq_s = which ? L.seq_sv : L.seq_sk;
+      dp.seq_o = which ? pl.dv_seq : pl.dk_seq;
+      for (int j = 0; j < desc->n_groups; ++j) {
+        dp.goff_c[j] = which ? L.goff_v[j] : L.goff_k[j];
+        dp.goff_s[j] = which ? L.soff_v[j] : L.soff_k[j];
+        dp.goff_o[j] = which ? pl.dv_goff[j] : pl.dk_goff[j];
+        dp.rank[j] = which ? desc->rank_v[j] : desc->rank_k[j];
+        dp.nch[j] = (dp.rank[j] + 31) / 32;
+        while ((1 << dp.cs_log2) < dp.nch[j]) ++dp.cs_log2;
+      }
+      hipError_t e = launch_dequant(desc->act_dtype == PALU_F16 ? 1 : 2, dp, stream);
+      if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
+    }
+  }
   DecodeParams p;
   memset(&p, 0, sizeof(p));
   p.q = q; p.zk = (const uint8_t*)cache->zk; p.zv = (const uint8_t*)cache->zv;
@@ -321,6 +378,15 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
     bk += (int64_t)desc->rank_k[j] * w; bv += (int64_t)desc->rank_v[j] * w;
     p.rk[j] = desc->rank_k[j]; p.rv[j] = desc->rank_v[j];
     p.pk[j] = (int)L.pk[j]; p.pv[j] = (int)L.pv[j];
+  }
+  if (pl.q4) {
+    p.zk = dense_k; p.zv = dense_v;
+    p.seq_bytes_k = pl.dk_seq; p.seq_bytes_v = pl.dv_seq;
+    for (int j = 0; j < desc->n_groups; ++j) {
+      p.goff_k[j] = pl.dk_goff[j]; p.goff_v[j] = pl.dv_goff[j];
+      p.pk[j] = (int)pl.dk_pitch[j]; p.pv[j] = (int)pl.dv_pitch[j];
+    }
+    p.zero_padded = 1;
   }
   hipError_t e;
   if (!desc->use_rope) {

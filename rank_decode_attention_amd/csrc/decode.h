@@ -36,6 +36,7 @@ struct DecodeParams {
   int64_t boff_k[kMaxGroups], boff_v[kMaxGroups];   // element offset of B^j inside B_k / B_v
   int rk[kMaxGroups], rv[kMaxGroups];               // ranks
   int pk[kMaxGroups], pv[kMaxGroups];               // row pitches in bytes
+  int zero_padded;          // rows hold zeros from the rank up to the next multiple of 32 (int4 copies)
 };
 
 // Key of a compiled decode-attention instantiation.

@@ -791,8 +791,10 @@ bool mha_supported(const DecodeKey& k, const DecodeParams& p) {
   if (!((k.elt == Elt::F16 || k.elt == Elt::BF16) && k.head_dim == 128 && k.kv_per_group == 4 &&
         k.q_per_kv == 1 && k.rope && k.rk_max <= 256 && k.rv_max <= 256))
     return false;
+  // B_k is staged in whole 32-row chunks: rows past the rank (the last row
+  // repeated) must meet zero latents
   for (int j = 0; j < p.G; ++j)
-    if (p.rk[j] % 32 != 0) return false;   // B_k is staged in whole 32-row chunks
+    if (p.rk[j] % 32 != 0 && !p.zero_padded) return false;
   return p.rvp >= 256;                     // every wave writes its 32 value ranks of the record
 }
 

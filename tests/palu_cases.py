@@ -67,13 +67,16 @@ class LazyLatents:
 
     def __getitem__(self, b):
         L = int(self.lens[b])
+        if self.wl.latent == "i4":
+            packed, scales = PI.latent_int4(self.wl, self.which, b, self.j, n=max(L, 1))
+            return oracle.int4_latent(packed, scales, int(PI.ranks(self.wl)[self.j]), self.wl.act)
         a = PI.latent(self.wl, self.which, b, self.j, n=max(L, 1))
         return oracle.upcast(a, self.wl.latent)
 
 
 def build_decode_case(wl: PI.Workload, q_scale: float = 1.0, lens: Optional[np.ndarray] = None,
                       device="cuda") -> Dict:
-    """Device inputs of one decode step of workload wl (fp16/bf16/fp32 latents)."""
+    """Device inputs of one decode step of workload wl (fp16/bf16/fp32 or int4 latents)."""
     import torch
     import rank_decode_attention_amd as R
     desc = desc_of(wl)
@@ -87,6 +90,8 @@ def build_decode_case(wl: PI.Workload, q_scale: float = 1.0, lens: Optional[np.n
 
     def rows(which, b, j):
         n = int(min(max(lens[b], 1), wl.max_len))
+        if wl.latent == "i4":
+            return PI.latent_int4(wl, "k" if which == 0 else "v", b, j, n=n)
         a = PI.latent(wl, "k" if which == 0 else "v", b, j, n=n)
         return padded_rows(a, wl.latent, int(ranks[j]))
 

@@ -88,7 +88,7 @@ def test_decode_argument_errors(lib):
     assert _call_decode(lib, _desc(), batch=-1) == INVALID
     assert _call_decode(lib, _desc(), max_len=0) == INVALID
     assert _call_decode(lib, _desc(), batch=5000) == UNSUP
-    assert _call_decode(lib, _desc(latent_dtype="i4", act_dtype="f16")) == UNSUP
+    assert _call_decode(lib, _desc(latent_dtype="i4", act_dtype="f32")) == UNSUP
     assert _call_decode(lib, _desc(latent_dtype="f16", act_dtype="bf16")) == UNSUP
     assert _call_decode(lib, _desc(head_dim=96)) == UNSUP                # no kernel for this head_dim
     assert _call_decode(lib, _desc(rank_k=[512] * 8)) == UNSUP          # rank above every compiled cap

@@ -328,9 +328,60 @@ def pin_upcast():
     np.testing.assert_array_equal(O.upcast(np.array([0.1], np.float16), "f16"), [float(np.float16(0.1))])
 
 
+def pin_round_to():
+    """round_to against the library conversions: numpy's float64 -> float16
+    and torch's float32 -> bfloat16 (both round to nearest, ties to even),
+    on random values and on exact ties."""
+    import torch
+    rng = np.random.default_rng(77)
+    # normal-range values of both formats: |x| in [2^-13, 2^13)
+    x = rng.choice([-1.0, 1.0], 4000) * rng.uniform(1.0, 2.0, 4000) * np.exp2(rng.integers(-13, 13, 4000))
+    x = np.concatenate([x, [0.0, 1.0, -1.0]])
+    ties16 = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -(2 + 5 * 2.0 ** -10), 0.75 + 2.0 ** -12])
+    got = O.round_to(np.concatenate([x, ties16]), "f16")
+    want = np.concatenate([x, ties16]).astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, want), "f16 rounding differs from numpy"
+    x32 = x.astype(np.float32).astype(np.float64)   # torch rounds from binary32
+    ties_b = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(4 + 2.0 ** -6), 3 * 2.0 ** -9 + 2.0 ** -17])
+    xb = np.concatenate([x32, ties_b])
+    want_b = torch.from_numpy(xb.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to(xb, "bf16"), want_b), "bf16 rounding differs from torch"
+    # the ties go to the even neighbour
+    assert O.round_to(np.array([1 + 2.0 ** -11]), "f16")[0] == 1.0
+    assert O.round_to(np.array([1 + 3 * 2.0 ** -11]), "f16")[0] == 1 + 2.0 ** -9
+
+
+def pin_int4_latent():
+    """int4_latent over every code and a sweep of binary16 scales, against
+    the library conversion of the exact product; the byte layout against a
+    hand-packed row (codes 1..7, -1..-7, 0 in the documented nibble order)."""
+    import torch
+    codes = np.arange(-7, 8, dtype=np.int8)                       # 15 codes
+    rng = np.random.default_rng(5)
+    s = rng.uniform(0.01, 3.0, 64).astype(np.float16)
+    grid_c = np.tile(codes, 64).reshape(64, 15)
+    # pad each row of 15 codes to a 32-element chunk of zeros
+    full = np.zeros((64, 32), dtype=np.int8)
+    full[:, :15] = grid_c
+    packed = O.pack_int4(full)
+    exact = full.astype(np.float64) * s.astype(np.float64)[:, None]
+    got16 = O.int4_latent(packed, s[:, None], 32, "f16")
+    assert np.array_equal(got16, exact.astype(np.float16).astype(np.float64))
+    gotb = O.int4_latent(packed, s[:, None], 32, "bf16")
+    wantb = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(gotb, wantb)
+    # hand-packed row: element 2i in the low nibble of byte i, two's complement
+    row = bytes([0x21, 0x43, 0x65, 0xF7, 0xDE, 0xBC, 0x9A, 0x00] + [0] * 8)
+    want = [1, 2, 3, 4, 5, 6, 7, -1, -2, -3, -4, -5, -6, -7, 0, 0]
+    got = O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[1.0]], np.float16), 16, "f16")
+    assert got[0].tolist() == want
+    # rank shorter than the chunk: only the first r elements come back
+    assert O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[0.5]], np.float16), 3, "f16").shape == (1, 3)
+
+
 PINS = [pin_absorbed_and_fused_value, pin_mpmath_bruteforce, pin_softmax_closed_forms, pin_rope, pin_gqa,
         pin_split_merge, pin_golden_decode, pin_rope_closed_form_d2, pin_project, pin_int4_golden,
-        pin_int4_properties, pin_upcast]
+        pin_int4_properties, pin_upcast, pin_round_to, pin_int4_latent]
 
 
 @pytest.mark.parametrize("use_rope", [False, True])
@@ -385,6 +436,22 @@ def _merge_no_rescale(parts):
     return sum(p[2] for p in parts) / sum(p[1] for p in parts)
 
 
+def _round_truncate(x, fmt):
+    x = np.asarray(x, dtype=np.float64)
+    p = O._SIG_BITS[fmt]
+    m, e = np.frexp(x)
+    return np.ldexp(np.trunc(np.ldexp(m, p)), e - p)
+
+
+def _round_f16_as_bf16(x, fmt):
+    return O.__dict__["_orig_round"](x, "bf16")
+
+
+def _unpack_nibbles_swapped(packed, r):
+    p = np.asarray(packed, dtype=np.uint8)
+    return O.__dict__["_orig_unpack"](((p << 4) | (p >> 4)).astype(np.uint8), r)
+
+
 MUTANTS = [
     ("rope", _interleaved_rope),
     ("rope", _wrong_sign_rope),
@@ -393,6 +460,9 @@ MUTANTS = [
     ("reconstruct", _reconstruct_dropped_row),
     ("quant_int4", _quant_ties_away),
     ("merge_partials", _merge_no_rescale),
+    ("round_to", _round_truncate),
+    ("round_to", _round_f16_as_bf16),
+    ("unpack_int4", _unpack_nibbles_swapped),
 ]
 
 
@@ -402,6 +472,8 @@ def test_planted_mistakes(name, mutant, monkeypatch):
     monkeypatch.setitem(O.__dict__, "_orig_rope", O.rope)
     monkeypatch.setitem(O.__dict__, "_orig_attend", O.attend)
     monkeypatch.setitem(O.__dict__, "_orig_quant", O.quant_int4)
+    monkeypatch.setitem(O.__dict__, "_orig_round", O.round_to)
+    monkeypatch.setitem(O.__dict__, "_orig_unpack", O.unpack_int4)
     monkeypatch.setattr(O, name, mutant)
     caught = False
     for pin in [lambda: pin_identity_vs_sdpa(True), lambda: pin_identity_vs_sdpa(False)] + PINS:

@@ -32,6 +32,13 @@ SMALL = [
     ("gqa_norope_small", _small("gqa_norope", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
     ("7b_f16_gqa_shape", PI.scaled("gqa_rope", latent="f16", act="f16", batch=2, max_len=96,
                                    fixed_lengths=(96, 50)), None),
+    # int4 latents: expanded to 16-bit rows (rank rounded up to 32), then the
+    # MHA-group kernel (rank 154 -> 160, 100 -> 128) or the split kernel
+    ("int4_small", _small("int4", batch=3, max_len=300, fixed_lengths=(300, 1, 77)), None),
+    ("int4_bf16_r100", _small("int4", act="bf16", rank=100, batch=2, max_len=200, fixed_lengths=(200, 65)), None),
+    ("int4_empty_seq", _small("int4", batch=3, max_len=100, fixed_lengths=(0, 100, 33)), None),
+    ("int4_norope", _small("int4", use_rope=False, batch=2, max_len=160, fixed_lengths=(160, 3)), None),
+    ("int4_gqa", _small("gqa_rope", latent="i4", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
 ]
 
 
@@ -78,6 +85,28 @@ def test_batch_zero_is_noop():
     torch.cuda.synchronize()
 
 
+def test_int4_workspace_and_errors():
+    """int4 latents add their 16-bit expansion (rank rounded up to 32, keys
+    and values) to the workspace; missing scales are an argument error."""
+    import ctypes
+    import rank_decode_attention_amd as R
+    lib = R.load()
+    batch, max_len = 3, 100
+    wl = _small("int4", batch=batch, max_len=max_len)
+    f = R.AttnDesc(32, 32, 128, 8, [154] * 8, latent_dtype="f16", act_dtype="f16")
+    i = R.AttnDesc(32, 32, 128, 8, [154] * 8, latent_dtype="i4", act_dtype="f16")
+    wf = R.decode_workspace_bytes(f, batch, max_len)
+    wi = R.decode_workspace_bytes(i, batch, max_len)
+    dense = batch * max_len * 8 * 2 * 160
+    assert wi == wf + 2 * ((dense + 255) // 256 * 256)
+    case = build_decode_case(wl)
+    c = case["cache"]
+    no_scales = R.LatentCache(c.zk, c.zv, None, None, c.max_len)
+    with pytest.raises(R.PaluError, match="scales"):
+        R.palu_decode_attn(case["desc"], case["q"], no_scales, case["Bk"], case["Bv"], case["seq_lens"], None,
+                           case["sm_scale"], case["out"], case["ws"])
+
+
 def test_deterministic():
     wl = _small("long_b4", batch=2, max_len=2000, ragged=True, name="long_det")
     case = build_decode_case(wl)
@@ -92,6 +121,7 @@ FULL = [
     ("long_b4", [(0, 3), (3, 28)]),
     ("gqa_rope", [(0, 0), (5, 9), (31, 31)]),
     ("gqa_norope", [(0, 1), (17, 20), (31, 30)]),
+    ("int4", [(0, 0), (3, 17), (7, 31)]),
 ]
 
 
