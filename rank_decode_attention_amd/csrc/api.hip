@@ -331,30 +331,32 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   uint8_t* const dense_k = (uint8_t*)workspace + pl.hdr_bytes + pl.rec_bytes + pl.qabs_bytes;
   uint8_t* const dense_v = dense_k + pl.dense_k_bytes;
   if (pl.q4) {
-    // int4 latents -> 16-bit rows (the history of every sequence, keys then values)
+    // int4 latents -> 16-bit rows (the history of every sequence, keys and values)
     static_assert(kDqMaxGroups >= kMaxGroups, "group arrays");
+    DequantParams dp;
+    memset(&dp, 0, sizeof(dp));
+    dp.seq_lens = seq_lens;
+    dp.batch = batch; dp.G = desc->n_groups; dp.max_len = cache->max_len;
     for (int which = 0; which < 2; ++which) {
-      DequantParams dp;
-      memset(&dp, 0, sizeof(dp));
-      dp.codes = (const uint8_t*)(which ? cache->zv : cache->zk);
-      dp.scales = (const uint8_t*)(which ? cache->sv : cache->sk);
-      dp.out = which ? dense_v : dense_k;
-      dp.seq_lens = seq_lens;
-      dp.batch = batch; dp.G = desc->n_groups; dp.max_len = cache->max_len;
-      dp.seq_c = which ? L.seq_v : L.seq_k;
-      dp.seq_s = which ? L.seq_sv : L.seq_sk;
-      dp.seq_o = which ? pl.dv_seq : pl.dk_seq;
+      DequantSide& sd = dp.side[which];
+      sd.codes = (const uint8_t*)(which ? cache->zv : cache->zk);
+      sd.scales = (const uint8_t*)(which ? cache->sv : cache->sk);
+      sd.out = which ? dense_v : dense_k;
+      sd.seq_c = which ? L.seq_v : L.seq_k;
+      sd.seq_s = which ? L.seq_sv : L.seq_sk;
+      sd.seq_o = which ? pl.dv_seq : pl.dk_seq;
       for (int j = 0; j < desc->n_groups; ++j) {
-        dp.goff_c[j] = which ? L.goff_v[j] : L.goff_k[j];
-        dp.goff_s[j] = which ? L.soff_v[j] : L.soff_k[j];
-        dp.goff_o[j] = which ? pl.dv_goff[j] : pl.dk_goff[j];
-        dp.rank[j] = which ? desc->rank_v[j] : desc->rank_k[j];
-        dp.nch[j] = (dp.rank[j] + 31) / 32;
-        while ((1 << dp.cs_log2) < dp.nch[j]) ++dp.cs_log2;
+        sd.goff_c[j] = which ? L.goff_v[j] : L.goff_k[j];
+        sd.goff_s[j] = which ? L.soff_v[j] : L.soff_k[j];
+        sd.goff_o[j] = which ? pl.dv_goff[j] : pl.dk_goff[j];
+        sd.rank[j] = which ? desc->rank_v[j] : desc->rank_k[j];
+        sd.nch[j] = (sd.rank[j] + 31) / 32;
+        sd.magic[j] = (unsigned)(((1ull << 32) + (uint64_t)sd.nch[j] - 1) / (uint64_t)sd.nch[j]);
+        dp.max_nch = sd.nch[j] > dp.max_nch ? sd.nch[j] : dp.max_nch;
       }
-      hipError_t e = launch_dequant(desc->act_dtype == PALU_F16 ? 1 : 2, dp, stream);
-      if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
     }
+    hipError_t e = launch_dequant(desc->act_dtype == PALU_F16 ? 1 : 2, dp, stream);
+    if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
   }
   DecodeParams p;
   memset(&p, 0, sizeof(p));

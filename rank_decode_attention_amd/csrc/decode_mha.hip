@@ -39,12 +39,13 @@
 namespace palu {
 namespace {
 
-template <class LT_>
+template <class LT_, int NKC_>
 struct MhaCfg {
   typedef LT_ LT;
   static constexpr int DH = 128, NH = 4, NW = 8, NT = 512, TT = 32;
-  static constexpr int RK = 256, RV = 256;
-  static constexpr int NKC = RK / 32;          // 32-deep k-chunks of the key rebuild
+  static constexpr int RK = 256, RV = 256;     // rank capacity of an LDS latent row
+  static constexpr int NKC = NKC_;             // 32-deep k-chunks of the key rebuild (rank <= 32 NKC)
+  static_assert(NKC >= 4 && NKC <= RK / 32, "key chunks");
   static constexpr int NMT = DH / 32;          // 16-row M-tiles per wave (half a head: 4)
   static constexpr int ROWB = RK * 2;          // bytes per LDS latent row (512)
   static constexpr int TILEB = TT * ROWB;      // 16 KB per latent tile
@@ -120,9 +121,9 @@ __device__ __forceinline__ float sum16(float x) {
 
 }  // namespace
 
-template <class LT>
+template <class LT, int NKC>
 __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodeParams p) {
-  typedef MhaCfg<LT> C;
+  typedef MhaCfg<LT, NKC> C;
   typedef typename Vec8<LT>::type op_t;
   typedef short s8 __attribute__((ext_vector_type(8)));
   __shared__ uint4 zkb[C::NKB * C::TILEB / 16];
@@ -724,6 +725,9 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // (ranks below 256: the pieces laid out for chunks NKC..7 follow)
+#pragma unroll
+      for (int slot = 4 * C::NKC; slot < 32; ++slot) work(slot);
     } else if (HAD) {
       softmax_fast(n - 1, i_p, sm, ln);
     }
@@ -738,27 +742,36 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       op_t bq[3];
       bq[0] = bload(1, 0);
       bq[1] = bload(1, 1);
+      // piece (kc, mt): RoPE and query dot of rotation pair kc of tokens
+      // 0-15 (eight pairs per lane), and the angles of tokens 16-31
+      auto wb = [&](int kc, int mt) __attribute__((always_inline)) {
+        const int j = kc >> 2, e = kc & 3;
+        const float ka = k0[2 * j][e], kb = k0[2 * j + 1][e];
+        if (mt == 0) klo = ka * ca0[j][e] - kb * sa0[j][e];
+        if (mt == 1) khi = ka * sa0[j][e] + kb * ca0[j][e];
+        if (mt == 2) part = fmaf(qhi[j][e], khi, fmaf(qlo[j][e], klo, part));
+        if (mt == 3 && kc >= 4) {
+          if (kc == 4) ca1[0] = tc[16 * C::AP];
+          if (kc == 5) sa1[0] = ts[16 * C::AP];
+          if (kc == 6) ca1[1] = tc[16 * C::AP + 4];
+          if (kc == 7) sa1[1] = ts[16 * C::AP + 4];
+        }
+      };
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kc = 0; kc < C::NKC; ++kc) {
-        const int j = kc >> 2, e = kc & 3;
-        const float ka = k0[2 * j][e], kb = k0[2 * j + 1][e];
 #pragma unroll
         for (int mt = 0; mt < C::NMT; ++mt) {
           k1[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k1[mt]);
-          if (mt == 0) klo = ka * ca0[j][e] - kb * sa0[j][e];
-          if (mt == 1) khi = ka * sa0[j][e] + kb * ca0[j][e];
-          if (mt == 2) part = fmaf(qhi[j][e], khi, fmaf(qlo[j][e], klo, part));
+          wb(kc, mt);
           if (mt == 3 && kc + 2 < C::NKC) bq[(kc + 2) % 3] = bload(1, kc + 2);
-          if (mt == 3 && kc >= 4) {
-            // angles of tokens 16-31 for the tail
-            if (kc == 4) ca1[0] = tc[16 * C::AP];
-            if (kc == 5) sa1[0] = ts[16 * C::AP];
-            if (kc == 6) ca1[1] = tc[16 * C::AP + 4];
-            if (kc == 7) sa1[1] = ts[16 * C::AP + 4];
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+#pragma unroll
+      for (int kc = C::NKC; kc < 8; ++kc) {
+#pragma unroll
+        for (int mt = 0; mt < C::NMT; ++mt) wb(kc, mt);
       }
       const float sc0 = rows4_sum(part);
       if (HAD) pv_mfma((const uint8_t*)zvb + ((n - 1) % C::NVB) * C::TILEB, ln);
@@ -798,20 +811,37 @@ bool mha_supported(const DecodeKey& k, const DecodeParams& p) {
   return p.rvp >= 256;                     // every wave writes its 32 value ranks of the record
 }
 
+template <class LT, int NKC>
+static void launch_mha_inst(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid(p.G * p.P), block(512);
+  if (t0 && t1)
+    hipExtLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC>), grid, block, 0, stream, t0, t1, 0, p);
+  else
+    hipLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC>), grid, block, 0, stream, p);
+}
+
+template <class LT>
+static void launch_mha_t(int nkc, const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  switch (nkc) {
+    case 4: launch_mha_inst<LT, 4>(p, stream, t0, t1); break;
+    case 5: launch_mha_inst<LT, 5>(p, stream, t0, t1); break;
+    case 6: launch_mha_inst<LT, 6>(p, stream, t0, t1); break;
+    case 7: launch_mha_inst<LT, 7>(p, stream, t0, t1); break;
+    default: launch_mha_inst<LT, 8>(p, stream, t0, t1); break;
+  }
+}
+
 hipError_t launch_decode_mha(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
                              hipEvent_t t1) {
-  const dim3 grid(p.G * p.P), block(512);
-  if (k.elt == Elt::F16) {
-    if (t0 && t1)
-      hipExtLaunchKernelGGL(palu_decode_mha_kernel<_Float16>, grid, block, 0, stream, t0, t1, 0, p);
-    else
-      hipLaunchKernelGGL(palu_decode_mha_kernel<_Float16>, grid, block, 0, stream, p);
-  } else {
-    if (t0 && t1)
-      hipExtLaunchKernelGGL(palu_decode_mha_kernel<__bf16>, grid, block, 0, stream, t0, t1, 0, p);
-    else
-      hipLaunchKernelGGL(palu_decode_mha_kernel<__bf16>, grid, block, 0, stream, p);
-  }
+  // the instance with the fewest 32-deep key chunks that covers every rank
+  // (at least 4)
+  int nkc = (k.rk_max + 31) / 32;
+  nkc = nkc < 4 ? 4 : nkc;
+  if (nkc > 8) return hipErrorInvalidValue;
+  if (k.elt == Elt::F16)
+    launch_mha_t<_Float16>(nkc, p, stream, t0, t1);
+  else
+    launch_mha_t<__bf16>(nkc, p, stream, t0, t1);
   return hipGetLastError();
 }
 

@@ -10,6 +10,8 @@
 #include "common.h"
 #include "quant.h"
 
+#include <type_traits>
+
 namespace palu {
 
 template <class T>
@@ -66,42 +68,98 @@ static hipError_t launch_q(const void* z, int64_t n_rows, int r, int64_t stride,
   return hipGetLastError();
 }
 
-// One thread per (row, chunk slot): 16 bytes of codes and one scale in,
-// 32 values out (four 16-byte stores).  The decode consumes the int4 latent
-// ẑ = code * scale (PALU page, section "Rollout", route C: quantization on
-// top of the low-rank cache); the product is exact in fp32 and is rounded
-// once, to the activation format that the decode's MFMA takes.
+// The chunks (32 elements) of one (sequence, group) block are numbered
+// c = t * nch + chunk; codes, scales and output rows are then plain arrays
+// of chunks (16, 2 and 64 bytes each), and rows t < L are exactly the chunks
+// c < L * nch.  A wave expands 64 consecutive chunks: in round k its lane l
+// takes the 8-element piece (quarter l % 4 of chunk 16 k + l / 4), so that
+// every load and store instruction of the wave covers contiguous memory
+// (256 bytes of codes in, 1 KB out); the four rounds' loads are issued
+// before any is used.  The decode consumes the int4 latent
+// z_hat = code * scale (PALU page, section "Rollout", route C: quantization
+// on top of the low-rank cache); the product is exact in fp32 and is
+// rounded once, to the activation format that the decode's MFMA takes.
+template <class T>
+__device__ __forceinline__ uint4 expand8(unsigned w, float s) {
+  unsigned out[4];
+  if constexpr (std::is_same<T, _Float16>::value) {
+    // packed fp16: the nibble pair (2k, 2k+1) of byte k becomes the halves
+    // 1024 + (q + 8) (bits 0x6400 | (nibble ^ 8)); subtracting 1032 gives q
+    // exactly, and one fp16 multiply rounds q * s to nearest even, which is
+    // the exact product rounded once
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const unsigned lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const h2 s2 = {(_Float16)s, (_Float16)s};
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // bytes [lo byte k, 0, hi byte k, 0]
+      const unsigned sel = (unsigned)k | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
+      const unsigned pr = (__builtin_amdgcn_perm(hi, lo, sel) ^ 0x00080008u) | 0x64006400u;
+      out[k] = __builtin_bit_cast(unsigned, (__builtin_bit_cast(h2, pr) + bias) * s2);
+    }
+  } else {
+    T v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = (int)(w << (28 - 4 * i)) >> 28;   // nibble i, 4-bit two's complement
+      v[i] = from_f32<T>((float)q * s);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = *(const unsigned*)&v[2 * k];
+  }
+  return uint4{out[0], out[1], out[2], out[3]};
+}
+
 template <class T>
 __global__ void __launch_bounds__(256) palu_dequant_kernel(const DequantParams p) {
   const int b = blockIdx.y / p.G, j = blockIdx.y - b * p.G;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int t = (int)(idx >> p.cs_log2), ch = (int)(idx & ((1 << p.cs_log2) - 1));
-  if (t >= p.max_len || ch >= p.nch[j]) return;
+  const DequantSide& d = p.side[blockIdx.z];
+  const unsigned nch = (unsigned)d.nch[j];
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
-  if (t >= L) return;
-  const int nch = p.nch[j];
-  const uint8_t* cr = p.codes + b * p.seq_c + p.goff_c[j] + (int64_t)t * (16 * nch) + 16 * ch;
-  const uint8_t* sr = p.scales + b * p.seq_s + p.goff_s[j] + (int64_t)t * (2 * nch) + 2 * ch;
-  uint8_t* orow = p.out + b * p.seq_o + p.goff_o[j] + (int64_t)t * (64 * nch) + 64 * ch;
-  const uint4 c = *(const uint4*)cr;
-  const float s = (float)*(const _Float16*)sr;
-  const unsigned w[4] = {c.x, c.y, c.z, c.w};
-  T v[32];
+  const unsigned n_chunks = (unsigned)L * nch;
+  const int l = threadIdx.x & 63;
+  const unsigned c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 64 + (l >> 2);   // chunk of round 0
+  if (c0 >= n_chunks) return;
+  const uint8_t* codes = d.codes + b * d.seq_c + d.goff_c[j] + 4 * (l & 3);
+  const uint8_t* scales = d.scales + b * d.seq_s + d.goff_s[j];
+  uint8_t* out = d.out + b * d.seq_o + d.goff_o[j] + 16 * (l & 3);
+  unsigned w[4];
+  float s[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int nib = (int)((w[i >> 3] >> (4 * (i & 7))) & 0xF);
-    const int q = nib >= 8 ? nib - 16 : nib;   // 4-bit two's complement
-    v[i] = from_f32<T>(32 * ch + i < p.rank[j] ? (float)q * s : 0.0f);
+  for (int k = 0; k < 4; ++k) {
+    const unsigned c = c0 + 16 * k;
+    if (c < n_chunks) {
+      w[k] = *(const unsigned*)(codes + 16 * (int64_t)c);
+      s[k] = (float)*(const _Float16*)(scales + 2 * (int64_t)c);
+    }
   }
+  const int tail = d.rank[j] & 31;   // elements in a row's last chunk (0: a whole chunk)
 #pragma unroll
-  for (int k = 0; k < 4; ++k) ((uint4*)orow)[k] = *(const uint4*)&v[8 * k];
+  for (int k = 0; k < 4; ++k) {
+    const unsigned c = c0 + 16 * k;
+    if (c < n_chunks) {
+      uint4 o = expand8<T>(w[k], s[k]);
+      if (tail != 0 && c - __umulhi(c, d.magic[j]) * nch == nch - 1) {
+        // the row's last chunk: zero from the rank on (elements e0 .. e0+7 here)
+        const int nv = tail - 8 * (l & 3);
+        unsigned* h = (unsigned*)&o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          h[q] &= (2 * q < nv ? 0xFFFFu : 0u) | (2 * q + 1 < nv ? 0xFFFF0000u : 0u);
+      }
+      *(uint4*)(out + 64 * (int64_t)c) = o;
+    }
+  }
 }
 
 hipError_t launch_dequant(int out_dtype, const DequantParams& p, hipStream_t stream) {
   if (p.batch == 0 || p.G == 0) return hipSuccess;
-  if (p.cs_log2 < 0 || p.cs_log2 > 5) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)cdiv64((int64_t)p.max_len << p.cs_log2, 256), (unsigned)(p.batch * p.G), 1);
+  const uint64_t chunks = (uint64_t)p.max_len * (uint64_t)p.max_nch;
+  if (chunks * (uint64_t)p.max_nch >= (1ull << 32)) return hipErrorInvalidValue;
+  // 256 chunks per block of 256 threads
+  const dim3 grid((unsigned)cdiv64((int64_t)chunks, 256), (unsigned)(p.batch * p.G), 2);
   if (out_dtype == 1)
     hipLaunchKernelGGL(palu_dequant_kernel<_Float16>, grid, dim3(256), 0, stream, p);
   else if (out_dtype == 2)
