@@ -293,7 +293,7 @@ def main():
     achieved = st["latent_bytes"] / (ms_roof * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
     line = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "llama2_7b" else METRIC.replace("Llama-2-7B", f"{wl.name} workload"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -142,6 +142,24 @@ palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows,
                               int64_t z_row_stride, void* codes, void* scales, hipStream_t stream);
 
 /*
+ * palu_dequant_latent - int4 latent rows to 16-bit rows (quantization on top
+ * of the low-rank cache: PALU page, section "Rollout", route C).  The same
+ * expansion palu_decode_attn applies to an I4 cache before attending.
+ *   codes    device [n_rows][16 * ceil(r/32)] bytes (layout of PALU_I4 above)
+ *   scales   device [n_rows][ceil(r/32)] binary16
+ *   out      device [n_rows][32 * ceil(r/32)] out_dtype (output): element e of
+ *            row i is code * scale of its 32-element chunk, formed exactly in
+ *            binary32 and rounded to nearest even into out_dtype, for e < r;
+ *            0 for r <= e < 32 * ceil(r/32) (pad nibbles are not read as data)
+ * n_rows == 0 is a no-op after the argument checks (pointers may be NULL).
+ * Errors: INVALID_ARG for null pointers, n_rows < 0, r <= 0, codes not
+ * 4-byte, scales not 2-byte or out not 16-byte aligned; UNSUPPORTED for
+ * out_dtype other than F16 / BF16, or n_rows * ceil(r/32)^2 >= 2^32.
+ */
+palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n_rows, int32_t r,
+                                palu_dtype out_dtype, void* out, hipStream_t stream);
+
+/*
  * palu_project - prefill: write the latents of n_tok new tokens of sequence
  * `seq` (PALU page, section "Inference flow", prefill steps 3-4: compute
  * z_k = x A_k, z_v = x A_v and cache them instead of K/V).

@@ -82,14 +82,21 @@ def round_to(x: np.ndarray, fmt: str) -> np.ndarray:
     """Round fp64 values to nearest (ties to even) at the precision of 'f16'
     or 'bf16', returned in fp64.  Written from the definition: with
     x = m * 2^e (0.5 <= |m| < 1), keep rint(m * 2^p) * 2^(e - p) for p
-    significant bits.  Only normal-range values (and zero) are accepted,
-    which holds for every value it is used on here."""
+    significant bits; below the smallest normal (binary16: 2^-14) the
+    quantum stays that of the smallest binade (2^-24), as IEEE gradual
+    underflow has it.  Values that would overflow are rejected (none occur
+    here); bf16 is only used in its normal range."""
     x = np.asarray(x, dtype=np.float64)
     p = _SIG_BITS[fmt]
     nz = x != 0
-    lo, hi = (2.0 ** -14, 65504.0) if fmt == "f16" else (2.0 ** -126, 3.0e38)
-    assert np.all(np.abs(x[nz]) >= lo) and np.all(np.abs(x) <= hi), "round_to: value outside the normal range"
+    if fmt == "f16":
+        assert np.all(np.abs(x) <= 65504.0), "round_to: binary16 overflow"
+    else:
+        assert np.all(np.abs(x[nz]) >= 2.0 ** -126) and np.all(np.abs(x) <= 3.0e38), "round_to: outside bf16 normals"
     m, e = np.frexp(x)
+    if fmt == "f16":
+        e = np.maximum(e, -13)          # x = m' * 2^-13 with |m'| < 0.5 below 2^-14
+        m = np.ldexp(x, -e)
     return np.ldexp(np.rint(np.ldexp(m, p)), e - p)
 
 

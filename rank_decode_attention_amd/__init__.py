@@ -77,6 +77,8 @@ def load():
     lib.palu_latent_offset.restype = i64
     lib.palu_quant_latent.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp]
     lib.palu_quant_latent.restype = ctypes.c_int
+    lib.palu_dequant_latent.argtypes = [vp, vp, i64, i32, ctypes.c_int, vp, vp]
+    lib.palu_dequant_latent.restype = ctypes.c_int
     lib.palu_project.argtypes = [D, vp, i32, i64, vp, C, i32, i32, vp]
     lib.palu_project.restype = ctypes.c_int
     lib.palu_decode_workspace_bytes.argtypes = [D, i32, i32]
@@ -231,6 +233,15 @@ def palu_project(desc: AttnDesc, x, A_kv, cache: LatentCache, seq: int, pos0: in
     c = cache.c()
     _check(load().palu_project(desc.ref(), x.data_ptr(), int(x.shape[1]), int(x.shape[0]), A_kv.data_ptr(),
                                ctypes.byref(c), int(seq), int(pos0), _stream(stream)))
+
+
+def palu_dequant_latent(codes, scales, n_rows: int, r: int, out, stream=None):
+    """int4 rows -> 16-bit rows (palu_dequant_latent); out is a float16 or
+    bfloat16 device tensor of n_rows x 32*ceil(r/32) elements."""
+    import torch
+    dt = {torch.float16: 1, torch.bfloat16: 2}[out.dtype]
+    _check(load().palu_dequant_latent(codes.data_ptr(), scales.data_ptr(), int(n_rows), int(r), dt, out.data_ptr(),
+                                      _stream(stream)))
 
 
 def palu_quant_latent(z, r: int, row_stride: int, codes, scales, stream=None):

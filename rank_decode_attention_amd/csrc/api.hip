@@ -249,6 +249,33 @@ palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows,
   return ok();
 }
 
+palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n_rows, int32_t r,
+                                palu_dtype out_dtype, void* out, hipStream_t stream) {
+  if (n_rows < 0 || r <= 0) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r");
+  if (out_dtype != PALU_F16 && out_dtype != PALU_BF16) return fail(PALU_ERR_UNSUPPORTED, "out_dtype must be F16 or BF16");
+  if (n_rows == 0) return ok();
+  if (!codes || !scales || !out) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (((uintptr_t)codes & 3u) != 0 || ((uintptr_t)scales & 1u) != 0 || !aligned16(out))
+    return fail(PALU_ERR_INVALID_ARG, "codes must be 4-byte, scales 2-byte and out 16-byte aligned");
+  const int nch = (r + 31) / 32;
+  if (n_rows > INT32_MAX || (uint64_t)n_rows * (uint64_t)nch * (uint64_t)nch >= (1ull << 32))
+    return fail(PALU_ERR_UNSUPPORTED, "too many rows for one call");
+  DequantParams dp;
+  memset(&dp, 0, sizeof(dp));
+  DequantSide& sd = dp.side[0];
+  sd.codes = (const uint8_t*)codes;
+  sd.scales = (const uint8_t*)scales;
+  sd.out = (uint8_t*)out;
+  sd.nch[0] = nch;
+  sd.rank[0] = r;
+  sd.magic[0] = (unsigned)(((1ull << 32) + (uint64_t)nch - 1) / (uint64_t)nch);
+  dp.seq_lens = nullptr;
+  dp.batch = 1; dp.G = 1; dp.max_len = (int)n_rows; dp.max_nch = nch; dp.n_sides = 1;
+  hipError_t e = launch_dequant(out_dtype == PALU_F16 ? 1 : 2, dp, stream);
+  if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
+  return ok();
+}
+
 palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
                          const palu_latent_cache* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
   palu_status s = check_desc(desc);
@@ -355,6 +382,7 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
         dp.max_nch = sd.nch[j] > dp.max_nch ? sd.nch[j] : dp.max_nch;
       }
     }
+    dp.n_sides = 2;
     hipError_t e = launch_dequant(desc->act_dtype == PALU_F16 ? 1 : 2, dp, stream);
     if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
   }

@@ -27,8 +27,9 @@ struct DequantSide {
 };
 struct DequantParams {
   DequantSide side[2];      // keys, values
-  const int* seq_lens;      // [batch], clamped to [0, max_len]
+  const int* seq_lens;      // device [batch], clamped to [0, max_len]; NULL: every length is max_len
   int batch, G, max_len, max_nch;   // (max_len * max_nch^2 < 2^32)
+  int n_sides;              // 2: keys and values; 1: side[0] only
 };
 // out_dtype: 1 = fp16, 2 = bf16
 hipError_t launch_dequant(int out_dtype, const DequantParams& p, hipStream_t stream);

@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(256) palu_dequant_kernel(const DequantParams p
   const int b = blockIdx.y / p.G, j = blockIdx.y - b * p.G;
   const DequantSide& d = p.side[blockIdx.z];
   const unsigned nch = (unsigned)d.nch[j];
-  int L = p.seq_lens[b];
+  int L = p.seq_lens ? p.seq_lens[b] : p.max_len;
   L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
   const unsigned n_chunks = (unsigned)L * nch;
   const int l = threadIdx.x & 63;
@@ -159,7 +159,8 @@ hipError_t launch_dequant(int out_dtype, const DequantParams& p, hipStream_t str
   const uint64_t chunks = (uint64_t)p.max_len * (uint64_t)p.max_nch;
   if (chunks * (uint64_t)p.max_nch >= (1ull << 32)) return hipErrorInvalidValue;
   // 256 chunks per block of 256 threads
-  const dim3 grid((unsigned)cdiv64((int64_t)chunks, 256), (unsigned)(p.batch * p.G), 2);
+  if (p.n_sides != 1 && p.n_sides != 2) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)cdiv64((int64_t)chunks, 256), (unsigned)(p.batch * p.G), (unsigned)p.n_sides);
   if (out_dtype == 1)
     hipLaunchKernelGGL(palu_dequant_kernel<_Float16>, grid, dim3(256), 0, stream, p);
   else if (out_dtype == 2)

@@ -106,6 +106,20 @@ def test_quant_argument_errors(lib):
     assert lib.palu_quant_latent(p, 0, 0, 32, 32, p, p, None) == 0        # nothing to do
 
 
+def test_dequant_argument_errors(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.palu_dequant_latent(None, p, 4, 32, 1, p, None) == INVALID
+    assert lib.palu_dequant_latent(p, p, -1, 32, 1, p, None) == INVALID
+    assert lib.palu_dequant_latent(p, p, 4, 0, 1, p, None) == INVALID
+    assert lib.palu_dequant_latent(p, p, 4, 32, 0, p, None) == UNSUP        # fp32 output
+    assert lib.palu_dequant_latent(p, p, 4, 32, 3, p, None) == UNSUP        # int4 output
+    assert lib.palu_dequant_latent(ctypes.c_void_p(258), p, 4, 32, 1, p, None) == INVALID  # codes misaligned
+    assert lib.palu_dequant_latent(p, ctypes.c_void_p(257), 4, 32, 1, p, None) == INVALID  # scales misaligned
+    assert lib.palu_dequant_latent(p, p, 4, 32, 1, ctypes.c_void_p(264), None) == INVALID  # out misaligned
+    assert lib.palu_dequant_latent(p, p, 1 << 23, 1024, 1, p, None) == UNSUP  # too many rows for one call
+    assert lib.palu_dequant_latent(p, p, 0, 32, 1, p, None) == 0            # nothing to do
+
+
 def test_project_argument_errors(lib):
     d = _desc()
     p = ctypes.c_void_p(256)

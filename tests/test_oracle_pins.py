@@ -346,6 +346,10 @@ def pin_round_to():
     xb = np.concatenate([x32, ties_b])
     want_b = torch.from_numpy(xb.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(O.round_to(xb, "bf16"), want_b), "bf16 rounding differs from torch"
+    # binary16 subnormals (quantum 2^-24) and the boundary to the normals
+    sub = np.concatenate([rng.uniform(-2.0 ** -14, 2.0 ** -14, 2000), np.arange(-40, 41) * 2.0 ** -25,
+                          [2.0 ** -14, -2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 2.0 ** -24, 2.0 ** -26]])
+    assert np.array_equal(O.round_to(sub, "f16"), sub.astype(np.float16).astype(np.float64)), "f16 subnormals"
     # the ties go to the even neighbour
     assert O.round_to(np.array([1 + 2.0 ** -11]), "f16")[0] == 1.0
     assert O.round_to(np.array([1 + 3 * 2.0 ** -11]), "f16")[0] == 1 + 2.0 ** -9
