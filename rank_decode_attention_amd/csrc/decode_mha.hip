@@ -4,26 +4,32 @@
 // V = z_v B_v) and section "Inference flow" (decode: read the latents,
 // rebuild, attend); arXiv 2407.21118v2 abstract (keys rebuilt on the fly,
 // RoPE-based attention, fused kernels).  Same results and split records as
-// palu_decode_kernel; this instantiation covers head-groups of 4 kv heads with
-// one query head each, head_dim 128, ranks <= 256 (multiples of 32), 16-bit
-// latents, RoPE.
+// palu_decode_kernel; this kernel covers head-groups of 4 kv heads with one
+// query head each, head_dim 128, ranks <= 256, 16-bit latents, RoPE.  It is
+// instantiated for 4..8 key chunks of 32 ranks (NKC); ranks that are not a
+// multiple of 32 need rows that are zero up to the next multiple (the int4
+// expansion writes such rows).
 //
 // Design (ours):
 //  * Block = 8 waves, two per SIMD; wave w owns kv head c = w % 4 and the
 //    frequency half w / 4 (32 rotation frequencies, both RoPE halves: 64 of
-//    the head's 128 dims).  Its B_k^T rows (64 dims x 256 ranks) stay in 128
+//    the head's 128 dims).  Its B_k^T rows (64 dims x 32 NKC ranks) stay in
 //    AGPRs for the whole block, feeding the MFMA A operand directly.
-//  * 32-token tiles stream HBM -> LDS through LDS DMA, two tiles ahead (key
-//    tiles XOR-swizzled per row for conflict-free MFMA operand reads; value
-//    tiles unswizzled).  Key tiles use a ring of 3 buffers, value tiles a
-//    ring of 4: the value tile of step n is consumed in step n + 1.
-//  * Per step n (one barrier): the online softmax of tile n-1 from the two
-//    half-head partial scores both waves of the head left in LDS before the
-//    barrier (summed in a fixed order, so both waves hold identical P);
-//    P z_v of tile n-1 on the VALU (each wave half of the ranks) beside the
-//    key rebuild of tokens 0-15 of tile n on MFMA; the rebuild of tokens
-//    16-31 beside RoPE and the query dot of tokens 0-15; then RoPE and the
-//    dot of tokens 16-31, and the partial scores go to LDS.
+//  * 32-token tiles stream HBM -> LDS through LDS DMA, two tiles ahead, the
+//    four DMA pieces of a wave spread over the MFMA window of a step.  Key
+//    rows are XOR-swizzled in 16-byte chunks (conflict-free MFMA operand
+//    reads), value rows in 32-byte pairs (conflict-free transposed reads).
+//    Key tiles use a ring of 3 buffers, value tiles a ring of 4: the value
+//    tile of step n is consumed in step n + 1.
+//  * Per step n (one barrier): window A = the key rebuild of tokens 0-15 of
+//    tile n on MFMA, with the online softmax of tile n-1 (all four heads in
+//    every wave, from the half-head partial scores in LDS, summed in a fixed
+//    order so that all waves hold identical P) and the rotation of the next
+//    angle table laid between the MFMAs; window B = the rebuild of tokens
+//    16-31 with RoPE and the query dot of tokens 0-15 between the MFMAs;
+//    then P z_v of tile n-1 on MFMA (P split into hi + lo 16-bit parts, each
+//    wave 32 value ranks of all four heads, value tile read transposed), RoPE
+//    and the dot of tokens 16-31, and the partial scores go to LDS.
 //  * RoPE angles (64 frequencies x 32 positions per tile) are formed once
 //    per block into a shared table, one step ahead, by rotating the previous
 //    tile's entries by 32 positions (re-seeded exactly in fp64 at every
