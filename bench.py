@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # passes, calibrated against a plain copy of known size; valid only for the
 # kernel sources it was measured on (their hash is stored beside the figures).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "palu_decode_mha_kernel_llama2_7b_traffic.json")
-KERNEL_SOURCES = ["decode.hip", "decode_mha.hip", "decode.h", "common.h"]
+KERNEL_SOURCES = ["decode.hip", "decode_mha.hip", "decode.h", "common.h", "int4.h"]
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, AMD published
 METRIC = "decode attn tokens/s and latent GB/s (% of HBM peak) at Llama-2-7B shape"
 
@@ -174,12 +174,15 @@ def main_kernel_name(wl) -> str:
     the general split-attention kernel otherwise."""
     import palu_inputs as PI
     r = PI.ranks(wl)
-    q4 = wl.latent == "i4"   # (int4 caches are expanded to 16-bit rows of the rank rounded up to 32 first)
+    q4 = wl.latent == "i4"
     mha = ((wl.latent in ("f16", "bf16") or q4) and wl.head_dim == 128 and wl.kv_per_group == 4
            and wl.n_q_heads == wl.n_kv_heads and wl.use_rope
            and all((q4 or int(x) % 32 == 0) and int(x) <= 256 for x in r))
-    name = "palu_decode_mha_kernel (fused, MHA head-groups)" if mha else "palu_decode_kernel (split attention)"
-    return ("palu_dequant_kernel, then " + name) if q4 else name
+    if mha:
+        # (int4 codes are expanded into the kernel's LDS tiles)
+        return "palu_decode_mha_kernel (fused, MHA head-groups" + (", int4 codes)" if q4 else ")")
+    # (int4 caches are first expanded to 16-bit rows of the rank rounded up to 32)
+    return ("palu_dequant_kernel, then " if q4 else "") + "palu_decode_kernel (split attention)"
 
 
 def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str = TRAFFIC_FILE):
@@ -287,8 +290,8 @@ def main():
     ms_step = statistics.mean(t_call)
     ms_main = statistics.mean(t_main)
     tokens_per_s = wl.batch / (ms_step * 1e-3)
-    # int4 caches: the step is two kernels (expansion, then the decode), so the
-    # rate is taken over the whole call
+    # int4 caches: the rate is taken over the whole call (where the expansion
+    # runs as a kernel of its own, it is part of the step)
     ms_roof = ms_step if wl.latent == "i4" else ms_main
     achieved = st["latent_bytes"] / (ms_roof * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)

@@ -124,7 +124,7 @@ struct DecodePlan {
   size_t hdr_bytes, rec_bytes, qabs_bytes, total;
   // int4 latents: the decode runs on a 16-bit copy of the cache in the
   // workspace (ranks rounded up to 32, rows zero-padded), expanded first
-  bool q4;
+  bool q4, fused4;   // fused4: the MHA kernel reads the int4 codes itself (no expansion pass)
   size_t dense_k_bytes, dense_v_bytes;
   int64_t dk_pitch[kMaxGroups], dv_pitch[kMaxGroups], dk_goff[kMaxGroups], dv_goff[kMaxGroups];
   int64_t dk_seq, dv_seq;
@@ -175,7 +175,22 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   pl->qabs_bytes = d->use_rope ? 0 : (size_t)roundup((int64_t)batch * d->n_q_heads * pl->qabs_stride * 4, 256);
   pl->dense_k_bytes = pl->dense_v_bytes = 0;
   pl->dk_seq = pl->dv_seq = 0;
+  pl->fused4 = false;
   if (pl->q4) {
+    DecodeParams t;
+    memset(&t, 0, sizeof(t));
+    t.G = d->n_groups;
+    t.q4 = 1;
+    t.rvp = pl->rvp;
+    for (int j = 0; j < d->n_groups; ++j) {
+      t.rk[j] = d->rank_k[j];
+      t.rv[j] = d->rank_v[j];
+      t.pk[j] = (int)row_pitch(PALU_I4, d->rank_k[j]);
+      t.pv[j] = (int)row_pitch(PALU_I4, d->rank_v[j]);
+    }
+    pl->fused4 = mha_supported(pl->key, t);
+  }
+  if (pl->q4 && !pl->fused4) {
     for (int j = 0; j < d->n_groups; ++j) {
       pl->dk_pitch[j] = 2 * roundup(d->rank_k[j], 32);
       pl->dv_pitch[j] = 2 * roundup(d->rank_v[j], 32);
@@ -357,7 +372,7 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   make_layout(desc, cache->max_len, &L);
   uint8_t* const dense_k = (uint8_t*)workspace + pl.hdr_bytes + pl.rec_bytes + pl.qabs_bytes;
   uint8_t* const dense_v = dense_k + pl.dense_k_bytes;
-  if (pl.q4) {
+  if (pl.q4 && !pl.fused4) {
     // int4 latents -> 16-bit rows (the history of every sequence, keys and values)
     static_assert(kDqMaxGroups >= kMaxGroups, "group arrays");
     DequantParams dp;
@@ -409,7 +424,15 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
     p.rk[j] = desc->rank_k[j]; p.rv[j] = desc->rank_v[j];
     p.pk[j] = (int)L.pk[j]; p.pv[j] = (int)L.pv[j];
   }
-  if (pl.q4) {
+  if (pl.fused4) {
+    // the MHA kernel expands the int4 tiles itself
+    p.q4 = 1;
+    p.sk = (const uint8_t*)cache->sk; p.sv = (const uint8_t*)cache->sv;
+    p.seq_sbytes_k = L.seq_sk; p.seq_sbytes_v = L.seq_sv;
+    for (int j = 0; j < desc->n_groups; ++j) {
+      p.soff_k[j] = L.soff_k[j]; p.soff_v[j] = L.soff_v[j];
+    }
+  } else if (pl.q4) {
     p.zk = dense_k; p.zv = dense_v;
     p.seq_bytes_k = pl.dk_seq; p.seq_bytes_v = pl.dv_seq;
     for (int j = 0; j < desc->n_groups; ++j) {

@@ -37,6 +37,13 @@ struct DecodeParams {
   int rk[kMaxGroups], rv[kMaxGroups];               // ranks
   int pk[kMaxGroups], pv[kMaxGroups];               // row pitches in bytes
   int zero_padded;          // rows hold zeros from the rank up to the next multiple of 32 (int4 copies)
+  // int4 caches read directly (MHA kernel): zk / zv hold the codes (pitch
+  // pk / pv = 16 bytes per 32 ranks), sk / sv the binary16 scales
+  int q4;
+  const uint8_t* sk;
+  const uint8_t* sv;
+  int64_t seq_sbytes_k, seq_sbytes_v;
+  int64_t soff_k[kMaxGroups], soff_v[kMaxGroups];
 };
 
 // Key of a compiled decode-attention instantiation.

@@ -38,6 +38,7 @@
 //    more than 2^8, so the accumulator rescale is rare.
 #include "common.h"
 #include "decode.h"
+#include "int4.h"
 
 #include <hip/hip_ext.h>
 #include <type_traits>
@@ -45,9 +46,10 @@
 namespace palu {
 namespace {
 
-template <class LT_, int NKC_>
+template <class LT_, int NKC_, bool Q4_>
 struct MhaCfg {
   typedef LT_ LT;
+  static constexpr bool Q4 = Q4_;              // int4 codes in HBM, expanded into the LDS tiles
   static constexpr int DH = 128, NH = 4, NW = 8, NT = 512, TT = 32;
   static constexpr int RK = 256, RV = 256;     // rank capacity of an LDS latent row
   static constexpr int NKC = NKC_;             // 32-deep k-chunks of the key rebuild (rank <= 32 NKC)
@@ -57,12 +59,15 @@ struct MhaCfg {
   static constexpr int TILEB = TT * ROWB;      // 16 KB per latent tile
   static constexpr int NDT = TILEB / (16 * NT);   // DMA instructions per wave per latent tile (2)
   static constexpr int NDMA = 2 * NDT;         // per tile step: keys, values (+ a query at segment starts)
-  static constexpr int NKB = 3, NVB = 4;       // key / value buffer rings
+  // key / value buffer rings: tiles arrive by LDS DMA two steps ahead, or
+  // (int4) are expanded into the ring one step ahead
+  static constexpr int NKB = Q4 ? 2 : 3, NVB = Q4 ? 3 : 4;
+  static constexpr int NSTG = Q4 ? 2 : 3;      // B_k staging slots
   static constexpr int AP = 17;                // angle-table row pitch in 16-byte units (68 floats)
   static constexpr int STGB = 32 * DH * NH * 2;   // bytes of one staged B_k chunk (32 ranks x 512 columns)
   static_assert(NDT * 16 * NT == TILEB, "tile DMA");
   static_assert(NT / 32 == 16, "one DMA instruction covers 16 rows");
-  static_assert(STGB <= NKB * TILEB && 2 * STGB <= NVB * TILEB, "B_k staging");
+  static_assert(STGB <= NKB * TILEB && (NSTG - 1) * STGB <= NVB * TILEB, "B_k staging");
 };
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 domain)
@@ -127,9 +132,9 @@ __device__ __forceinline__ float sum16(float x) {
 
 }  // namespace
 
-template <class LT, int NKC>
+template <class LT, int NKC, bool Q4>
 __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodeParams p) {
-  typedef MhaCfg<LT, NKC> C;
+  typedef MhaCfg<LT, NKC, Q4> C;
   typedef typename Vec8<LT>::type op_t;
   typedef short s8 __attribute__((ext_vector_type(8)));
   __shared__ uint4 zkb[C::NKB * C::TILEB / 16];
@@ -226,6 +231,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   const int cprk = pk >> 4, cprv = pv >> 4;
   const uint8_t* zk_seq = p.zk + p.goff_k[g];
   const uint8_t* zv_seq = p.zv + p.goff_v[g];
+  // int4 caches: zk / zv hold the codes (16 bytes per 32 ranks, pitch pk / pv),
+  // sk / sv the binary16 scales (pitch pk / 8, pv / 8)
+  const uint8_t* sk_seq = Q4 ? p.sk + p.soff_k[g] : nullptr;
+  const uint8_t* sv_seq = Q4 ? p.sv + p.soff_v[g] : nullptr;
   const int64_t sbk = p.seq_bytes_k, sbv = p.seq_bytes_v;
   const int h = g * C::NH + c;                    // query head of this wave (one per kv head)
 
@@ -271,8 +280,18 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       if (kc < nkc) {
         if (kc + 1 < nkc) wait_vmcnt<NSI>(); else wait_vmcnt<0>();
         barrier();
-        if (kc + 2 < nkc) stage((kc + 2) % 3, kc + 2);
-        gather(kc % 3, kc);
+        if constexpr (C::NSTG == 3) {
+          if (kc + 2 < nkc) stage((kc + 2) % 3, kc + 2);
+          gather(kc % 3, kc);
+        } else {
+          // two slots: chunk kc + 2 goes into kc's slot once every wave has read it
+          gather(kc % 2, kc);
+          if (kc + 2 < nkc) {
+            wait_lgkm0();
+            barrier();
+            stage(kc % 2, kc + 2);
+          }
+        }
       } else {
 #pragma unroll
         for (int mt = 0; mt < C::NMT; ++mt) {
@@ -284,6 +303,17 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     }
     wait_lgkm0();
     barrier();   // staging buffers are free before the tile DMA overwrites them
+    if constexpr (C::Q4) {
+      // ring rows past a group's ranks are read by the MFMAs but never
+      // written by the expansion: they must hold finite values (zeros)
+      constexpr int NZ = (C::NKB + C::NVB) * C::TILEB / 16;
+      for (int i = tid; i < NZ; i += C::NT) {
+        uint4* dst = i < C::NKB * C::TILEB / 16 ? zkb + i : zvb + (i - C::NKB * C::TILEB / 16);
+        *dst = uint4{0u, 0u, 0u, 0u};
+      }
+      wait_lgkm0();
+      barrier();
+    }
   }
 
   // ---------------------------------------------------------------- per-lane constants
@@ -338,10 +368,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     int L = sload_i32(p.seq_lens + b);
     return L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
   };
-  struct DCur { int b, t0, L, st; const uint8_t* kb; const uint8_t* vb; };
+  struct DCur { int b, t0, L, st; const uint8_t* kb; const uint8_t* vb; const uint8_t* skb; const uint8_t* svb; };
   auto dma_addr = [&](DCur& d) __attribute__((always_inline)) {
     d.kb = zk_seq + (int64_t)d.b * sbk + (int64_t)d.t0 * pk;
     d.vb = zv_seq + (int64_t)d.b * sbv + (int64_t)d.t0 * pv;
+    if constexpr (C::Q4) {
+      d.skb = sk_seq + (int64_t)d.b * p.seq_sbytes_k + (int64_t)d.t0 * (pk >> 3);
+      d.svb = sv_seq + (int64_t)d.b * p.seq_sbytes_v + (int64_t)d.t0 * (pv >> 3);
+    }
   };
   DCur cd;
   cd.b = __builtin_amdgcn_readfirstlane(start_info[0]);
@@ -362,6 +396,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     d.t0 += C::TT;
     d.kb += C::TT * pk;
     d.vb += C::TT * pv;
+    if constexpr (C::Q4) {
+      d.skb += C::TT * (pk >> 3);
+      d.svb += C::TT * (pv >> 3);
+    }
     d.st = 0;
     if (d.t0 >= d.L) {
       int b = d.b + 1, L = len_of(b);
@@ -406,12 +444,83 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     const uint8_t* qb = (const uint8_t*)p.q + ((int64_t)d.b * p.H + h) * (C::DH * 2);
     if (ln.l < 16) dma16s(qb, 16u * ln.l, lds_addr(&qst[m % 3][w][0]));
   };
+  // ---- int4 tiles: lane tid expands one 32-rank chunk of a tile row, keys
+  // for tid < 32 nchk (row tid / nchk), values for the next 32 nchv lanes.
+  // Its 16 bytes of codes and its scale are loaded into registers one step
+  // ahead (rows past the history repeat its last row); the expansion writes
+  // the chunk's four 16-byte pieces into the tile ring in the swizzled layout
+  // the DMA would have produced, zero past the rank and on rows past the
+  // history.
+  const int nchk = pk >> 4, nchv = pv >> 4;
+  const int magk = (65536 + nchk - 1) / nchk, magv = (65536 + nchv - 1) / nchv;
+  struct Q4It { int row, ch; bool isv, ok; };
+  auto q4_item = [&](const Lane& ln) __attribute__((always_inline)) {
+    Q4It it;
+    int u = ln.t;
+    it.isv = u >= 32 * nchk;
+    if (it.isv) u -= 32 * nchk;
+    const int n = it.isv ? nchv : nchk;
+    it.row = (u * (it.isv ? magv : magk)) >> 16;   // u / n (u < 256, n <= 8)
+    it.ch = u - it.row * n;
+    it.ok = !it.isv || u < 32 * nchv;
+    return it;
+  };
+  struct Q4Plan { const uint8_t* kb; const uint8_t* vb; const uint8_t* skb; const uint8_t* svb; int lim; };
+  auto q4_plan = [&](const DCur& d) __attribute__((always_inline)) {
+    return Q4Plan{d.kb, d.vb, d.skb, d.svb, d.L - 1 - d.t0};
+  };
+  typedef const __attribute__((address_space(1))) u32x4* gq4;
+  typedef const __attribute__((address_space(1))) unsigned short* gs16;
+  u32x4 q4c = u32x4{0u, 0u, 0u, 0u};   // this lane's codes and scale of the next tile
+  unsigned q4s = 0;
+  auto q4_load = [&](const Q4Plan& q, const Lane& ln) __attribute__((always_inline)) {
+    const Q4It it = q4_item(ln);
+    if (it.ok) {
+      const int r = min(it.row, q.lim);
+      const int pitch = it.isv ? pv : pk;
+      const uint8_t* cb = (it.isv ? q.vb : q.kb) + r * pitch + 16 * it.ch;
+      const uint8_t* sb = (it.isv ? q.svb : q.skb) + r * (pitch >> 3) + 2 * it.ch;
+      q4c = *(gq4)cb;
+      q4s = *(gs16)sb;
+    }
+  };
+  auto q4_mask = [](int q, int n) __attribute__((always_inline)) {
+    return (2 * q < n ? 0xFFFFu : 0u) | (2 * q + 1 < n ? 0xFFFF0000u : 0u);
+  };
+  auto q4_expand = [&](int m, int nvalid, const Lane& ln) __attribute__((always_inline)) {
+    const Q4It it = q4_item(ln);
+    if (!it.ok) return;
+    // elements of this chunk below the rank (none on rows past the history)
+    const int tail = it.row < nvalid ? (it.isv ? p.rv[g] : rk) - 32 * it.ch : 0;
+    uint8_t* rowp = it.isv ? (uint8_t*)zvb + (m % C::NVB) * C::TILEB + it.row * C::ROWB
+                           : (uint8_t*)zkb + (m % C::NKB) * C::TILEB + it.row * C::ROWB;
+    const int swz = it.isv ? 2 * vswz(it.row) : (it.row & 15);
+    const float sf = (float)__builtin_bit_cast(_Float16, (unsigned short)q4s);
+    const unsigned cw[4] = {q4c[0], q4c[1], q4c[2], q4c[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 o = expand8<LT>(cw[i], sf);
+      const int nv8 = tail - 8 * i;
+      if (nv8 < 8) {
+        o.x &= q4_mask(0, nv8);
+        o.y &= q4_mask(1, nv8);
+        o.z &= q4_mask(2, nv8);
+        o.w &= q4_mask(3, nv8);
+      }
+      *(uint4*)(rowp + 16 * ((4 * it.ch + i) ^ swz)) = o;
+    }
+  };
+
   auto issue = [&](const DCur& d, int m, int info) __attribute__((always_inline)) {
     const Lane ln = lane();
     if (info & F_START) dma_query(d, m, ln);
-    const DmaPlan q = dma_plan(d, m, ln);
+    if constexpr (C::Q4) {
+      q4_load(q4_plan(d), ln);
+    } else {
+      const DmaPlan q = dma_plan(d, m, ln);
 #pragma unroll
-    for (int i = 0; i < 2 * C::NDT; ++i) dma_piece(q, i);
+      for (int i = 0; i < 2 * C::NDT; ++i) dma_piece(q, i);
+    }
   };
 
   // Angle table of tile cr.n: entries (position t & 31, frequencies
@@ -600,6 +709,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // tiles n_begin and n_begin + 1 (info words of the current and next tile)
   int i_c = info_of(cd), i_a = 0, i_p = 0, t0_a = 0;
   issue(cd, n_begin, i_c);
+  if constexpr (C::Q4) q4_expand(n_begin, (i_c >> 16) & 63, lane());   // (waits for its loads)
   ang_seed(n_begin, cd.t0);
   if (n_begin + 1 < n_end) {
     advance(cd);
@@ -615,7 +725,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // (ALL2: tile n + 2 exists, known at compile time in the steady state)
   auto step = [&](int n, auto have_t, auto had_t, auto all2_t) __attribute__((always_inline)) {
     constexpr bool HAVE = decltype(have_t)::value, HAD = decltype(had_t)::value, ALL2 = decltype(all2_t)::value;
-    if (HAVE) {
+    if constexpr (C::Q4) {
+      wait_vmcnt<0>();   // the query of tile n; this lane's chunk of tile n + 1
+      wait_lgkm0();      // the expansion of tile n (last step) is in LDS
+    } else if (HAVE) {
       if (n + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
     }
     barrier();   // tile n, angle table n and the partial scores of tile n - 1 are visible
@@ -624,21 +737,31 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     const bool seed = n + 1 < n_end && ((i_a & F_START) || ((n + 1 - n_begin) & 63) == 0);
     if (HAVE && (i_c & F_START)) load_query(n, i_c);
     const Lane ln = lnk;
+    // int4: tile n + 1 into its ring slots (its slots held tiles n - 1 and
+    // n - 2, consumed before this step's barrier)
+    if constexpr (C::Q4) {
+      if (n + 1 < n_end) q4_expand(n + 1, (i_a >> 16) & 63, ln);
+    }
     // tile n + 2: its DMA instructions go out between the MFMAs of window A
     // (where there is no window A, here); a waiting count of NDMA at the next
     // step stays safe with a query load in front of them
     const bool load2 = ALL2 || n + 2 < n_end;
     DmaPlan dq;
+    Q4Plan q4p;
     int i_d = 0, t0_d = 0;
     if (load2) {
       i_d = info_of(cd);
       t0_d = cd.t0;
       if (i_d & F_START) dma_query(cd, n + 2, ln);
-      dq = dma_plan(cd, n + 2, ln);
+      if constexpr (C::Q4) q4p = q4_plan(cd); else dq = dma_plan(cd, n + 2, ln);
       if (n + 3 < n_end) advance(cd);   // (the cursor never walks past the range)
       if (!HAVE) {
+        if constexpr (C::Q4) {
+          q4_load(q4p, ln);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 2 * C::NDT; ++i) dma_piece(dq, i);
+          for (int i = 0; i < 2 * C::NDT; ++i) dma_piece(dq, i);
+        }
       }
     }
     Sm sm;
@@ -711,7 +834,11 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
           angs[((n + 1) & 1) * (C::TT * C::AP) + ae] = os;
         }
         // angles of tokens 0-15 for window B
-        if (slot % 6 == 3 && slot / 6 < 2 * C::NDT && load2) dma_piece(dq, slot / 6);
+        if constexpr (C::Q4) {
+          if (slot == 3 && load2) q4_load(q4p, ln);
+        } else {
+          if (slot % 6 == 3 && slot / 6 < 2 * C::NDT && load2) dma_piece(dq, slot / 6);
+        }
         if (slot == 24) ca0[0] = tc[0];
         if (slot == 25) sa0[0] = ts[0];
         if (slot == 26) ca0[1] = tc[4];
@@ -811,19 +938,30 @@ bool mha_supported(const DecodeKey& k, const DecodeParams& p) {
         k.q_per_kv == 1 && k.rope && k.rk_max <= 256 && k.rv_max <= 256))
     return false;
   // B_k is staged in whole 32-row chunks: rows past the rank (the last row
-  // repeated) must meet zero latents
+  // repeated) must meet zero latents (int4 tiles are expanded that way)
   for (int j = 0; j < p.G; ++j)
-    if (p.rk[j] % 32 != 0 && !p.zero_padded) return false;
+    if (p.rk[j] % 32 != 0 && !p.zero_padded && !p.q4) return false;
+  if (p.q4)
+    for (int j = 0; j < p.G; ++j)
+      if (p.pk[j] != 16 * ((p.rk[j] + 31) / 32) || p.pv[j] != 16 * ((p.rv[j] + 31) / 32)) return false;
   return p.rvp >= 256;                     // every wave writes its 32 value ranks of the record
+}
+
+template <class LT, int NKC, bool Q4>
+static void launch_mha_q(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid(p.G * p.P), block(512);
+  if (t0 && t1)
+    hipExtLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC, Q4>), grid, block, 0, stream, t0, t1, 0, p);
+  else
+    hipLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC, Q4>), grid, block, 0, stream, p);
 }
 
 template <class LT, int NKC>
 static void launch_mha_inst(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const dim3 grid(p.G * p.P), block(512);
-  if (t0 && t1)
-    hipExtLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC>), grid, block, 0, stream, t0, t1, 0, p);
+  if (p.q4)
+    launch_mha_q<LT, NKC, true>(p, stream, t0, t1);
   else
-    hipLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC>), grid, block, 0, stream, p);
+    launch_mha_q<LT, NKC, false>(p, stream, t0, t1);
 }
 
 template <class LT>

@@ -9,6 +9,7 @@
 // even), code = 0 where s == 0; element 2i in the low nibble of byte i.
 #include "common.h"
 #include "quant.h"
+#include "int4.h"
 
 #include <type_traits>
 
@@ -79,38 +80,6 @@ static hipError_t launch_q(const void* z, int64_t n_rows, int r, int64_t stride,
 // z_hat = code * scale (PALU page, section "Rollout", route C: quantization
 // on top of the low-rank cache); the product is exact in fp32 and is
 // rounded once, to the activation format that the decode's MFMA takes.
-template <class T>
-__device__ __forceinline__ uint4 expand8(unsigned w, float s) {
-  unsigned out[4];
-  if constexpr (std::is_same<T, _Float16>::value) {
-    // packed fp16: the nibble pair (2k, 2k+1) of byte k becomes the halves
-    // 1024 + (q + 8) (bits 0x6400 | (nibble ^ 8)); subtracting 1032 gives q
-    // exactly, and one fp16 multiply rounds q * s to nearest even, which is
-    // the exact product rounded once
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const unsigned lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    const h2 s2 = {(_Float16)s, (_Float16)s};
-    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // bytes [lo byte k, 0, hi byte k, 0]
-      const unsigned sel = (unsigned)k | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
-      const unsigned pr = (__builtin_amdgcn_perm(hi, lo, sel) ^ 0x00080008u) | 0x64006400u;
-      out[k] = __builtin_bit_cast(unsigned, (__builtin_bit_cast(h2, pr) + bias) * s2);
-    }
-  } else {
-    T v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = (int)(w << (28 - 4 * i)) >> 28;   // nibble i, 4-bit two's complement
-      v[i] = from_f32<T>((float)q * s);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = *(const unsigned*)&v[2 * k];
-  }
-  return uint4{out[0], out[1], out[2], out[3]};
-}
-
 template <class T>
 __global__ void __launch_bounds__(256) palu_dequant_kernel(const DequantParams p) {
   const int b = blockIdx.y / p.G, j = blockIdx.y - b * p.G;

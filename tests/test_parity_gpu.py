@@ -86,19 +86,18 @@ def test_batch_zero_is_noop():
 
 
 def test_int4_workspace_and_errors():
-    """int4 latents add their 16-bit expansion (rank rounded up to 32, keys
-    and values) to the workspace; missing scales are an argument error."""
-    import ctypes
+    """int4 latents on shapes the MHA kernel covers are expanded inside it (no
+    extra workspace); elsewhere (here: no RoPE) the 16-bit expansion (rank
+    rounded up to 32, keys and values) is added to the workspace.  Missing
+    scales are an argument error."""
     import rank_decode_attention_amd as R
-    lib = R.load()
     batch, max_len = 3, 100
     wl = _small("int4", batch=batch, max_len=max_len)
-    f = R.AttnDesc(32, 32, 128, 8, [154] * 8, latent_dtype="f16", act_dtype="f16")
-    i = R.AttnDesc(32, 32, 128, 8, [154] * 8, latent_dtype="i4", act_dtype="f16")
-    wf = R.decode_workspace_bytes(f, batch, max_len)
-    wi = R.decode_workspace_bytes(i, batch, max_len)
     dense = batch * max_len * 8 * 2 * 160
-    assert wi == wf + 2 * ((dense + 255) // 256 * 256)
+    for rope, extra in ((True, 0), (False, 2 * ((dense + 255) // 256 * 256))):
+        f = R.AttnDesc(32, 32, 128, 8, [154] * 8, use_rope=rope, latent_dtype="f16", act_dtype="f16")
+        i = R.AttnDesc(32, 32, 128, 8, [154] * 8, use_rope=rope, latent_dtype="i4", act_dtype="f16")
+        assert R.decode_workspace_bytes(i, batch, max_len) == R.decode_workspace_bytes(f, batch, max_len) + extra
     case = build_decode_case(wl)
     c = case["cache"]
     no_scales = R.LatentCache(c.zk, c.zv, None, None, c.max_len)
