@@ -39,6 +39,13 @@ SMALL = [
     ("int4_empty_seq", _small("int4", batch=3, max_len=100, fixed_lengths=(0, 100, 33)), None),
     ("int4_norope", _small("int4", use_rope=False, batch=2, max_len=160, fixed_lengths=(160, 3)), None),
     ("int4_gqa", _small("gqa_rope", latent="i4", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
+    # MHA-group kernel with fewer than 8 key chunks, and per-group ranks
+    ("7b_r160", _small("llama2_7b", rank=160, batch=2, max_len=300, fixed_lengths=(300, 77)), None),
+    ("long_r128_bf16", _small("long_b4", rank=128, batch=2, max_len=400), None),
+    ("7b_mixed_ranks", _small("llama2_7b", rank=None, rank_choices=(96, 160, 256), batch=2, max_len=200,
+                              fixed_lengths=(200, 45)), None),
+    ("int4_mixed_ranks", _small("int4", rank=None, rank_choices=(70, 154, 200), batch=2, max_len=260,
+                                fixed_lengths=(260, 31)), None),
 ]
 
 
