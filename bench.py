@@ -215,15 +215,20 @@ def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str 
     print(json.dumps(rec))
 
 
+def _blas_threads() -> int:
+    """Threads of the BLAS the oracle's numpy calls run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(wl, n_seq: int, reps: int = 3):
     """The fp64 oracle (as it stands) on the first n_seq sequences of the workload."""
     import oracle
     import palu_inputs as PI
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = _blas_threads()
     lens = PI.lengths(wl)[:n_seq]
 
     def lat(which, b, j):
@@ -248,6 +253,100 @@ def cpu_baseline(wl, n_seq: int, reps: int = 3):
                       f"fp64 numpy, median of {reps} runs of {t:.2f} s"}
 
 
+def bench_prefill(wl, args, hip):
+    """Prefill workloads (n_tok > 0): palu_project (z = x A for every latent
+    row, int4-quantised in its epilogue when the cache is int4) over one chunk
+    of n_tok tokens, and palu_quant_latent over the same number of latent rows
+    on its own.  One JSON line; roofline: the projection against the dense
+    MFMA peak of its dtype, the quantiser against HBM."""
+    import torch
+    import palu_inputs as PI
+    import oracle
+    import rank_decode_attention_amd as R
+
+    ranks = PI.ranks(wl)
+    desc = R.AttnDesc(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_groups, ranks.tolist(), use_rope=wl.use_rope,
+                      rope_base=wl.rope_base, latent_dtype=wl.latent, act_dtype=wl.act)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.act]
+
+    def dev(a):
+        if wl.act == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    n_tok = wl.n_tok
+    x = dev(PI.prefill_x(wl))
+    As = PI.prefill_A(wl)
+    A_kv = dev(np.concatenate([a.T for a in As], axis=0))
+    cache = R.alloc_cache(desc, 1, n_tok)
+    n_lat = int(2 * ranks.sum())
+    flops = 2.0 * n_tok * wl.d_model * n_lat
+    scrub = None if args.no_scrub else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(steps):
+            if scrub is not None:
+                scrub.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) for a, b in ts)
+
+    ms_proj = timed(lambda: R.palu_project(desc, x, A_kv, cache, 0, 0), args.steps, args.warmup)
+    # the quantiser alone on n_tok x (2 G) latent rows of rank r in the activation format
+    r = int(ranks[0])
+    rows = [PI.latent_f32(wl, which, 0, j, n=n_tok) for which in ("k", "v") for j in range(wl.n_groups)]
+    z = dev(PI.to_format(np.concatenate(rows), wl.act))
+    nc = (r + 31) // 32
+    codes = torch.empty((z.shape[0], 16 * nc), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((z.shape[0], nc), dtype=torch.int16, device="cuda")
+    ms_q = timed(lambda: R.palu_quant_latent(z, r, r, codes, scales), args.steps, args.warmup)
+    q_bytes = z.numel() * z.element_size() + codes.numel() + scales.numel() * 2
+
+    line = {
+        "metric": "prefill latent write tokens/s (palu_project, z = x A with the int4 epilogue)",
+        "value": round(n_tok / (ms_proj * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_proj, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.act,
+        "data": "synthetic (seeded N(0,1) activations, Gaussian A with std 1/sqrt(d_model))",
+        "config": {"workload": f"{wl.name}: prefill chunk of {n_tok} tokens x d_model {wl.d_model}, {n_lat} latent "
+                               f"columns ({wl.n_groups} groups, rank {r}, keys and values), {wl.latent} latents",
+                   "global_batch": 1, "seq_len": n_tok, "parallelism": "single GPU",
+                   "cache": "cold (1 GiB scrub before each step)" if scrub is not None else "warm"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (ms_proj * 1e-3) / 1e12, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (ms_proj * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "palu_project_kernel", "kernel_ms": round(ms_proj, 4), "flops": flops},
+        "quant_latent": {"rows": int(z.shape[0]), "rank": r, "ms": round(ms_q, 4), "bytes": int(q_bytes),
+                         "bound": "hbm", "achieved_GBps": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+                         "frac": round(q_bytes / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if args.cpu_seqs > 0:
+        n_cpu = 2048
+        xs = oracle.upcast(PI.prefill_x(wl, n_cpu), wl.act)
+        Aup = [oracle.upcast(a, wl.act) for a in As]
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for a in Aup:
+                zc = oracle.project(xs, a)
+                if wl.latent == "i4":
+                    oracle.quant_int4(zc.astype(np.float32))
+            times.append(time.perf_counter() - t0)
+        t = statistics.median(times)
+        line["cpu_baseline"] = {"value": n_cpu / t, "unit": "tokens/s", "cores": _blas_threads(),
+                                "kind": "oracle", "sample": f"{n_cpu} of {n_tok} tokens, every latent column, "
+                                                             f"fp64 numpy, median of 3 runs of {t:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,7 +354,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-scrub", action="store_true", help="time with warm caches")
-    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=16,
+                    help="sequences in the CPU-oracle sample (0: skip; prefill: any value > 0 times 2048 tokens)")
     ap.add_argument("--detail", default="", help="also write a detailed JSON record to this path")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
@@ -278,8 +378,11 @@ def main():
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
     wl = PI.workload(args.workload)
-    st = setup(wl)
     hip = _hip()
+    if wl.n_tok > 0:
+        bench_prefill(wl, args, hip)
+        return
+    st = setup(wl)
     scrub = None if args.no_scrub else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
     run_steps(st, args.warmup, scrub, hip, ev_main=False)

@@ -9,8 +9,9 @@
 // Layout: x [n_tok][D] row-major; A is passed as its transpose A^T
 // [n_lat][D] (the weight layout of a Linear(D -> n_lat)), so both MFMA
 // operands are 16-byte contiguous runs of D.  Block = 256 tokens x up to 160
-// latent channels of one latent row (group j of keys or values); 4 waves of
-// 64 tokens x 160 channels; K-steps of 128 bytes staged by LDS DMA, double-buffered.
+// latent channels of one latent row (group j of keys or values); 8 waves of
+// 32 tokens x 160 channels (two per SIMD); K-steps of 128 bytes staged by LDS
+// DMA, double-buffered.
 #include "common.h"
 #include "project.h"
 
@@ -23,8 +24,8 @@ struct PrjCfg {
   typedef T_ T;
   static constexpr bool F32 = std::is_same<T, float>::value;
   static constexpr int ESZ = sizeof(T);
-  static constexpr int BM = 256, BN = 160, BK = F32 ? 32 : 64, NW = 4, NT = 256;
-  static constexpr int MT = 4, NTL = 10;                 // m-tiles / n-tiles per wave
+  static constexpr int BM = 256, BN = 160, BK = F32 ? 32 : 64, NW = 8, NT = 512;
+  static constexpr int MT = BM / (16 * NW), NTL = 10;    // m-tiles / n-tiles per wave
   static constexpr int CPR = BK * ESZ / 16;              // 16-byte chunks per staged row
   static constexpr int PIT = CPR + 1;                    // padded LDS row pitch (slots)
   static constexpr int SX = cdiv(BM * PIT, 64 * NW) * 64 * NW;   // x slots (whole instructions)
@@ -104,7 +105,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
       op_t xa[C::MT];
 #pragma unroll
       for (int a = 0; a < C::MT; ++a) {
-        const int row = 64 * w + 16 * a + rr;
+        const int row = C::MT * 16 * w + 16 * a + rr;
         // 16-bit: chunk 4*kc + kq holds k = 32 kc + 8 kq .. +7; fp32: 4 floats
         xa[a] = *(const op_t*)(buf + row * C::PIT + 4 * kc + kq);
       }
@@ -169,7 +170,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     for (int a = 0; a < C::MT; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t tok = m0 + 64 * w + 16 * a + 4 * kq + e;
+        const int64_t tok = m0 + C::MT * 16 * w + 16 * a + 4 * kq + e;
         if (tok < p.n_tok) {
           uint8_t* rowp = zb + (p.pos0 + tok) * pitch;
 #pragma unroll
@@ -192,8 +193,8 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     // The region reuses a stage buffer: every wave has passed the main
     // loop's final barrier, so no stage data is read any more.
     constexpr int TP = 20;                                  // floats per staged column (16 tokens + pad)
-    static_assert(C::NW * C::BN * TP * 4 <= C::BUF * 16, "staging");
-    float* zs = (float*)st0 + w * (C::BN * TP);
+    static_assert((C::NW / 2) * C::BN * TP * 4 <= C::BUF * 16, "staging");
+    float* zs = (float*)(w < C::NW / 2 ? st0 : st1) + (w % (C::NW / 2)) * (C::BN * TP);
     uint8_t* sb = (is_v ? p.sv : p.sk) + (int64_t)p.seq * (is_v ? p.seq_sbytes_v : p.seq_sbytes_k) +
                   (is_v ? p.soff_v[gj] : p.soff_k[gj]);
     const int nc_row = cdiv(r, 32);
@@ -205,7 +206,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
       wait_lgkm0();
       for (int it = l; it < 16 * nchunk; it += 64) {
         const int trow = it & 15, c = it >> 4;
-        const int64_t tok = m0 + 64 * w + 16 * a + trow;
+        const int64_t tok = m0 + C::MT * 16 * w + 16 * a + trow;
         const int cg = n0 / 32 + c;                // chunk index within the latent row
         const int n = min(32, r - cg * 32);
         if (tok < p.n_tok) {

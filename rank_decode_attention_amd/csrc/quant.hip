@@ -15,11 +15,14 @@
 
 namespace palu {
 
-template <class T>
-__device__ __forceinline__ float load_f32(const T* p) { return to_f32(*p); }
-
 // One thread per (row, 32-element chunk).  Stores 16 bytes of codes and one
-// binary16 scale.
+// binary16 scale.  The chunk's 32 loads are issued before any is used (the
+// index is clamped inside the row, values past the rank are dropped after).
+// code = rint(fl(z / s)) needs the correctly rounded binary32 quotient only
+// where it decides the rounding: t = z * fl(1 / s) lies within 1.5e-6 of
+// fl(z / s) for |t| < 8 (two roundings of relative size 2^-24 each), so
+// rint(t) is the code unless t is within 4e-6 of a half-integer, where the
+// exact quotient is formed; beyond |t| >= 8 both clamp to +-7.
 template <class T>
 __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z, int64_t n_rows, int r,
                                                          int64_t stride, uint8_t* __restrict__ codes,
@@ -31,26 +34,31 @@ __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z
   const int c = (int)(idx - row * nc);
   const T* zr = z + row * stride + c * 32;
   const int n = min(32, r - c * 32);
+  T raw[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) raw[i] = zr[min(i, n - 1)];
   float v[32];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    v[i] = i < n ? load_f32(zr + i) : 0.f;
+    v[i] = i < n ? to_f32(raw[i]) : 0.f;
     amax = fmaxf(amax, fabsf(v[i]));
   }
   const float s32 = __fdiv_rn(amax, 7.0f);
   const _Float16 s16 = (_Float16)s32;
   const float sf = (float)s16;
   unsigned int words[4] = {0u, 0u, 0u, 0u};
+  if (sf != 0.f) {
+    const float inv = __fdiv_rn(1.0f, sf);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    int q = 0;
-    if (sf != 0.f && i < n) {
-      float qf = rintf(__fdiv_rn(v[i], sf));
+    for (int i = 0; i < 32; ++i) {
+      const float t = v[i] * inv;
+      float qf = rintf(t);
+      if (fabsf(t) < 8.f && fabsf(fabsf(t - qf) - 0.5f) < 4e-6f) qf = rintf(__fdiv_rn(v[i], sf));
       qf = fminf(fmaxf(qf, -7.f), 7.f);
-      q = (int)qf;
+      const int q = i < n ? (int)qf : 0;
+      words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
     }
-    words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
   }
   uint4 packed = make_uint4(words[0], words[1], words[2], words[3]);
   *(uint4*)(codes + row * (int64_t)(16 * nc) + 16 * c) = packed;
