@@ -329,7 +329,7 @@ def bench_prefill(wl, args, hip):
                          "frac": round(q_bytes / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if args.cpu_seqs > 0:
-        n_cpu = 2048
+        n_cpu = n_tok
         xs = oracle.upcast(PI.prefill_x(wl, n_cpu), wl.act)
         Aup = [oracle.upcast(a, wl.act) for a in As]
         times = []
@@ -355,7 +355,7 @@ def main():
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-scrub", action="store_true", help="time with warm caches")
     ap.add_argument("--cpu-seqs", type=int, default=16,
-                    help="sequences in the CPU-oracle sample (0: skip; prefill: any value > 0 times 2048 tokens)")
+                    help="sequences in the CPU-oracle sample (0: skip; prefill workloads: any value > 0 runs it on the whole chunk)")
     ap.add_argument("--detail", default="", help="also write a detailed JSON record to this path")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
