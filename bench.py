@@ -248,9 +248,22 @@ def cpu_baseline(wl, n_seq: int, reps: int = 3):
                                 rope_base=wl.rope_base, sm_scale=1.0 / math.sqrt(wl.head_dim))
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    return {"value": n_seq / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_seq} of {wl.batch} sequences (history {int(lens[0])}, all {wl.n_q_heads} heads), "
-                      f"fp64 numpy, median of {reps} runs of {t:.2f} s"}
+    out = {"value": n_seq / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{n_seq} of {wl.batch} sequences (history {int(lens[0])}, all {wl.n_q_heads} heads), "
+                     f"fp64 numpy, median of {reps} runs of {t:.2f} s"}
+    try:
+        # the same oracle on one host thread, first sequence only
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.decode_attention(q[:1], [z[:1] for z in zk], [z[:1] for z in zv], Bk, Bv, lens[:1],
+                                    n_kv_heads=wl.n_kv_heads, use_rope=wl.use_rope, rope_base=wl.rope_base,
+                                    sm_scale=1.0 / math.sqrt(wl.head_dim))
+            t1 = time.perf_counter() - t0
+        out["one_thread"] = {"value": 1 / t1, "unit": "tokens/s", "sample": f"1 sequence, one run of {t1:.2f} s"}
+    except ImportError:  # pragma: no cover
+        pass
+    return out
 
 
 def bench_prefill(wl, args, hip):
@@ -392,6 +405,8 @@ def main():
 
     ms_step = statistics.mean(t_call)
     ms_main = statistics.mean(t_main)
+    # warm caches (no scrub), for information
+    t_call_w, t_main_w = run_steps(st, max(5, args.steps // 5), None, hip, ev_main=True)
     tokens_per_s = wl.batch / (ms_step * 1e-3)
     # int4 caches: the rate is taken over the whole call (where the expansion
     # runs as a kernel of its own, it is part of the step)
@@ -418,6 +433,9 @@ def main():
             "global_batch": wl.batch, "seq_len": wl.max_len, "parallelism": "single GPU",
             "cache": "cold (1 GiB scrub before each step)" if scrub is not None else "warm",
         },
+        "ms_per_step_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_call, [10, 50, 90])],
+        "warm": {"ms_per_step": round(statistics.mean(t_call_w), 4), "kernel_ms": round(statistics.mean(t_main_w), 4),
+                 "cache": "warm (no scrub; latents partly served from the 256 MB Infinity Cache)"},
         "latent_GBps": round(st["latent_bytes"] / (ms_step * 1e-3) / 1e9, 1),
         "latent_frac_of_hbm_peak": round(st["latent_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
