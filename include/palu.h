@@ -105,6 +105,28 @@ typedef struct {
   int32_t max_len;         /* tokens per (sequence, group) block, > 0 */
 } palu_latent_cache;
 
+/* Caller-owned paged latent cache of one layer (the cache manager's block
+ * tables: PALU page, section "Rollout", engine integration - the cache
+ * manager stores the latents; paged KV and continuous batching compose with
+ * the method).  Each pool is a set of n_pages pages; a page holds page_size
+ * consecutive tokens of one sequence for every group, laid out exactly as
+ * the contiguous cache above with max_len = page_size and "sequence" = page
+ * (so palu_latent_bytes / palu_latent_offset with max_len = page_size give
+ * the pool size and the row offsets inside a page).  Token t of sequence b
+ * lives in page block_table[b * max_pages + t / page_size], row
+ * t % page_size.  Pages may be shared between sequences (read only). */
+typedef struct {
+  void* zk;                     /* device: key latent page pool (codes for I4) */
+  void* zv;                     /* device: value latent page pool */
+  void* sk;                     /* device: I4 key scale page pool, else NULL */
+  void* sv;                     /* device: I4 value scale page pool, else NULL */
+  const int32_t* block_table;   /* device int32 [batch][max_pages]: page index, in [0, n_pages) for
+                                   every page a sequence's history reaches */
+  int32_t page_size;            /* tokens per page: a power of two, >= 32 */
+  int32_t max_pages;            /* block_table row length; histories are at most max_pages * page_size */
+  int32_t n_pages;              /* pages in each pool */
+} palu_paged_cache;
+
 /* Human-readable name of a status code (static string). */
 const char* palu_status_string(palu_status s);
 
@@ -225,6 +247,22 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
                              const void* B_k, const void* B_v, const int32_t* seq_lens,
                              const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * palu_decode_attn_paged - palu_decode_attn over a paged latent cache: the
+ * same computation and results, with row t of sequence b read from page
+ * block_table[b * max_pages + t / page_size] (see palu_paged_cache).
+ * seq_lens are clamped to [0, max_pages * page_size]; the workspace is
+ * palu_decode_workspace_bytes(desc, batch, max_pages * page_size) bytes.
+ * Errors: as palu_decode_attn, plus INVALID_ARG for a NULL block_table,
+ * page_size not a power of two >= 32, max_pages <= 0 or n_pages <= 0;
+ * UNSUPPORTED for I4 pools on shapes other than MHA head-groups of 4 kv
+ * heads with head_dim 128 and RoPE.
+ */
+palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, const palu_paged_cache* cache,
+                                   const void* B_k, const void* B_v, const int32_t* seq_lens,
+                                   const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * palu_profile_events - timing hook for benchmark harnesses (not part of the

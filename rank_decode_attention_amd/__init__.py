@@ -16,9 +16,10 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "PaluError", "AttnDesc", "LatentCache", "lib_path", "load",
+    "PaluError", "AttnDesc", "LatentCache", "PagedCache", "lib_path", "load",
     "latent_bytes", "latent_offset", "row_pitch", "scale_pitch", "alloc_cache", "fill_cache",
-    "decode_workspace_bytes", "palu_decode_attn", "palu_project", "palu_quant_latent", "palu_profile_events",
+    "decode_workspace_bytes", "palu_decode_attn", "palu_decode_attn_paged", "palu_project", "palu_quant_latent",
+    "palu_dequant_latent", "palu_profile_events",
 ]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +51,12 @@ class _Desc(ctypes.Structure):
 class _Cache(ctypes.Structure):
     _fields_ = [("zk", ctypes.c_void_p), ("zv", ctypes.c_void_p), ("sk", ctypes.c_void_p), ("sv", ctypes.c_void_p),
                 ("max_len", ctypes.c_int32)]
+
+
+class _PagedCache(ctypes.Structure):
+    _fields_ = [("zk", ctypes.c_void_p), ("zv", ctypes.c_void_p), ("sk", ctypes.c_void_p), ("sv", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
 
 
 _LIB = None
@@ -85,6 +92,9 @@ def load():
     lib.palu_decode_workspace_bytes.restype = sz
     lib.palu_decode_attn.argtypes = [D, vp, C, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.palu_decode_attn.restype = ctypes.c_int
+    lib.palu_decode_attn_paged.argtypes = [D, vp, ctypes.POINTER(_PagedCache), vp, vp, vp, vp, i32, ctypes.c_float,
+                                           vp, vp, sz, vp]
+    lib.palu_decode_attn_paged.restype = ctypes.c_int
     lib.palu_profile_events.argtypes = [vp, vp]
     lib.palu_profile_events.restype = ctypes.c_int
     _LIB = lib
@@ -131,6 +141,21 @@ class LatentCache:
     def c(self) -> _Cache:
         ptr = lambda t: None if t is None else t.data_ptr()
         return _Cache(ptr(self.zk), ptr(self.zv), ptr(self.sk), ptr(self.sv), self.max_len)
+
+
+class PagedCache:
+    """Caller-owned paged latent pools of one layer (uint8 device tensors) and
+    the block table (int32 device tensor [batch][max_pages])."""
+
+    def __init__(self, zk, zv, sk, sv, block_table, page_size: int, n_pages: int):
+        self.zk, self.zv, self.sk, self.sv, self.block_table = zk, zv, sk, sv, block_table
+        self.page_size, self.n_pages = int(page_size), int(n_pages)
+        self.max_pages = int(block_table.shape[1])
+
+    def c(self) -> _PagedCache:
+        ptr = lambda t: None if t is None else t.data_ptr()
+        return _PagedCache(ptr(self.zk), ptr(self.zv), ptr(self.sk), ptr(self.sv), ptr(self.block_table),
+                           self.page_size, self.max_pages, self.n_pages)
 
 
 def _stream(stream):
@@ -226,6 +251,16 @@ def palu_decode_attn(desc: AttnDesc, q, cache: LatentCache, B_k, B_v, seq_lens, 
                                    seq_lens.data_ptr(), None if q_pos is None else q_pos.data_ptr(),
                                    int(q.shape[0]), float(sm_scale), out.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def palu_decode_attn_paged(desc: AttnDesc, q, cache: PagedCache, B_k, B_v, seq_lens, q_pos, sm_scale: float, out,
+                           workspace, stream=None):
+    """One decode step over a paged latent cache (palu_decode_attn_paged)."""
+    c = cache.c()
+    _check(load().palu_decode_attn_paged(desc.ref(), q.data_ptr(), ctypes.byref(c), B_k.data_ptr(), B_v.data_ptr(),
+                                         seq_lens.data_ptr(), None if q_pos is None else q_pos.data_ptr(),
+                                         int(q.shape[0]), float(sm_scale), out.data_ptr(), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def palu_project(desc: AttnDesc, x, A_kv, cache: LatentCache, seq: int, pos0: int, stream=None):

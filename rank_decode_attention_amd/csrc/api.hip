@@ -344,14 +344,30 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
   return pl.total;
 }
 
-palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
-                             const void* B_k, const void* B_v, const int32_t* seq_lens, const int32_t* q_pos,
-                             int32_t batch, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
-  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+}  // extern "C"
+
+namespace {
+
+// The latent storage one decode call reads: a contiguous cache (rows per
+// block = history bound = max_len) or a paged one (rows per block = page
+// size; rows of sequence b found through the block table).
+struct CacheView {
+  void* zk; void* zv; void* sk; void* sv;
+  int32_t layout_len;            // rows of one (block, group) in the layout
+  int32_t max_len;               // longest history
+  const int32_t* block_table;    // paged: [batch][max_pages], else NULL
+  int32_t page_shift, max_pages;
+};
+
+palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheView* cache, const void* B_k,
+                        const void* B_v, const int32_t* seq_lens, const int32_t* q_pos, int32_t batch,
+                        float sm_scale, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   DecodePlan pl;
   palu_status s = plan_decode(desc, batch, cache->max_len, &pl);
   if (s != PALU_OK) return s;
+  if (cache->block_table && pl.q4 && !pl.fused4)
+    return fail(PALU_ERR_UNSUPPORTED, "paged int4 pools need the MHA head-group kernel shape "
+                                      "(4 kv heads per group, one query head each, head_dim 128, RoPE)");
   if (batch == 0) return ok();   // nothing is read or written
   if (!q || !B_k || !B_v || !seq_lens || !out || !cache->zk || !cache->zv)
     return fail(PALU_ERR_INVALID_ARG, "null pointer");
@@ -369,7 +385,7 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
       return fail(PALU_ERR_INVALID_ARG, "I4 scale buffers must be 2-byte aligned");
   }
   Layout L;
-  make_layout(desc, cache->max_len, &L);
+  make_layout(desc, cache->layout_len, &L);
   uint8_t* const dense_k = (uint8_t*)workspace + pl.hdr_bytes + pl.rec_bytes + pl.qabs_bytes;
   uint8_t* const dense_v = dense_k + pl.dense_k_bytes;
   if (pl.q4 && !pl.fused4) {
@@ -411,6 +427,7 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   p.qabs = desc->use_rope ? nullptr : (const float*)(ws + pl.hdr_bytes + pl.rec_bytes);
   p.out = out;
   p.batch = batch; p.max_len = cache->max_len; p.H = desc->n_q_heads; p.G = desc->n_groups; p.P = pl.P;
+  p.block_table = cache->block_table; p.page_shift = cache->page_shift; p.max_pages = cache->max_pages;
   p.rvp = pl.rvp; p.rec_stride = pl.nq * (2 + pl.rvp); p.qabs_stride = pl.qabs_stride;
   p.qscale = sm_scale * 1.4426950408889634f;
   p.rope_base = desc->rope_base;
@@ -452,6 +469,38 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   e = launch_merge(pl.key, p, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
+                             const void* B_k, const void* B_v, const int32_t* seq_lens, const int32_t* q_pos,
+                             int32_t batch, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
+  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, const palu_paged_cache* cache,
+                                   const void* B_k, const void* B_v, const int32_t* seq_lens,
+                                   const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  const int ps = cache->page_size;
+  if (ps < 32 || (ps & (ps - 1)) != 0) return fail(PALU_ERR_INVALID_ARG, "page_size must be a power of two >= 32");
+  if (cache->max_pages <= 0 || cache->n_pages <= 0) return fail(PALU_ERR_INVALID_ARG, "max_pages and n_pages must be positive");
+  if ((int64_t)cache->max_pages * ps > INT32_MAX / 2) return fail(PALU_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  if (batch > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
+  int shift = 0;
+  while ((1 << shift) < ps) ++shift;
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, ps, cache->max_pages * ps,
+                    cache->block_table, shift, cache->max_pages};
+  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
+                     stream);
 }
 
 }  // extern "C"

@@ -67,6 +67,19 @@ __device__ __forceinline__ void wait_lgkm0() {
 // LDS-DMA prefetches are not drained.  Callers order their own accesses.
 __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
+// Scalar load of a wave-uniform 32-bit value (waits in the same block; it
+// counts in lgkmcnt, so it leaves the vector-memory counter of DMA in flight
+// alone).
+__device__ __forceinline__ int sload_i32(const int* ptr) {
+  const uint64_t a = (uint64_t)ptr;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(u) : "memory");
+  return v;
+}
+
 __device__ __forceinline__ i16x4 ds_read_tr16(const void* lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((PALU_LDS i16x4*)lds_addr);
 }

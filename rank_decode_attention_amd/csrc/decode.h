@@ -44,6 +44,11 @@ struct DecodeParams {
   const uint8_t* sv;
   int64_t seq_sbytes_k, seq_sbytes_v;
   int64_t soff_k[kMaxGroups], soff_v[kMaxGroups];
+  // paged caches: row t of sequence b lies in page block_table[b * max_pages +
+  // (t >> page_shift)] (seq_bytes_* / seq_sbytes_* are then the page sizes and
+  // goff_* / soff_* offsets inside a page); NULL for a contiguous cache
+  const int* block_table;
+  int page_shift, max_pages;
 };
 
 // Key of a compiled decode-attention instantiation.

@@ -249,9 +249,16 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
 
   auto issue_tile = [&](uint4* bufp, int b, int t0, int L) __attribute__((always_inline)) {
     // wave-uniform 64-bit bases, per-lane 32-bit offsets (rows past the
-    // history are clamped to its last row: valid memory, masked later)
-    const uint8_t* kb = zk_seq + (int64_t)b * sbk + (uint32_t)t0 * (uint32_t)pk;
-    const uint8_t* vb = zv_seq + (int64_t)b * sbv + (uint32_t)t0 * (uint32_t)pv;
+    // history are clamped to its last row: valid memory, masked later).
+    // Paged caches: the tile's 32 rows lie in one page (pages hold a power
+    // of two >= 32 rows); block = page index, rows counted inside the page.
+    int blk = b, tin = t0;
+    if (p.block_table) {
+      blk = sload_i32(p.block_table + (int64_t)b * p.max_pages + (t0 >> p.page_shift));
+      tin = t0 & ((1 << p.page_shift) - 1);
+    }
+    const uint8_t* kb = zk_seq + (int64_t)blk * sbk + (uint32_t)tin * (uint32_t)pk;
+    const uint8_t* vb = zv_seq + (int64_t)blk * sbv + (uint32_t)tin * (uint32_t)pv;
     const int lim = L - 1 - t0;
 #pragma unroll
     for (int m = 0; m < C::NIK; ++m) {

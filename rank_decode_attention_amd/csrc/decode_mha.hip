@@ -86,17 +86,6 @@ __device__ __forceinline__ void sincos_turns(double t, double theta_turns, float
   *s = __builtin_amdgcn_sinf(r);
 }
 
-// Scalar load of a wave-uniform 32-bit value (waits in the same block).
-__device__ __forceinline__ int sload_i32(const int* ptr) {
-  const uint64_t a = (uint64_t)ptr;
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(u) : "memory");
-  return v;
-}
-
 // 16-byte global -> LDS copy from a wave-uniform base plus a per-lane 32-bit
 // byte offset; lane l lands at LDS byte `lds_wave_base` + 16*l.
 __device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned lds_wave_base) {
@@ -132,7 +121,7 @@ __device__ __forceinline__ float sum16(float x) {
 
 }  // namespace
 
-template <class LT, int NKC, bool Q4>
+template <class LT, int NKC, bool Q4, bool PAGED>
 __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodeParams p) {
   typedef MhaCfg<LT, NKC, Q4> C;
   typedef typename Vec8<LT>::type op_t;
@@ -369,12 +358,20 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     return L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
   };
   struct DCur { int b, t0, L, st; const uint8_t* kb; const uint8_t* vb; const uint8_t* skb; const uint8_t* svb; };
+  // (paged caches: the block is the page holding token t0, rows are counted
+  // inside it; a page holds a power of two >= 32 rows, so a tile never
+  // straddles two pages)
   auto dma_addr = [&](DCur& d) __attribute__((always_inline)) {
-    d.kb = zk_seq + (int64_t)d.b * sbk + (int64_t)d.t0 * pk;
-    d.vb = zv_seq + (int64_t)d.b * sbv + (int64_t)d.t0 * pv;
+    int blk = d.b, tin = d.t0;
+    if constexpr (PAGED) {
+      blk = sload_i32(p.block_table + (int64_t)d.b * p.max_pages + (d.t0 >> p.page_shift));
+      tin = d.t0 & ((1 << p.page_shift) - 1);
+    }
+    d.kb = zk_seq + (int64_t)blk * sbk + (int64_t)tin * pk;
+    d.vb = zv_seq + (int64_t)blk * sbv + (int64_t)tin * pv;
     if constexpr (C::Q4) {
-      d.skb = sk_seq + (int64_t)d.b * p.seq_sbytes_k + (int64_t)d.t0 * (pk >> 3);
-      d.svb = sv_seq + (int64_t)d.b * p.seq_sbytes_v + (int64_t)d.t0 * (pv >> 3);
+      d.skb = sk_seq + (int64_t)blk * p.seq_sbytes_k + (int64_t)tin * (pk >> 3);
+      d.svb = sv_seq + (int64_t)blk * p.seq_sbytes_v + (int64_t)tin * (pv >> 3);
     }
   };
   DCur cd;
@@ -409,6 +406,8 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       d.t0 = 0;
       d.st = F_START;
       dma_addr(d);
+    } else if (PAGED && (d.t0 & ((1 << p.page_shift) - 1)) == 0) {
+      dma_addr(d);   // next page of the same history
     }
   };
 
@@ -947,13 +946,21 @@ bool mha_supported(const DecodeKey& k, const DecodeParams& p) {
   return p.rvp >= 256;                     // every wave writes its 32 value ranks of the record
 }
 
-template <class LT, int NKC, bool Q4>
-static void launch_mha_q(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+template <class LT, int NKC, bool Q4, bool PAGED>
+static void launch_mha_qp(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const dim3 grid(p.G * p.P), block(512);
   if (t0 && t1)
-    hipExtLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC, Q4>), grid, block, 0, stream, t0, t1, 0, p);
+    hipExtLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC, Q4, PAGED>), grid, block, 0, stream, t0, t1, 0, p);
   else
-    hipLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC, Q4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((palu_decode_mha_kernel<LT, NKC, Q4, PAGED>), grid, block, 0, stream, p);
+}
+
+template <class LT, int NKC, bool Q4>
+static void launch_mha_q(const DecodeParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (p.block_table)
+    launch_mha_qp<LT, NKC, Q4, true>(p, stream, t0, t1);
+  else
+    launch_mha_qp<LT, NKC, Q4, false>(p, stream, t0, t1);
 }
 
 template <class LT, int NKC>

@@ -104,6 +104,78 @@ def build_decode_case(wl: PI.Workload, q_scale: float = 1.0, lens: Optional[np.n
                 sm_scale=1.0 / math.sqrt(wl.head_dim))
 
 
+def paged_from(case: Dict, page_size: int, seed: int = 0, extra_pages: int = 3, share_first: bool = False):
+    """Scatter the latent rows of a contiguous decode case into pages of
+    page_size tokens placed in random order in the pools (data placement
+    only).  Pool bytes that no history reaches, and rows past a history,
+    are 0xFF.  share_first: sequence 1's first page is sequence 0's (its
+    rows must then be equal in the contiguous cache too, which this makes
+    so).  Returns (PagedCache, block_table numpy)."""
+    import torch
+    import rank_decode_attention_amd as R
+    wl, desc, lens, cache = case["wl"], case["desc"], case["lens"], case["cache"]
+    ps, batch, max_len = int(page_size), wl.batch, wl.max_len
+    q4 = desc.latent_dtype == "i4"
+    host = {(w, sc): (cache.sv if sc else cache.zv) if w else (cache.sk if sc else cache.zk)
+            for w in (0, 1) for sc in ((False, True) if q4 else (False,))}
+    host = {k: t.cpu().numpy() for k, t in host.items()}
+    if share_first:
+        assert batch >= 2 and lens[0] >= ps and lens[1] >= ps
+        for (w, sc), buf in host.items():
+            ranks = desc.rank_v if w else desc.rank_k
+            for j in range(desc.n_groups):
+                pitch = R.scale_pitch(ranks[j]) if sc else R.row_pitch(desc.latent_dtype, ranks[j])
+                o0 = R.latent_offset(desc, max_len, w, sc, 0, j, 0)
+                o1 = R.latent_offset(desc, max_len, w, sc, 1, j, 0)
+                buf[o1:o1 + ps * pitch] = buf[o0:o0 + ps * pitch]
+        for (w, sc), buf in host.items():
+            t = (cache.sv if sc else cache.zv) if w else (cache.sk if sc else cache.zk)
+            t.copy_(torch.from_numpy(buf))
+    npg = [(int(L) + ps - 1) // ps for L in lens]
+    total = sum(npg) + extra_pages
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(total)
+    max_pages = (max_len + ps - 1) // ps
+    bt = np.full((batch, max_pages), -1, dtype=np.int32)
+    i = 0
+    for b in range(batch):
+        for k in range(npg[b]):
+            if share_first and b == 1 and k == 0:
+                bt[1, 0] = bt[0, 0]
+                continue
+            bt[b, k] = perm[i]
+            i += 1
+    pools = {}
+    for (w, sc), buf in host.items():
+        pool = np.full(max(16, R.latent_bytes(desc, total, ps, w, sc)), 0xFF, dtype=np.uint8)
+        ranks = desc.rank_v if w else desc.rank_k
+        for b in range(batch):
+            for j in range(desc.n_groups):
+                pitch = R.scale_pitch(ranks[j]) if sc else R.row_pitch(desc.latent_dtype, ranks[j])
+                for k in range(npg[b]):
+                    t0, t1 = k * ps, min((k + 1) * ps, int(lens[b]))
+                    src = R.latent_offset(desc, max_len, w, sc, b, j, t0)
+                    dst = R.latent_offset(desc, ps, w, sc, int(bt[b, k]), j, 0)
+                    pool[dst:dst + (t1 - t0) * pitch] = buf[src:src + (t1 - t0) * pitch]
+        pools[(w, sc)] = torch.from_numpy(pool).cuda()
+    pc = R.PagedCache(pools[(0, False)], pools[(1, False)], pools.get((0, True)), pools.get((1, True)),
+                      torch.from_numpy(bt).cuda(), ps, total)
+    return pc, bt
+
+
+def run_decode_paged(case: Dict, pc, q_pos=None):
+    import torch
+    import rank_decode_attention_amd as R
+    out = torch.empty_like(case["out"])
+    # (the workspace is sized for the paged history bound, max_pages * page_size)
+    wsb = R.decode_workspace_bytes(case["desc"], case["wl"].batch, pc.max_pages * pc.page_size)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    R.palu_decode_attn_paged(case["desc"], case["q"], pc, case["Bk"], case["Bv"], case["seq_lens"], q_pos,
+                             case["sm_scale"], out, ws)
+    torch.cuda.synchronize()
+    return from_device(out)
+
+
 def run_decode(case: Dict, q_pos=None):
     import torch
     import rank_decode_attention_amd as R

@@ -95,6 +95,23 @@ def test_decode_argument_errors(lib):
     assert b"no decode kernel" in lib.palu_last_error()
 
 
+def test_decode_paged_argument_errors(lib):
+    d = _desc()
+    p = ctypes.c_void_p(256)
+
+    def call(page_size=64, max_pages=4, n_pages=8, table=p, batch=1):
+        cache = R._PagedCache(16, 16, None, None, table, page_size, max_pages, n_pages)
+        return lib.palu_decode_attn_paged(d.ref(), p, ctypes.byref(cache), p, p, p, None, batch, 0.1, p, p, 1 << 20,
+                                          None)
+    assert call(page_size=48) == INVALID        # not a power of two
+    assert call(page_size=16) == INVALID        # below one tile
+    assert call(max_pages=0) == INVALID
+    assert call(n_pages=0) == INVALID
+    assert call(table=None) == INVALID
+    assert b"block_table" in lib.palu_last_error()
+    assert lib.palu_decode_attn_paged(d.ref(), p, None, p, p, p, None, 1, 0.1, p, p, 1 << 20, None) == INVALID
+
+
 def test_quant_argument_errors(lib):
     p = ctypes.c_void_p(256)
     assert lib.palu_quant_latent(None, 0, 4, 32, 32, p, p, None) == INVALID
