@@ -52,7 +52,7 @@ def _hip():
     return lib
 
 
-def setup(wl):
+def setup(wl, page_size: int = 0):
     import torch
     import palu_inputs as PI
     import rank_decode_attention_amd as R
@@ -72,7 +72,13 @@ def setup(wl):
         out[:, :a.shape[1]] = a
         return out.view(np.uint8)
 
-    cache = R.fill_cache(desc, wl.batch, wl.max_len, rows)
+    if page_size:
+        # paged cache: pages in a seeded random order, histories up to max_pages * page_size
+        cache = R.fill_paged_cache(desc, lens, page_size, rows, seed=wl.seed)
+        ws_len = cache.max_pages * cache.page_size
+    else:
+        cache = R.fill_cache(desc, wl.batch, wl.max_len, rows)
+        ws_len = wl.max_len
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.act]
 
     def dev(a):
@@ -84,7 +90,7 @@ def setup(wl):
     Bv = dev(np.concatenate([PI.factor(wl, "Bv", j).reshape(-1) for j in range(wl.n_groups)]))
     q = dev(PI.query(wl))
     seq_lens = torch.from_numpy(lens).cuda()
-    ws = torch.empty(R.decode_workspace_bytes(desc, wl.batch, wl.max_len), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(R.decode_workspace_bytes(desc, wl.batch, ws_len), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=tdt, device="cuda")
     if wl.latent == "i4":
         # half a byte per code plus one binary16 scale per 32 elements, keys and values
@@ -95,7 +101,7 @@ def setup(wl):
     recon_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * sum(
         2 * int(r) * wl.group_width for r in ranks)
     pv_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * wl.n_q_heads * 2 * int(ranks.max())
-    return dict(desc=desc, cache=cache, Bk=Bk, Bv=Bv, q=q, seq_lens=seq_lens, ws=ws, out=out,
+    return dict(desc=desc, cache=cache, paged=bool(page_size), Bk=Bk, Bv=Bv, q=q, seq_lens=seq_lens, ws=ws, out=out,
                 sm_scale=1.0 / math.sqrt(wl.head_dim), latent_bytes=latent_bytes,
                 flops=recon_flops + pv_flops, lens=lens)
 
@@ -117,8 +123,9 @@ def run_steps(st, steps, scrub, hip, ev_main):
             R.palu_profile_events(before, after)
             mains.append((before, after))
         starts[i].record()
-        R.palu_decode_attn(st["desc"], st["q"], st["cache"], st["Bk"], st["Bv"], st["seq_lens"], None,
-                           st["sm_scale"], st["out"], st["ws"])
+        call = R.palu_decode_attn_paged if st["paged"] else R.palu_decode_attn
+        call(st["desc"], st["q"], st["cache"], st["Bk"], st["Bv"], st["seq_lens"], None, st["sm_scale"], st["out"],
+             st["ws"])
         ends[i].record()
     R.palu_profile_events(None, None)
     torch.cuda.synchronize()
@@ -367,6 +374,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-scrub", action="store_true", help="time with warm caches")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="read the latents through a paged cache with pages of this many tokens")
     ap.add_argument("--cpu-seqs", type=int, default=16,
                     help="sequences in the CPU-oracle sample (0: skip; prefill workloads: any value > 0 runs it on the whole chunk)")
     ap.add_argument("--detail", default="", help="also write a detailed JSON record to this path")
@@ -395,7 +404,7 @@ def main():
     if wl.n_tok > 0:
         bench_prefill(wl, args, hip)
         return
-    st = setup(wl)
+    st = setup(wl, args.page_size)
     scrub = None if args.no_scrub else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
     run_steps(st, args.warmup, scrub, hip, ev_main=False)
@@ -432,6 +441,7 @@ def main():
                         f"{int(PI.ranks(wl)[0])} per group, {wl.latent} latents, RoPE {wl.use_rope}",
             "global_batch": wl.batch, "seq_len": wl.max_len, "parallelism": "single GPU",
             "cache": "cold (1 GiB scrub before each step)" if scrub is not None else "warm",
+            "layout": f"paged, {args.page_size}-token pages in random order" if args.page_size else "contiguous",
         },
         "ms_per_step_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_call, [10, 50, 90])],
         "warm": {"ms_per_step": round(statistics.mean(t_call_w), 4), "kernel_ms": round(statistics.mean(t_main_w), 4),

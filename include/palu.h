@@ -202,6 +202,20 @@ palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_mo
                          const void* A_kv, const palu_latent_cache* cache, int32_t seq, int32_t pos0,
                          hipStream_t stream);
 
+/*
+ * palu_project_paged - palu_project into a paged cache: the latents of the
+ * n_tok tokens pos0 .. pos0 + n_tok - 1 of sequence `seq` are written to row
+ * t % page_size of page block_table[seq * max_pages + t / page_size]; every
+ * page these positions reach must be assigned (seq indexes the block table's
+ * rows).  Same arithmetic and row contents as palu_project.
+ * Errors: as palu_project (with max_len = max_pages * page_size), plus
+ * INVALID_ARG for a NULL block_table (n_tok > 0), page_size not a power of
+ * two >= 32, max_pages <= 0 or n_pages <= 0.
+ */
+palu_status palu_project_paged(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok,
+                               const void* A_kv, const palu_paged_cache* cache, int32_t seq, int32_t pos0,
+                               hipStream_t stream);
+
 /* Workspace bytes palu_decode_attn needs for `batch` sequences on the
  * current device (0 for an invalid descriptor). */
 size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len);

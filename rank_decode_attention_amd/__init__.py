@@ -18,8 +18,8 @@ import numpy as np
 __all__ = [
     "PaluError", "AttnDesc", "LatentCache", "PagedCache", "lib_path", "load",
     "latent_bytes", "latent_offset", "row_pitch", "scale_pitch", "alloc_cache", "fill_cache",
-    "decode_workspace_bytes", "palu_decode_attn", "palu_decode_attn_paged", "palu_project", "palu_quant_latent",
-    "palu_dequant_latent", "palu_profile_events",
+    "fill_paged_cache", "decode_workspace_bytes", "palu_decode_attn", "palu_decode_attn_paged", "palu_project",
+    "palu_project_paged", "palu_quant_latent", "palu_dequant_latent", "palu_profile_events",
 ]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +87,8 @@ def load():
     lib.palu_dequant_latent.argtypes = [vp, vp, i64, i32, ctypes.c_int, vp, vp]
     lib.palu_dequant_latent.restype = ctypes.c_int
     lib.palu_project.argtypes = [D, vp, i32, i64, vp, C, i32, i32, vp]
+    lib.palu_project_paged.argtypes = [D, vp, i32, i64, vp, ctypes.POINTER(_PagedCache), i32, i32, vp]
+    lib.palu_project_paged.restype = ctypes.c_int
     lib.palu_project.restype = ctypes.c_int
     lib.palu_decode_workspace_bytes.argtypes = [D, i32, i32]
     lib.palu_decode_workspace_bytes.restype = sz
@@ -227,6 +229,46 @@ def fill_cache(desc: AttnDesc, batch: int, max_len: int, rows, device="cuda") ->
     return LatentCache(t[(0, False)], t[(1, False)], t.get((0, True)), t.get((1, True)), max_len)
 
 
+def fill_paged_cache(desc: AttnDesc, lens, page_size: int, rows, seed: int = 0, extra_pages: int = 0,
+                     device="cuda") -> PagedCache:
+    """Build a paged cache from host rows: ``rows(which, b, j)`` returns the
+    first lens[b] rows of (sequence b, group j) as in fill_cache.  Pages are
+    placed in a seeded random order in the pools (extra_pages unused pages,
+    pool bytes no history reaches are zero).  Pure data placement."""
+    import torch
+    ps, batch = int(page_size), len(lens)
+    npg = [(int(L) + ps - 1) // ps for L in lens]
+    total = sum(npg) + int(extra_pages)
+    max_pages = max(1, max(npg) if npg else 1)
+    order = np.random.default_rng(seed).permutation(max(total, 1))
+    table = np.full((batch, max_pages), -1, dtype=np.int32)
+    i = 0
+    for b in range(batch):
+        for k in range(npg[b]):
+            table[b, k] = order[i]
+            i += 1
+    pools = {}
+    for which in (0, 1):
+        ranks = desc.rank_k if which == 0 else desc.rank_v
+        for sc in ((False, True) if desc.latent_dtype == "i4" else (False,)):
+            pools[(which, sc)] = np.zeros(max(16, latent_bytes(desc, max(total, 1), ps, which, sc)), dtype=np.uint8)
+        for b in range(batch):
+            for j in range(desc.n_groups):
+                data = rows(which, b, j)
+                parts = data if isinstance(data, tuple) else (data,)
+                for sc, arr in zip((False, True), parts):
+                    pitch = scale_pitch(ranks[j]) if sc else row_pitch(desc.latent_dtype, ranks[j])
+                    arr = np.ascontiguousarray(arr).view(np.uint8).reshape(arr.shape[0], -1)
+                    assert arr.shape[1] == pitch, (arr.shape, pitch)
+                    for k in range(npg[b]):
+                        t0, t1 = k * ps, min((k + 1) * ps, int(lens[b]))
+                        off = latent_offset(desc, ps, which, sc, int(table[b, k]), j, 0)
+                        pools[(which, sc)][off:off + (t1 - t0) * pitch] = arr[t0:t1].reshape(-1)
+    t = {k: torch.from_numpy(v).to(device) for k, v in pools.items()}
+    return PagedCache(t[(0, False)], t[(1, False)], t.get((0, True)), t.get((1, True)),
+                      torch.from_numpy(table).to(device), ps, max(total, 1))
+
+
 # ------------------------------------------------------------------ entry points
 def decode_workspace_bytes(desc: AttnDesc, batch: int, max_len: int) -> int:
     n = int(load().palu_decode_workspace_bytes(desc.ref(), batch, max_len))
@@ -268,6 +310,13 @@ def palu_project(desc: AttnDesc, x, A_kv, cache: LatentCache, seq: int, pos0: in
     c = cache.c()
     _check(load().palu_project(desc.ref(), x.data_ptr(), int(x.shape[1]), int(x.shape[0]), A_kv.data_ptr(),
                                ctypes.byref(c), int(seq), int(pos0), _stream(stream)))
+
+
+def palu_project_paged(desc: AttnDesc, x, A_kv, cache: PagedCache, seq: int, pos0: int, stream=None):
+    """Prefill latent write into a paged cache (palu_project_paged)."""
+    c = cache.c()
+    _check(load().palu_project_paged(desc.ref(), x.data_ptr(), int(x.shape[1]), int(x.shape[0]), A_kv.data_ptr(),
+                                     ctypes.byref(c), int(seq), int(pos0), _stream(stream)))
 
 
 def palu_dequant_latent(codes, scales, n_rows: int, r: int, out, stream=None):

@@ -291,11 +291,23 @@ palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n
   return ok();
 }
 
-palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
-                         const palu_latent_cache* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Latent storage one prefill writes (contiguous, or paged through a block table).
+struct WriteView {
+  void* zk; void* zv; void* sk; void* sv;
+  int32_t layout_len, max_len;
+  const int32_t* block_table;
+  int32_t page_shift, max_pages;
+};
+
+palu_status project_impl(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
+                         const WriteView* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
   palu_status s = check_desc(desc);
   if (s != PALU_OK) return s;
-  if (!x || !A_kv || !cache || !cache->zk || !cache->zv) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (!x || !A_kv || !cache->zk || !cache->zv) return fail(PALU_ERR_INVALID_ARG, "null pointer");
   if (d_model <= 0 || n_tok < 0 || seq < 0 || pos0 < 0) return fail(PALU_ERR_INVALID_ARG, "bad d_model/n_tok/seq/pos0");
   if (cache->max_len <= 0) return fail(PALU_ERR_INVALID_ARG, "max_len must be positive");
   if ((int64_t)pos0 + n_tok > cache->max_len) return fail(PALU_ERR_INVALID_ARG, "pos0 + n_tok exceeds max_len");
@@ -309,9 +321,10 @@ palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_mo
   if (2 * desc->n_groups > kMaxLatentRows) return fail(PALU_ERR_UNSUPPORTED, "too many groups");
   if (n_tok == 0) return ok();
   Layout L;
-  make_layout(desc, cache->max_len, &L);
+  make_layout(desc, cache->layout_len, &L);
   ProjectParams p;
   memset(&p, 0, sizeof(p));
+  p.block_table = cache->block_table; p.page_shift = cache->page_shift; p.max_pages = cache->max_pages;
   p.x = x; p.A = A_kv;
   p.zk = (uint8_t*)cache->zk; p.zv = (uint8_t*)cache->zv;
   p.sk = (uint8_t*)cache->sk; p.sv = (uint8_t*)cache->sv;
@@ -336,6 +349,42 @@ palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_mo
   hipError_t e = launch_project((int)desc->act_dtype, p, max_rank, stream);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   return ok();
+}
+
+// page_size / max_pages / n_pages checks shared by the paged entry points
+palu_status check_paged(const palu_paged_cache* cache, int* shift) {
+  const int ps = cache->page_size;
+  if (ps < 32 || (ps & (ps - 1)) != 0) return fail(PALU_ERR_INVALID_ARG, "page_size must be a power of two >= 32");
+  if (cache->max_pages <= 0 || cache->n_pages <= 0) return fail(PALU_ERR_INVALID_ARG, "max_pages and n_pages must be positive");
+  if ((int64_t)cache->max_pages * ps > INT32_MAX / 2) return fail(PALU_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  int sh = 0;
+  while ((1 << sh) < ps) ++sh;
+  *shift = sh;
+  return PALU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
+                         const palu_latent_cache* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  const WriteView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
+  return project_impl(desc, x, d_model, n_tok, A_kv, &v, seq, pos0, stream);
+}
+
+palu_status palu_project_paged(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok,
+                               const void* A_kv, const palu_paged_cache* cache, int32_t seq, int32_t pos0,
+                               hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  int shift = 0;
+  palu_status s = check_paged(cache, &shift);
+  if (s != PALU_OK) return s;
+  if (n_tok > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
+  const WriteView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->page_size, cache->max_pages * cache->page_size,
+                    cache->block_table, shift, cache->max_pages};
+  return project_impl(desc, x, d_model, n_tok, A_kv, &v, seq, pos0, stream);
 }
 
 size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len) {
@@ -490,13 +539,11 @@ palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, co
                                    const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
-  const int ps = cache->page_size;
-  if (ps < 32 || (ps & (ps - 1)) != 0) return fail(PALU_ERR_INVALID_ARG, "page_size must be a power of two >= 32");
-  if (cache->max_pages <= 0 || cache->n_pages <= 0) return fail(PALU_ERR_INVALID_ARG, "max_pages and n_pages must be positive");
-  if ((int64_t)cache->max_pages * ps > INT32_MAX / 2) return fail(PALU_ERR_UNSUPPORTED, "max_pages * page_size too large");
-  if (batch > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
   int shift = 0;
-  while ((1 << shift) < ps) ++shift;
+  palu_status s = check_paged(cache, &shift);
+  if (s != PALU_OK) return s;
+  if (batch > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
+  const int ps = cache->page_size;
   const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, ps, cache->max_pages * ps,
                     cache->block_table, shift, cache->max_pages};
   return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,

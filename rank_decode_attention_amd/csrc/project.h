@@ -19,6 +19,11 @@ struct ProjectParams {
   int64_t goff_k[kMaxLatentRows / 2], goff_v[kMaxLatentRows / 2];
   int64_t soff_k[kMaxLatentRows / 2], soff_v[kMaxLatentRows / 2];
   int pk[kMaxLatentRows / 2], pv[kMaxLatentRows / 2];
+  // paged caches: row t of sequence seq lies in page block_table[seq *
+  // max_pages + (t >> page_shift)] (seq_bytes_* are then page sizes and
+  // goff_* / soff_* offsets inside a page); NULL for a contiguous cache
+  const int* block_table;
+  int page_shift, max_pages;
 };
 
 // dtype: 0 = fp32, 1 = fp16, 2 = bf16 (x, A and non-quantised latents)

@@ -162,9 +162,23 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   // ---- epilogue
   const int kq = l >> 4, rr = l & 15;
   const int gj = j % p.G, is_v = j >= p.G;
-  uint8_t* zb = (is_v ? p.zv : p.zk) + (int64_t)p.seq * (is_v ? p.seq_bytes_v : p.seq_bytes_k) +
-                (is_v ? p.goff_v[gj] : p.goff_k[gj]);
   const int pitch = is_v ? p.pv[gj] : p.pk[gj];
+  // block of latent row t of the written sequence (paged: the page holding
+  // t, with t counted inside it)
+  auto blk_of = [&](int64_t t, int64_t& tin) __attribute__((always_inline)) {
+    if (p.block_table) {
+      tin = t & ((1 << p.page_shift) - 1);
+      return (int64_t)p.block_table[(int64_t)p.seq * p.max_pages + (t >> p.page_shift)];
+    }
+    tin = t;
+    return (int64_t)p.seq;
+  };
+  auto zrow = [&](int64_t t) __attribute__((always_inline)) {
+    int64_t tin;
+    const int64_t blk = blk_of(t, tin);
+    return (is_v ? p.zv : p.zk) + blk * (is_v ? p.seq_bytes_v : p.seq_bytes_k) + (is_v ? p.goff_v[gj] : p.goff_k[gj]) +
+           tin * pitch;
+  };
   if (p.quant == 0) {
 #pragma unroll
     for (int a = 0; a < C::MT; ++a)
@@ -172,7 +186,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
       for (int e = 0; e < 4; ++e) {
         const int64_t tok = m0 + C::MT * 16 * w + 16 * a + 4 * kq + e;
         if (tok < p.n_tok) {
-          uint8_t* rowp = zb + (p.pos0 + tok) * pitch;
+          uint8_t* rowp = zrow(p.pos0 + tok);
 #pragma unroll
           for (int b = 0; b < C::NTL; ++b) {
             const int n = n0 + 16 * b + rr;
@@ -195,9 +209,13 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     constexpr int TP = 20;                                  // floats per staged column (16 tokens + pad)
     static_assert((C::NW / 2) * C::BN * TP * 4 <= C::BUF * 16, "staging");
     float* zs = (float*)(w < C::NW / 2 ? st0 : st1) + (w % (C::NW / 2)) * (C::BN * TP);
-    uint8_t* sb = (is_v ? p.sv : p.sk) + (int64_t)p.seq * (is_v ? p.seq_sbytes_v : p.seq_sbytes_k) +
-                  (is_v ? p.soff_v[gj] : p.soff_k[gj]);
     const int nc_row = cdiv(r, 32);
+    auto srow = [&](int64_t t) __attribute__((always_inline)) {
+      int64_t tin;
+      const int64_t blk = blk_of(t, tin);
+      return (is_v ? p.sv : p.sk) + blk * (is_v ? p.seq_sbytes_v : p.seq_sbytes_k) +
+             (is_v ? p.soff_v[gj] : p.soff_k[gj]) + tin * 2 * nc_row;
+    };
     const int nchunk = cdiv(nvalid, 32);
 #pragma unroll
     for (int a = 0; a < C::MT; ++a) {
@@ -226,8 +244,8 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
             }
             words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
           }
-          *(uint4*)(zb + (p.pos0 + tok) * pitch + 16 * cg) = make_uint4(words[0], words[1], words[2], words[3]);
-          ((_Float16*)(sb + (p.pos0 + tok) * 2 * nc_row))[cg] = s16;
+          *(uint4*)(zrow(p.pos0 + tok) + 16 * cg) = make_uint4(words[0], words[1], words[2], words[3]);
+          ((_Float16*)srow(p.pos0 + tok))[cg] = s16;
         }
       }
       wait_lgkm0();   // this m-tile's reads are done before the next one is staged

@@ -68,3 +68,46 @@ def test_paged_int4_unsupported_shape():
     pc, _ = paged_from(case, 64)
     with pytest.raises(R.PaluError, match="paged int4"):
         run_decode_paged(case, pc)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "i4"])
+def test_project_paged_equals_contiguous(fmt):
+    """palu_project_paged writes, row for row, the bytes palu_project writes
+    into a contiguous cache; pool bytes of other pages stay untouched."""
+    import torch
+    import rank_decode_attention_amd as R
+    from palu_cases import desc_of, to_device
+    wl = PI.scaled("int4_prefill", latent=fmt, d_model=512, batch=2, max_len=400, n_tok=300)
+    desc = desc_of(wl)
+    n_tok, seq, pos0, ps = 300, 1, 50, 64
+    x = to_device(PI.prefill_x(wl, n_tok), wl.act)
+    A_kv = to_device(np.ascontiguousarray(np.concatenate([a.T for a in PI.prefill_A(wl)], axis=0)), wl.act)
+    ref = R.alloc_cache(desc, wl.batch, wl.max_len)
+    R.palu_project(desc, x, A_kv, ref, seq, pos0)
+    # pages of sequence 1 in a shuffled pool of 16 pages; block table rows for 2 sequences
+    max_pages = (wl.max_len + ps - 1) // ps
+    n_pages = 16
+    table = np.full((wl.batch, max_pages), -1, dtype=np.int32)
+    table[1, :] = np.random.default_rng(5).permutation(n_pages)[:max_pages]
+    q4 = fmt == "i4"
+    pool = lambda w, sc: torch.full((max(16, R.latent_bytes(desc, n_pages, ps, w, sc)),), 0, dtype=torch.uint8,
+                                    device="cuda")
+    pc = R.PagedCache(pool(0, False), pool(1, False), pool(0, True) if q4 else None, pool(1, True) if q4 else None,
+                      torch.from_numpy(table).cuda(), ps, n_pages)
+    R.palu_project_paged(desc, x, A_kv, pc, seq, pos0)
+    torch.cuda.synchronize()
+    for which in (0, 1):
+        ranks = desc.rank_k if which == 0 else desc.rank_v
+        for sc in ((False, True) if q4 else (False,)):
+            got_pool = (pc.sv if sc else pc.zv) if which else (pc.sk if sc else pc.zk)
+            got_pool = got_pool.cpu().numpy()
+            ref_buf = ((ref.sv if sc else ref.zv) if which else (ref.sk if sc else ref.zk)).cpu().numpy()
+            touched = np.zeros(got_pool.size, dtype=bool)
+            for j in range(desc.n_groups):
+                pitch = R.scale_pitch(ranks[j]) if sc else R.row_pitch(desc.latent_dtype, ranks[j])
+                for t in range(pos0, pos0 + n_tok):
+                    o_ref = R.latent_offset(desc, wl.max_len, which, sc, seq, j, t)
+                    o_pg = R.latent_offset(desc, ps, which, sc, int(table[seq, t // ps]), j, t % ps)
+                    assert np.array_equal(got_pool[o_pg:o_pg + pitch], ref_buf[o_ref:o_ref + pitch]), (which, sc, j, t)
+                    touched[o_pg:o_pg + pitch] = True
+            assert np.all(got_pool[~touched] == 0), "bytes outside the written rows changed"
