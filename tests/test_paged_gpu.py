@@ -1,8 +1,8 @@
 """GPU: palu_decode_attn_paged.  The latent rows of a contiguous decode case
 are scattered into pages placed in random order (unused pool bytes and rows
-past a history are 0xFF), and the paged call must give exactly the
-contiguous call's output (same kernels and arithmetic, other addresses), and
-so meet the oracle bar as well."""
+past a history are 0xFF), and with the same history bound the paged call
+must give exactly the contiguous call's output (same kernels, same split of
+the history, other addresses), and so meet the oracle bar as well."""
 import numpy as np
 import pytest
 
@@ -13,13 +13,14 @@ from palu_cases import (build_decode_case, compare, oracle_decode, paged_from, r
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (name, workload, page size)
-    ("7b_ps32", PI.scaled("llama2_7b", batch=3, max_len=300, fixed_lengths=(300, 1, 77)), 32),
-    ("7b_ps256_empty", PI.scaled("llama2_7b", batch=3, max_len=600, fixed_lengths=(600, 257, 0)), 256),
-    ("long_bf16_ps64", PI.scaled("long_b4", batch=3, max_len=700), 64),
-    ("gqa_rope_ps64", PI.scaled("gqa_rope", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), 64),
-    ("gqa_norope_ps128", PI.scaled("gqa_norope", batch=2, max_len=300, fixed_lengths=(300, 129)), 128),
-    ("int4_ps64", PI.scaled("int4", batch=3, max_len=300, fixed_lengths=(300, 1, 77)), 64),
+    # (name, workload, page size); history bounds are multiples of the page
+    # size, so that both calls plan the same split of the history
+    ("7b_ps32", PI.scaled("llama2_7b", batch=3, max_len=320, fixed_lengths=(300, 1, 77)), 32),
+    ("7b_ps256_empty", PI.scaled("llama2_7b", batch=3, max_len=768, fixed_lengths=(600, 257, 0)), 256),
+    ("long_bf16_ps64", PI.scaled("long_b4", batch=3, max_len=704), 64),
+    ("gqa_rope_ps64", PI.scaled("gqa_rope", batch=3, max_len=256, fixed_lengths=(200, 33, 129)), 64),
+    ("gqa_norope_ps128", PI.scaled("gqa_norope", batch=2, max_len=384, fixed_lengths=(300, 129)), 128),
+    ("int4_ps64", PI.scaled("int4", batch=3, max_len=320, fixed_lengths=(300, 1, 77)), 64),
     ("tiny_f32_ps32", PI.workload("tiny"), 32),
 ]
 
