@@ -279,6 +279,39 @@ palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, co
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * palu_decode_attn_chunk - attention of q_len new tokens per sequence (a
+ * prefill chunk, or tokens to verify) over the latent cache, causal within
+ * the chunk: the same computation as palu_decode_attn for every query, with
+ * query i of sequence b at position p = L_b - q_len + i attending to the
+ * cached tokens 0 .. p (their latents, including the chunk's own, already
+ * written; RoPE position p).  p < 0 gives a zero output row.
+ *   q, out     device [batch][q_len][H][d_h] act_dtype
+ *   seq_lens   device int32 [batch]: L_b, clamped to [0, max_len]
+ *   workspace  palu_decode_chunk_workspace_bytes(desc, batch, q_len, max_len, 1) bytes
+ * The queries run as batch * q_len decode sequences that share their
+ * sequence's latents (batch * q_len <= 2048).  Errors: as palu_decode_attn,
+ * plus INVALID_ARG for q_len <= 0; UNSUPPORTED for batch * q_len > 2048 and
+ * for I4 caches on shapes other than MHA head-groups of 4 kv heads with
+ * head_dim 128 and RoPE.
+ */
+palu_status palu_decode_attn_chunk(const palu_attn_desc* desc, const void* q, int32_t q_len,
+                                   const palu_latent_cache* cache, const void* B_k, const void* B_v,
+                                   const int32_t* seq_lens, int32_t batch, float sm_scale, void* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same over a paged cache; workspace:
+ * palu_decode_chunk_workspace_bytes(desc, batch, q_len, max_pages * page_size, max_pages). */
+palu_status palu_decode_attn_chunk_paged(const palu_attn_desc* desc, const void* q, int32_t q_len,
+                                         const palu_paged_cache* cache, const void* B_k, const void* B_v,
+                                         const int32_t* seq_lens, int32_t batch, float sm_scale, void* out,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of a chunk call (max_pages: 1 for a contiguous cache);
+ * 0 for invalid arguments. */
+size_t palu_decode_chunk_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t q_len, int32_t max_len,
+                                         int32_t max_pages);
+
+/*
  * palu_profile_events - timing hook for benchmark harnesses (not part of the
  * method).  When both are set (non-NULL), every later palu_decode_attn call
  * on the calling thread launches its main split-attention kernel with

@@ -59,7 +59,7 @@ import numpy as np
 __all__ = [
     "upcast", "rope_theta", "rope", "reconstruct", "attend", "attend_partial", "merge_partials",
     "decode_attention", "project", "quant_int4", "pack_int4", "unpack_int4", "dequant_int4",
-    "chunks_per_row", "round_to", "int4_latent",
+    "chunks_per_row", "round_to", "int4_latent", "chunk_attention",
 ]
 
 QUANT_GROUP = 32
@@ -207,6 +207,26 @@ def decode_attention(q: np.ndarray, zk: Sequence[np.ndarray], zv: Sequence[np.nd
 
 
 # ------------------------------------------------------------------ prefill
+def chunk_attention(q: np.ndarray, zk, zv, Bk, Bv, seq_lens: Sequence[int], *, n_kv_heads: int,
+                    use_rope: bool = True, rope_base: float = 10000.0,
+                    sm_scale: Optional[float] = None) -> np.ndarray:
+    """Attention of a chunk of q_len new tokens per sequence, causal within
+    the chunk (reading of the pages' prefill/decode flow for several new
+    tokens: every new token attends to the history up to and including
+    itself).  q [batch][q_len][H][d_h]; the chunk's latents are the last
+    q_len of the L_b cached rows, so query i sits at p = L_b - q_len + i and
+    sees rows 0..p; p < 0 gives zeros.  Returns [batch][q_len][H][d_h]."""
+    q = np.asarray(q, dtype=np.float64)
+    batch, q_len = q.shape[:2]
+    out = np.zeros(q.shape)
+    for i in range(q_len):
+        pos = [int(seq_lens[b]) - q_len + i for b in range(batch)]
+        lens = [p + 1 if p >= 0 else 0 for p in pos]
+        out[:, i] = decode_attention(q[:, i], zk, zv, Bk, Bv, lens, [max(p, 0) for p in pos], n_kv_heads=n_kv_heads,
+                                     use_rope=use_rope, rope_base=rope_base, sm_scale=sm_scale)
+    return out
+
+
 def project(x: np.ndarray, A: np.ndarray) -> np.ndarray:
     """Prefill latents z = x A (fp64)."""
     return np.asarray(x, dtype=np.float64) @ np.asarray(A, dtype=np.float64)

@@ -39,12 +39,12 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "scaled",
     "to_f16", "to_bf16_bits", "to_format",
-    "ranks", "lengths", "factor", "latent", "latent_f32", "latent_int4", "query", "prefill_x",
+    "ranks", "lengths", "factor", "latent", "latent_f32", "latent_int4", "query", "query_chunk", "prefill_x",
     "prefill_A",
 ]
 
 # stream tags (stable: changing them changes every generated array)
-_T_RANK, _T_LEN, _T_BK, _T_BV, _T_AK, _T_AV, _T_ZK, _T_ZV, _T_Q, _T_X, _T_QK4, _T_QV4 = range(1, 13)
+_T_RANK, _T_LEN, _T_BK, _T_BV, _T_AK, _T_AV, _T_ZK, _T_ZV, _T_Q, _T_X, _T_QK4, _T_QV4, _T_QC = range(1, 14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -219,6 +219,12 @@ def latent_int4(wl: Workload, which: str, b: int, g: int, n: Optional[int] = Non
 def query(wl: Workload) -> np.ndarray:
     """Decode queries [batch][n_q_heads][head_dim] in the activation format."""
     x = _rng(wl, _T_Q).standard_normal((wl.batch, wl.n_q_heads, wl.head_dim), dtype=np.float32)
+    return to_format(x, wl.act)
+
+
+def query_chunk(wl: Workload, q_len: int) -> np.ndarray:
+    """Queries of a chunk of q_len tokens per sequence [batch][q_len][n_q_heads][head_dim]."""
+    x = _rng(wl, _T_QC, q_len).standard_normal((wl.batch, q_len, wl.n_q_heads, wl.head_dim), dtype=np.float32)
     return to_format(x, wl.act)
 
 

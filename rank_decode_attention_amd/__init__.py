@@ -20,6 +20,7 @@ __all__ = [
     "latent_bytes", "latent_offset", "row_pitch", "scale_pitch", "alloc_cache", "fill_cache",
     "fill_paged_cache", "decode_workspace_bytes", "palu_decode_attn", "palu_decode_attn_paged", "palu_project",
     "palu_project_paged", "palu_quant_latent", "palu_dequant_latent", "palu_profile_events",
+    "chunk_workspace_bytes", "palu_decode_attn_chunk",
 ]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,13 @@ def load():
     lib.palu_decode_attn_paged.argtypes = [D, vp, ctypes.POINTER(_PagedCache), vp, vp, vp, vp, i32, ctypes.c_float,
                                            vp, vp, sz, vp]
     lib.palu_decode_attn_paged.restype = ctypes.c_int
+    lib.palu_decode_attn_chunk.argtypes = [D, vp, i32, C, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
+    lib.palu_decode_attn_chunk.restype = ctypes.c_int
+    lib.palu_decode_attn_chunk_paged.argtypes = [D, vp, i32, ctypes.POINTER(_PagedCache), vp, vp, vp, i32,
+                                                 ctypes.c_float, vp, vp, sz, vp]
+    lib.palu_decode_attn_chunk_paged.restype = ctypes.c_int
+    lib.palu_decode_chunk_workspace_bytes.argtypes = [D, i32, i32, i32, i32]
+    lib.palu_decode_chunk_workspace_bytes.restype = sz
     lib.palu_profile_events.argtypes = [vp, vp]
     lib.palu_profile_events.restype = ctypes.c_int
     _LIB = lib
@@ -303,6 +311,26 @@ def palu_decode_attn_paged(desc: AttnDesc, q, cache: PagedCache, B_k, B_v, seq_l
                                          seq_lens.data_ptr(), None if q_pos is None else q_pos.data_ptr(),
                                          int(q.shape[0]), float(sm_scale), out.data_ptr(), workspace.data_ptr(),
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def chunk_workspace_bytes(desc: AttnDesc, batch: int, q_len: int, max_len: int, max_pages: int = 1) -> int:
+    n = int(load().palu_decode_chunk_workspace_bytes(desc.ref(), batch, q_len, max_len, max_pages))
+    if n == 0:
+        raise PaluError(-1, "palu_decode_chunk_workspace_bytes", load().palu_last_error().decode())
+    return n
+
+
+def palu_decode_attn_chunk(desc: AttnDesc, q, cache, B_k, B_v, seq_lens, sm_scale: float, out, workspace,
+                           stream=None):
+    """Causal attention of a chunk of q_len tokens per sequence
+    (palu_decode_attn_chunk / _paged): q and out are [batch][q_len][H][d_h];
+    cache is a LatentCache or a PagedCache."""
+    paged = isinstance(cache, PagedCache)
+    c = cache.c()
+    fn = load().palu_decode_attn_chunk_paged if paged else load().palu_decode_attn_chunk
+    _check(fn(desc.ref(), q.data_ptr(), int(q.shape[1]), ctypes.byref(c), B_k.data_ptr(), B_v.data_ptr(),
+              seq_lens.data_ptr(), int(q.shape[0]), float(sm_scale), out.data_ptr(), workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def palu_project(desc: AttnDesc, x, A_kv, cache: LatentCache, seq: int, pos0: int, stream=None):

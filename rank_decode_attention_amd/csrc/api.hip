@@ -551,3 +551,80 @@ palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, co
 }
 
 }  // extern "C"
+
+namespace {
+
+// workspace of a chunk call: virtual lengths, positions and block-table rows,
+// then the decode workspace of the virtual batch
+size_t chunk_front_bytes(int64_t vbatch, int max_pages) {
+  return (size_t)roundup(vbatch * (2 + (int64_t)max_pages) * 4, 256);
+}
+
+palu_status chunk_impl(const palu_attn_desc* desc, const void* q, int32_t q_len, const CacheView* base,
+                       const void* B_k, const void* B_v, const int32_t* seq_lens, int32_t batch, float sm_scale,
+                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (q_len <= 0) return fail(PALU_ERR_INVALID_ARG, "q_len must be positive");
+  if (batch < 0) return fail(PALU_ERR_INVALID_ARG, "batch < 0");
+  const int64_t vbatch = (int64_t)batch * q_len;
+  if (vbatch > kMaxBatch) return fail(PALU_ERR_UNSUPPORTED, "batch * q_len above %d", kMaxBatch);
+  if (batch == 0) return decode_impl(desc, q, base, B_k, B_v, seq_lens, nullptr, 0, sm_scale, out, workspace,
+                                     workspace_bytes, stream);
+  if (!seq_lens || !workspace) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(PALU_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t front = chunk_front_bytes(vbatch, base->max_pages);
+  if (workspace_bytes < front) return fail(PALU_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the chunk");
+  int* vlens = (int*)workspace;
+  int* vqpos = vlens + vbatch;
+  int* vtable = vqpos + vbatch;
+  hipError_t e = launch_chunk_expand(seq_lens, base->block_table, batch, q_len, base->max_len, base->max_pages,
+                                     vlens, vqpos, vtable, stream);
+  if (e != hipSuccess) return hip_fail(e, "chunk expansion launch");
+  CacheView v = *base;
+  v.block_table = vtable;
+  return decode_impl(desc, q, &v, B_k, B_v, vlens, vqpos, (int32_t)vbatch, sm_scale, out, (uint8_t*)workspace + front,
+                     workspace_bytes - front, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t palu_decode_chunk_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t q_len, int32_t max_len,
+                                         int32_t max_pages) {
+  if (batch < 0 || q_len <= 0 || max_pages < 0) return 0;
+  const int64_t vbatch = (int64_t)batch * q_len;
+  if (vbatch > kMaxBatch) return 0;
+  const size_t d = palu_decode_workspace_bytes(desc, (int32_t)vbatch, max_len);
+  return d == 0 ? 0 : d + chunk_front_bytes(vbatch, max_pages > 0 ? max_pages : 1);
+}
+
+palu_status palu_decode_attn_chunk(const palu_attn_desc* desc, const void* q, int32_t q_len,
+                                   const palu_latent_cache* cache, const void* B_k, const void* B_v,
+                                   const int32_t* seq_lens, int32_t batch, float sm_scale, void* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  if (cache->max_len <= 0) return fail(PALU_ERR_INVALID_ARG, "max_len must be positive");
+  // a contiguous cache is a pool of one block per sequence: block b, rows
+  // counted from 0 (the shift only has to exceed every row index)
+  int shift = 0;
+  while ((1 << shift) < cache->max_len) ++shift;
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, shift, 1};
+  return chunk_impl(desc, q, q_len, &v, B_k, B_v, seq_lens, batch, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+palu_status palu_decode_attn_chunk_paged(const palu_attn_desc* desc, const void* q, int32_t q_len,
+                                         const palu_paged_cache* cache, const void* B_k, const void* B_v,
+                                         const int32_t* seq_lens, int32_t batch, float sm_scale, void* out,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  int shift = 0;
+  palu_status s = check_paged(cache, &shift);
+  if (s != PALU_OK) return s;
+  if (batch > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
+  const int ps = cache->page_size;
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, ps, cache->max_pages * ps, cache->block_table, shift,
+                    cache->max_pages};
+  return chunk_impl(desc, q, q_len, &v, B_k, B_v, seq_lens, batch, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

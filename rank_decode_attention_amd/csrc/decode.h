@@ -70,5 +70,9 @@ bool mha_supported(const DecodeKey& k, const DecodeParams& p);
 hipError_t launch_decode_mha(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
                              hipEvent_t t1);
 hipError_t launch_merge(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
+// Virtual sequences of a multi-query chunk (see decode.hip): lengths, query
+// positions and block-table rows (block_table NULL: row b is block b).
+hipError_t launch_chunk_expand(const int* seq_lens, const int* block_table, int batch, int q_len, int max_len,
+                               int max_pages, int* vlens, int* vqpos, int* vtable, hipStream_t stream);
 
 }  // namespace palu

@@ -1072,4 +1072,32 @@ hipError_t launch_merge(const DecodeKey& k, const DecodeParams& p, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+// Multi-query (chunk) attention as decode over virtual sequences: query i
+// of sequence b (v = b q_len + i) sits at position L_b - q_len + i and sees
+// the history up to and including it; its latent rows are sequence b's
+// (the block-table row of b, or block b of a contiguous cache).
+__global__ void __launch_bounds__(256) palu_chunk_expand_kernel(const int* seq_lens, const int* block_table, int batch,
+                                                                 int q_len, int max_len, int max_pages, int* vlens,
+                                                                 int* vqpos, int* vtable) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= batch * q_len) return;
+  const int b = v / q_len, i = v - b * q_len;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > max_len ? max_len : L);
+  const int pos = L - q_len + i;
+  vlens[v] = pos >= 0 ? pos + 1 : 0;
+  vqpos[v] = pos >= 0 ? pos : 0;
+  for (int k = 0; k < max_pages; ++k)
+    vtable[(int64_t)v * max_pages + k] = block_table ? block_table[(int64_t)b * max_pages + k] : b;
+}
+
+hipError_t launch_chunk_expand(const int* seq_lens, const int* block_table, int batch, int q_len, int max_len,
+                               int max_pages, int* vlens, int* vqpos, int* vtable, hipStream_t stream) {
+  const int n = batch * q_len;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(palu_chunk_expand_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, seq_lens,
+                     block_table, batch, q_len, max_len, max_pages, vlens, vqpos, vtable);
+  return hipGetLastError();
+}
+
 }  // namespace palu

@@ -198,6 +198,36 @@ def oracle_decode(case: Dict, heads: Optional[Sequence[Tuple[int, int]]] = None,
                                    heads=heads)
 
 
+def run_chunk(case: Dict, q_len: int, paged=None):
+    """Chunk attention of q_len seeded queries per sequence over the case's
+    cache (or a PagedCache of the same rows); returns (gpu, host queries)."""
+    import torch
+    import rank_decode_attention_amd as R
+    wl = case["wl"]
+    qh = PI.query_chunk(wl, q_len)
+    q = to_device(qh, wl.act)
+    out = torch.empty(qh.shape, dtype=_torch_dtype(wl.act), device="cuda")
+    cache = paged if paged is not None else case["cache"]
+    if paged is not None:
+        wsb = R.chunk_workspace_bytes(case["desc"], wl.batch, q_len, paged.max_pages * paged.page_size, paged.max_pages)
+    else:
+        wsb = R.chunk_workspace_bytes(case["desc"], wl.batch, q_len, wl.max_len, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    R.palu_decode_attn_chunk(case["desc"], q, cache, case["Bk"], case["Bv"], case["seq_lens"], case["sm_scale"], out, ws)
+    torch.cuda.synchronize()
+    return from_device(out), qh
+
+
+def oracle_chunk(case: Dict, qh: np.ndarray) -> np.ndarray:
+    wl, lens = case["wl"], case["lens"]
+    zk = [LazyLatents(wl, "k", j, lens) for j in range(wl.n_groups)]
+    zv = [LazyLatents(wl, "v", j, lens) for j in range(wl.n_groups)]
+    Bk = [oracle.upcast(b, wl.act) for b in case["Bk_host"]]
+    Bv = [oracle.upcast(b, wl.act) for b in case["Bv_host"]]
+    return oracle.chunk_attention(oracle.upcast(qh, wl.act), zk, zv, Bk, Bv, lens, n_kv_heads=wl.n_kv_heads,
+                                  use_rope=wl.use_rope, rope_base=wl.rope_base, sm_scale=case["sm_scale"])
+
+
 def half_ulp(ref: np.ndarray, fmt: str) -> np.ndarray:
     mag = np.maximum(np.abs(ref), 2.0 ** -14)
     return 0.5 * 2.0 ** (np.floor(np.log2(mag)) - _ULP_BITS[fmt])

@@ -112,6 +112,18 @@ def test_decode_paged_argument_errors(lib):
     assert lib.palu_decode_attn_paged(d.ref(), p, None, p, p, p, None, 1, 0.1, p, p, 1 << 20, None) == INVALID
 
 
+def test_chunk_argument_errors(lib):
+    d = _desc()
+    p = ctypes.c_void_p(256)
+    cache = R._Cache(16, 16, None, None, 64)
+    call = lambda q_len, batch=1: lib.palu_decode_attn_chunk(d.ref(), p, q_len, ctypes.byref(cache), p, p, p, batch,
+                                                             0.1, p, p, 1 << 30, None)
+    assert call(0) == INVALID
+    assert call(-2) == INVALID
+    assert call(64, batch=64) == UNSUP                 # more than 2048 virtual sequences
+    assert lib.palu_decode_chunk_workspace_bytes(d.ref(), 1, 0, 64, 1) == 0
+
+
 def test_quant_argument_errors(lib):
     p = ctypes.c_void_p(256)
     assert lib.palu_quant_latent(None, 0, 4, 32, 32, p, p, None) == INVALID

@@ -383,9 +383,42 @@ def pin_int4_latent():
     assert O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[0.5]], np.float16), 3, "f16").shape == (1, 3)
 
 
+def pin_chunk_attention():
+    """Chunk attention: q_len = 1 is the decode step; later latents do not
+    reach earlier queries; in the identity case A = W, B = I it equals
+    standard attention with a causal offset mask (torch SDPA, float64)."""
+    import torch
+    rng = np.random.default_rng(21)
+    q, zk, zv, Bk, Bv, lens = _rand_case(rng, batch=2, H=4, Hkv=2, d_h=8, G=2, r=5, L=9)
+    lens = np.array([9, 6])
+    q1 = q[:, None]
+    a = oracle.chunk_attention(q1, zk, zv, Bk, Bv, lens, n_kv_heads=2)
+    b = oracle.decode_attention(q, zk, zv, Bk, Bv, lens, n_kv_heads=2)
+    assert np.allclose(a[:, 0], b, atol=1e-13)
+    qc = rng.standard_normal((2, 4, 4, 8))
+    base = oracle.chunk_attention(qc, zk, zv, Bk, Bv, lens, n_kv_heads=2)
+    zk2 = [z.copy() for z in zk]
+    zv2 = [z.copy() for z in zv]
+    for z in zk2 + zv2:
+        z[0, 7:] += 5.0                      # rows past query 1's position (L 9, q_len 4: p = 5, 6, 7, 8)
+    moved = oracle.chunk_attention(qc, zk2, zv2, Bk, Bv, lens, n_kv_heads=2)
+    assert np.allclose(moved[0, :2], base[0, :2], atol=1e-13) and not np.allclose(moved[0, 2:], base[0, 2:])
+    # identity: K = z_k, V = z_v, one group of one kv head, no RoPE, mask t <= L - q_len + i
+    d, L, ql = 6, 7, 3
+    zk1 = [rng.standard_normal((1, L, d))]
+    zv1 = [rng.standard_normal((1, L, d))]
+    qq = rng.standard_normal((1, ql, 1, d))
+    got = oracle.chunk_attention(qq, zk1, zv1, [np.eye(d)], [np.eye(d)], [L], n_kv_heads=1, use_rope=False)
+    mask = torch.tensor([[t <= L - ql + i for t in range(L)] for i in range(ql)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qq[:, :, 0][:, None]), torch.from_numpy(zk1[0][:, None]), torch.from_numpy(zv1[0][:, None]),
+        attn_mask=mask, scale=1.0 / math.sqrt(d))
+    assert np.allclose(got[:, :, 0], ref[:, 0].numpy(), atol=1e-12)
+
+
 PINS = [pin_absorbed_and_fused_value, pin_mpmath_bruteforce, pin_softmax_closed_forms, pin_rope, pin_gqa,
         pin_split_merge, pin_golden_decode, pin_rope_closed_form_d2, pin_project, pin_int4_golden,
-        pin_int4_properties, pin_upcast, pin_round_to, pin_int4_latent]
+        pin_int4_properties, pin_upcast, pin_round_to, pin_int4_latent, pin_chunk_attention]
 
 
 @pytest.mark.parametrize("use_rope", [False, True])
