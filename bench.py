@@ -367,6 +367,76 @@ def bench_prefill(wl, args, hip):
     print(json.dumps(line), flush=True)
 
 
+def bench_chunk(wl, args, hip):
+    """Chunk attention (palu_decode_attn_chunk): q_len new tokens per
+    sequence, causal within the chunk, over the workload's cache.  The
+    queries run as batch * q_len decode sequences; `achieved` counts each
+    sequence's latent bytes once (what the chunk has to read)."""
+    import torch
+    import palu_inputs as PI
+    import rank_decode_attention_amd as R
+    st = setup(wl, args.page_size)
+    ql = args.q_len
+    qh = PI.query_chunk(wl, ql)
+    if wl.act == "bf16":
+        q = torch.from_numpy(np.ascontiguousarray(qh).view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(np.ascontiguousarray(qh)).cuda()
+    out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    cache = st["cache"]
+    if st["paged"]:
+        wsb = R.chunk_workspace_bytes(st["desc"], wl.batch, ql, cache.max_pages * cache.page_size, cache.max_pages)
+    else:
+        wsb = R.chunk_workspace_bytes(st["desc"], wl.batch, ql, wl.max_len, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    scrub = None if args.no_scrub else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def call():
+        R.palu_decode_attn_chunk(st["desc"], q, cache, st["Bk"], st["Bv"], st["seq_lens"], st["sm_scale"], out, ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ts, mains = [], []
+    for i in range(args.steps):
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
+        before, after = ctypes.c_void_p(), ctypes.c_void_p()
+        hip.hipEventCreate(ctypes.byref(before))
+        hip.hipEventCreate(ctypes.byref(after))
+        R.palu_profile_events(before, after)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        ts.append((a, b))
+        mains.append((before, after))
+    R.palu_profile_events(None, None)
+    torch.cuda.synchronize()
+    ms_step = statistics.mean(a.elapsed_time(b) for a, b in ts)
+    kms = []
+    for before, after in mains:
+        ms = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(ms), before, after)
+        kms.append(ms.value)
+        hip.hipEventDestroy(before)
+        hip.hipEventDestroy(after)
+    ms_main = statistics.mean(kms)
+    achieved = st["latent_bytes"] / (ms_main * 1e-3) / 1e9
+    line = {
+        "metric": f"chunk attention tokens/s ({ql} new tokens per sequence, causal) at {wl.name} workload shape",
+        "value": round(wl.batch * ql / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.act, "data": "synthetic (seeded latents, queries and factors)",
+        "config": {"workload": f"{wl.name} with {ql}-token chunks", "global_batch": wl.batch, "seq_len": wl.max_len,
+                   "q_len": ql, "parallelism": "single GPU",
+                   "layout": f"paged, {args.page_size}-token pages" if args.page_size else "contiguous"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": main_kernel_name(wl),
+                     "kernel_ms": round(ms_main, 4), "algorithmic_bytes": st["latent_bytes"]},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -374,6 +444,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-scrub", action="store_true", help="time with warm caches")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="new tokens per sequence: above 1, time the chunk attention (causal within the chunk)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="read the latents through a paged cache with pages of this many tokens")
     ap.add_argument("--cpu-seqs", type=int, default=16,
@@ -403,6 +475,9 @@ def main():
     hip = _hip()
     if wl.n_tok > 0:
         bench_prefill(wl, args, hip)
+        return
+    if args.q_len > 1:
+        bench_chunk(wl, args, hip)
         return
     st = setup(wl, args.page_size)
     scrub = None if args.no_scrub else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
