@@ -12,9 +12,14 @@ Before each timed step a 1 GiB buffer is overwritten so that no latent bytes
 are served from the 256 MB Infinity Cache or the L2s (cold-cache timing).
 
 Output (stdout, one JSON line): decode tokens/s (batch / step time), plus
-`roofline` for the dominant kernel (the fused split-attention kernel, timed
-with HIP events recorded around it by the library) and `cpu_baseline` (the
+`roofline` for the dominant kernel (the decode kernel the library picks,
+timed with HIP events stamped by its own dispatch) and `cpu_baseline` (the
 fp64 oracle on the host cores on a bounded sample of the same workload).
+
+Other modes: `--workload NAME` (any workload of palu_inputs; prefill
+workloads time palu_project and palu_quant_latent), `--page-size N` (the
+latents through a paged cache), `--q-len N` (chunk attention, N new tokens
+per sequence).  `--gpus` above 1 is refused: the path runs on one GPU.
 """
 from __future__ import annotations
 

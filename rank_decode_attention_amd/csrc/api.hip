@@ -205,96 +205,6 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   pl->total = pl->hdr_bytes + pl->rec_bytes + pl->qabs_bytes + pl->dense_k_bytes + pl->dense_v_bytes;
   return PALU_OK;
 }
-
-}  // namespace
-
-extern "C" {
-
-const char* palu_status_string(palu_status s) {
-  switch (s) {
-    case PALU_OK: return "PALU_OK";
-    case PALU_ERR_INVALID_ARG: return "PALU_ERR_INVALID_ARG";
-    case PALU_ERR_UNSUPPORTED: return "PALU_ERR_UNSUPPORTED";
-    case PALU_ERR_WORKSPACE_TOO_SMALL: return "PALU_ERR_WORKSPACE_TOO_SMALL";
-    case PALU_ERR_HIP: return "PALU_ERR_HIP";
-  }
-  return "PALU_ERR_UNKNOWN";
-}
-
-const char* palu_last_error(void) { return g_err; }
-
-palu_status palu_profile_events(hipEvent_t before_main, hipEvent_t after_main) {
-  g_prof_before = before_main;
-  g_prof_after = after_main;
-  return ok();
-}
-
-size_t palu_latent_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len, int32_t which,
-                         int32_t scales) {
-  if (check_desc(desc) != PALU_OK || batch < 0 || max_len <= 0 || (which != 0 && which != 1)) return 0;
-  if (scales && desc->latent_dtype != PALU_I4) return 0;
-  Layout L;
-  make_layout(desc, max_len, &L);
-  const int64_t per = scales ? (which ? L.seq_sv : L.seq_sk) : (which ? L.seq_v : L.seq_k);
-  return (size_t)(per * batch);
-}
-
-int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t which, int32_t scales, int32_t b,
-                           int32_t j, int32_t t) {
-  if (check_desc(desc) != PALU_OK || max_len <= 0 || (which != 0 && which != 1)) return -1;
-  if (b < 0 || j < 0 || j >= desc->n_groups || t < 0 || t >= max_len) return -1;
-  if (scales && desc->latent_dtype != PALU_I4) return -1;
-  Layout L;
-  make_layout(desc, max_len, &L);
-  if (scales)
-    return which ? b * L.seq_sv + L.soff_v[j] + t * L.spv[j] : b * L.seq_sk + L.soff_k[j] + t * L.spk[j];
-  return which ? b * L.seq_v + L.goff_v[j] + t * L.pv[j] : b * L.seq_k + L.goff_k[j] + t * L.pk[j];
-}
-
-palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r, int64_t z_row_stride,
-                              void* codes, void* scales, hipStream_t stream) {
-  if (n_rows < 0 || r <= 0 || z_row_stride < r) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r / z_row_stride");
-  if (z_dtype == PALU_I4) return fail(PALU_ERR_UNSUPPORTED, "input must be F32, F16 or BF16");
-  if (!valid_dtype(z_dtype)) return fail(PALU_ERR_INVALID_ARG, "invalid dtype");
-  if (n_rows == 0) return ok();
-  if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
-  if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
-  hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream);
-  if (e != hipSuccess) return hip_fail(e, "quantiser launch");
-  return ok();
-}
-
-palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n_rows, int32_t r,
-                                palu_dtype out_dtype, void* out, hipStream_t stream) {
-  if (n_rows < 0 || r <= 0) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r");
-  if (out_dtype != PALU_F16 && out_dtype != PALU_BF16) return fail(PALU_ERR_UNSUPPORTED, "out_dtype must be F16 or BF16");
-  if (n_rows == 0) return ok();
-  if (!codes || !scales || !out) return fail(PALU_ERR_INVALID_ARG, "null pointer");
-  if (((uintptr_t)codes & 3u) != 0 || ((uintptr_t)scales & 1u) != 0 || !aligned16(out))
-    return fail(PALU_ERR_INVALID_ARG, "codes must be 4-byte, scales 2-byte and out 16-byte aligned");
-  const int nch = (r + 31) / 32;
-  if (n_rows > INT32_MAX || (uint64_t)n_rows * (uint64_t)nch * (uint64_t)nch >= (1ull << 32))
-    return fail(PALU_ERR_UNSUPPORTED, "too many rows for one call");
-  DequantParams dp;
-  memset(&dp, 0, sizeof(dp));
-  DequantSide& sd = dp.side[0];
-  sd.codes = (const uint8_t*)codes;
-  sd.scales = (const uint8_t*)scales;
-  sd.out = (uint8_t*)out;
-  sd.nch[0] = nch;
-  sd.rank[0] = r;
-  sd.magic[0] = (unsigned)(((1ull << 32) + (uint64_t)nch - 1) / (uint64_t)nch);
-  dp.seq_lens = nullptr;
-  dp.batch = 1; dp.G = 1; dp.max_len = (int)n_rows; dp.max_nch = nch; dp.n_sides = 1;
-  hipError_t e = launch_dequant(out_dtype == PALU_F16 ? 1 : 2, dp, stream);
-  if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
-  return ok();
-}
-
-}  // extern "C"
-
-namespace {
-
 // Latent storage one prefill writes (contiguous, or paged through a block table).
 struct WriteView {
   void* zk; void* zv; void* sk; void* sv;
@@ -362,41 +272,6 @@ palu_status check_paged(const palu_paged_cache* cache, int* shift) {
   *shift = sh;
   return PALU_OK;
 }
-
-}  // namespace
-
-extern "C" {
-
-palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
-                         const palu_latent_cache* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
-  if (!cache) return fail(PALU_ERR_INVALID_ARG, "null pointer");
-  const WriteView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
-  return project_impl(desc, x, d_model, n_tok, A_kv, &v, seq, pos0, stream);
-}
-
-palu_status palu_project_paged(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok,
-                               const void* A_kv, const palu_paged_cache* cache, int32_t seq, int32_t pos0,
-                               hipStream_t stream) {
-  if (!cache) return fail(PALU_ERR_INVALID_ARG, "null pointer");
-  int shift = 0;
-  palu_status s = check_paged(cache, &shift);
-  if (s != PALU_OK) return s;
-  if (n_tok > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
-  const WriteView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->page_size, cache->max_pages * cache->page_size,
-                    cache->block_table, shift, cache->max_pages};
-  return project_impl(desc, x, d_model, n_tok, A_kv, &v, seq, pos0, stream);
-}
-
-size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len) {
-  DecodePlan pl;
-  if (plan_decode(desc, batch, max_len, &pl) != PALU_OK) return 0;
-  return pl.total;
-}
-
-}  // extern "C"
-
-namespace {
-
 // The latent storage one decode call reads: a contiguous cache (rows per
 // block = history bound = max_len) or a paged one (rows per block = page
 // size; rows of sequence b found through the block table).
@@ -519,41 +394,6 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
 }
-
-}  // namespace
-
-extern "C" {
-
-palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
-                             const void* B_k, const void* B_v, const int32_t* seq_lens, const int32_t* q_pos,
-                             int32_t batch, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
-  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
-  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
-  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
-                     stream);
-}
-
-palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, const palu_paged_cache* cache,
-                                   const void* B_k, const void* B_v, const int32_t* seq_lens,
-                                   const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
-                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
-  int shift = 0;
-  palu_status s = check_paged(cache, &shift);
-  if (s != PALU_OK) return s;
-  if (batch > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
-  const int ps = cache->page_size;
-  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, ps, cache->max_pages * ps,
-                    cache->block_table, shift, cache->max_pages};
-  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
-                     stream);
-}
-
-}  // extern "C"
-
-namespace {
-
 // workspace of a chunk call: virtual lengths, positions and block-table rows,
 // then the decode workspace of the virtual batch
 size_t chunk_front_bytes(int64_t vbatch, int max_pages) {
@@ -588,6 +428,139 @@ palu_status chunk_impl(const palu_attn_desc* desc, const void* q, int32_t q_len,
 }  // namespace
 
 extern "C" {
+
+const char* palu_status_string(palu_status s) {
+  switch (s) {
+    case PALU_OK: return "PALU_OK";
+    case PALU_ERR_INVALID_ARG: return "PALU_ERR_INVALID_ARG";
+    case PALU_ERR_UNSUPPORTED: return "PALU_ERR_UNSUPPORTED";
+    case PALU_ERR_WORKSPACE_TOO_SMALL: return "PALU_ERR_WORKSPACE_TOO_SMALL";
+    case PALU_ERR_HIP: return "PALU_ERR_HIP";
+  }
+  return "PALU_ERR_UNKNOWN";
+}
+
+const char* palu_last_error(void) { return g_err; }
+
+palu_status palu_profile_events(hipEvent_t before_main, hipEvent_t after_main) {
+  g_prof_before = before_main;
+  g_prof_after = after_main;
+  return ok();
+}
+
+size_t palu_latent_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len, int32_t which,
+                         int32_t scales) {
+  if (check_desc(desc) != PALU_OK || batch < 0 || max_len <= 0 || (which != 0 && which != 1)) return 0;
+  if (scales && desc->latent_dtype != PALU_I4) return 0;
+  Layout L;
+  make_layout(desc, max_len, &L);
+  const int64_t per = scales ? (which ? L.seq_sv : L.seq_sk) : (which ? L.seq_v : L.seq_k);
+  return (size_t)(per * batch);
+}
+
+int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t which, int32_t scales, int32_t b,
+                           int32_t j, int32_t t) {
+  if (check_desc(desc) != PALU_OK || max_len <= 0 || (which != 0 && which != 1)) return -1;
+  if (b < 0 || j < 0 || j >= desc->n_groups || t < 0 || t >= max_len) return -1;
+  if (scales && desc->latent_dtype != PALU_I4) return -1;
+  Layout L;
+  make_layout(desc, max_len, &L);
+  if (scales)
+    return which ? b * L.seq_sv + L.soff_v[j] + t * L.spv[j] : b * L.seq_sk + L.soff_k[j] + t * L.spk[j];
+  return which ? b * L.seq_v + L.goff_v[j] + t * L.pv[j] : b * L.seq_k + L.goff_k[j] + t * L.pk[j];
+}
+
+palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r, int64_t z_row_stride,
+                              void* codes, void* scales, hipStream_t stream) {
+  if (n_rows < 0 || r <= 0 || z_row_stride < r) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r / z_row_stride");
+  if (z_dtype == PALU_I4) return fail(PALU_ERR_UNSUPPORTED, "input must be F32, F16 or BF16");
+  if (!valid_dtype(z_dtype)) return fail(PALU_ERR_INVALID_ARG, "invalid dtype");
+  if (n_rows == 0) return ok();
+  if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantiser launch");
+  return ok();
+}
+
+palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n_rows, int32_t r,
+                                palu_dtype out_dtype, void* out, hipStream_t stream) {
+  if (n_rows < 0 || r <= 0) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r");
+  if (out_dtype != PALU_F16 && out_dtype != PALU_BF16) return fail(PALU_ERR_UNSUPPORTED, "out_dtype must be F16 or BF16");
+  if (n_rows == 0) return ok();
+  if (!codes || !scales || !out) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (((uintptr_t)codes & 3u) != 0 || ((uintptr_t)scales & 1u) != 0 || !aligned16(out))
+    return fail(PALU_ERR_INVALID_ARG, "codes must be 4-byte, scales 2-byte and out 16-byte aligned");
+  const int nch = (r + 31) / 32;
+  if (n_rows > INT32_MAX || (uint64_t)n_rows * (uint64_t)nch * (uint64_t)nch >= (1ull << 32))
+    return fail(PALU_ERR_UNSUPPORTED, "too many rows for one call");
+  DequantParams dp;
+  memset(&dp, 0, sizeof(dp));
+  DequantSide& sd = dp.side[0];
+  sd.codes = (const uint8_t*)codes;
+  sd.scales = (const uint8_t*)scales;
+  sd.out = (uint8_t*)out;
+  sd.nch[0] = nch;
+  sd.rank[0] = r;
+  sd.magic[0] = (unsigned)(((1ull << 32) + (uint64_t)nch - 1) / (uint64_t)nch);
+  dp.seq_lens = nullptr;
+  dp.batch = 1; dp.G = 1; dp.max_len = (int)n_rows; dp.max_nch = nch; dp.n_sides = 1;
+  hipError_t e = launch_dequant(out_dtype == PALU_F16 ? 1 : 2, dp, stream);
+  if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
+  return ok();
+}
+
+palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok, const void* A_kv,
+                         const palu_latent_cache* cache, int32_t seq, int32_t pos0, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  const WriteView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
+  return project_impl(desc, x, d_model, n_tok, A_kv, &v, seq, pos0, stream);
+}
+
+palu_status palu_project_paged(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok,
+                               const void* A_kv, const palu_paged_cache* cache, int32_t seq, int32_t pos0,
+                               hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  int shift = 0;
+  palu_status s = check_paged(cache, &shift);
+  if (s != PALU_OK) return s;
+  if (n_tok > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
+  const WriteView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->page_size, cache->max_pages * cache->page_size,
+                    cache->block_table, shift, cache->max_pages};
+  return project_impl(desc, x, d_model, n_tok, A_kv, &v, seq, pos0, stream);
+}
+
+size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t max_len) {
+  DecodePlan pl;
+  if (plan_decode(desc, batch, max_len, &pl) != PALU_OK) return 0;
+  return pl.total;
+}
+
+palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
+                             const void* B_k, const void* B_v, const int32_t* seq_lens, const int32_t* q_pos,
+                             int32_t batch, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
+  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+palu_status palu_decode_attn_paged(const palu_attn_desc* desc, const void* q, const palu_paged_cache* cache,
+                                   const void* B_k, const void* B_v, const int32_t* seq_lens,
+                                   const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  int shift = 0;
+  palu_status s = check_paged(cache, &shift);
+  if (s != PALU_OK) return s;
+  if (batch > 0 && !cache->block_table) return fail(PALU_ERR_INVALID_ARG, "block_table is NULL");
+  const int ps = cache->page_size;
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, ps, cache->max_pages * ps,
+                    cache->block_table, shift, cache->max_pages};
+  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
+                     stream);
+}
 
 size_t palu_decode_chunk_workspace_bytes(const palu_attn_desc* desc, int32_t batch, int32_t q_len, int32_t max_len,
                                          int32_t max_pages) {

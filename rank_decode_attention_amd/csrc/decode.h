@@ -63,9 +63,9 @@ bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap);
 hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream,
                          hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_qabs(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
-// One-wave-per-kv-head kernel for MHA groups of 4 kv heads (head_dim 128,
-// ranks <= 256 and multiples of 32, 16-bit, RoPE); launch_decode uses it
-// where it applies.
+// Eight-wave kernel for MHA head-groups of 4 kv heads (head_dim 128, ranks
+// <= 256, 16-bit or int4 latents, RoPE; contiguous or paged caches);
+// launch_decode uses it where it applies.
 bool mha_supported(const DecodeKey& k, const DecodeParams& p);
 hipError_t launch_decode_mha(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
                              hipEvent_t t1);
