@@ -142,3 +142,20 @@ def test_full_size_sampled(name, heads):
     stats = compare(gpu[bs, hs], ref[bs, hs], wl.act, name)
     assert np.all(np.isfinite(gpu))
     print(name, stats)
+
+
+def test_maximum_batch_and_groups():
+    """The largest batch the library takes (2048 sequences, short ragged
+    histories) and the largest group count (16 groups of 2 kv heads)."""
+    wl = PI.scaled("tiny", name="tiny_b2048", batch=2048, max_len=64, ragged=True)
+    case = build_decode_case(wl)
+    gpu = run_decode(case)
+    seqs = [0, 1, 1023, 2046, 2047]
+    heads = [(b, h) for b in seqs for h in (0, 7)]
+    ref = oracle_decode(case, heads=heads)
+    bs, hs = [b for b, _ in heads], [h for _, h in heads]
+    compare(gpu[bs, hs], ref[bs, hs], wl.act, "batch 2048")
+    wl = PI.scaled("gqa_rope", name="gqa_g16", n_q_heads=128, n_kv_heads=32, n_groups=16, batch=2, max_len=100,
+                   fixed_lengths=(100, 37), rank_choices=(64, 128))
+    case = build_decode_case(wl)
+    compare(run_decode(case), oracle_decode(case), wl.act, "16 groups")
