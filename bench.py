@@ -191,7 +191,9 @@ def main_kernel_name(wl) -> str:
     """Name of the decode kernel the library runs for a workload: the fused
     MHA-group kernel where it applies (16-bit latents, head_dim 128, groups of
     4 kv heads with one query head each, RoPE, ranks multiples of 32 up to 256),
-    the general split-attention kernel otherwise."""
+    the absorbed-query kernel without RoPE (16-bit latents, at most 8 query
+    heads per group, ranks up to 320), the general split-attention kernel
+    otherwise."""
     import palu_inputs as PI
     r = PI.ranks(wl)
     q4 = wl.latent == "i4"
@@ -201,6 +203,11 @@ def main_kernel_name(wl) -> str:
     if mha:
         # (int4 codes are expanded into the kernel's LDS tiles)
         return "palu_decode_mha_kernel (fused, MHA head-groups" + (", int4 codes)" if q4 else ")")
+    nq = wl.n_q_heads // wl.n_groups
+    if (not wl.use_rope and wl.latent in ("f16", "bf16", "i4") and nq <= 8
+            and all(int(x) <= 320 for x in r)):
+        # (int4 caches are first expanded to 16-bit rows of the rank rounded up to 32)
+        return ("palu_dequant_kernel, then " if q4 else "") + "palu_decode_abs_kernel (absorbed query)"
     # (int4 caches are first expanded to 16-bit rows of the rank rounded up to 32)
     return ("palu_dequant_kernel, then " if q4 else "") + "palu_decode_kernel (split attention)"
 

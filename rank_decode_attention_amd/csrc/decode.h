@@ -69,6 +69,12 @@ hipError_t launch_qabs(const DecodeKey& k, const DecodeParams& p, hipStream_t st
 bool mha_supported(const DecodeKey& k, const DecodeParams& p);
 hipError_t launch_decode_mha(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
                              hipEvent_t t1);
+// Eight-wave kernel for 16-bit latents without RoPE (absorbed query against
+// the latent rows; at most 8 query heads per group, ranks <= 320);
+// launch_decode uses it where it applies.
+bool abs_supported(const DecodeKey& k, const DecodeParams& p);
+hipError_t launch_decode_abs(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
+                             hipEvent_t t1);
 hipError_t launch_merge(const DecodeKey& k, const DecodeParams& p, hipStream_t stream);
 // Virtual sequences of a multi-query chunk (see decode.hip): lengths, query
 // positions and block-table rows (block_table NULL: row b is block b).

@@ -1006,6 +1006,7 @@ hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t 
   const Entry* e = find_entry(k);
   if (!e) return hipErrorInvalidValue;
   if (mha_supported(k, p)) return launch_decode_mha(k, p, stream, t0, t1);
+  if (abs_supported(k, p)) return launch_decode_abs(k, p, stream, t0, t1);
   return e->decode(p, stream, t0, t1);
 }
 
