@@ -121,6 +121,7 @@ palu_status device_cus(int* out) {
 struct DecodePlan {
   DecodeKey key;
   int P, rvp, qabs_stride, nq;
+  int Pg[kMaxGroups], gblk[kMaxGroups];   // blocks of each group and the first block id of its range
   size_t hdr_bytes, rec_bytes, qabs_bytes, total;
   // int4 latents: the decode runs on a 16-bit copy of the cache in the
   // workspace (ranks rounded up to 32, rows zero-padded), expanded first
@@ -131,6 +132,9 @@ struct DecodePlan {
 };
 
 Elt elt_of(palu_dtype d) { return d == PALU_F32 ? Elt::F32 : d == PALU_F16 ? Elt::F16 : Elt::BF16; }
+
+// fixed time per tile of the absorbed-query kernel, in ranks of row bytes
+constexpr int kAbsTileRanks = 1024;
 
 palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodePlan* pl) {
   palu_status s = check_desc(d);
@@ -166,10 +170,57 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   int64_t P = (cus + d->n_groups - 1) / d->n_groups;
   if (P > tiles_bound) P = tiles_bound;
   if (P < 1) P = 1;
-  pl->P = (int)P;
   pl->nq = ng * qpk;
   pl->rvp = (int)roundup(rv_cap, 16);
   pl->qabs_stride = (int)roundup(rk_cap, 4);
+  for (int j = 0; j < d->n_groups; ++j) pl->Pg[j] = (int)P;
+  if (!d->use_rope) {
+    // The absorbed-query kernel's time per 32-token tile is a fixed part plus
+    // a part proportional to the row bytes: on MI355X about 0.85 us + 0.83 ns
+    // per rank of r_k + r_v, i.e. the fixed part weighs as much as 1024 ranks
+    // (GQA 8B shape: 1.38 us per tile at r_k + r_v = 640, 1.06 us at 256).
+    // The same total of blocks goes to the groups in proportion to
+    // r_k + r_v + 1024, so that groups of mixed ranks end together.
+    DecodeParams t;
+    memset(&t, 0, sizeof(t));
+    t.G = d->n_groups;
+    t.qabs_stride = pl->qabs_stride;
+    for (int j = 0; j < d->n_groups; ++j) {
+      t.rk[j] = dense_rank(d->rank_k[j]);
+      t.rv[j] = dense_rank(d->rank_v[j]);
+      t.pk[j] = pl->q4 ? 2 * t.rk[j] : (int)row_pitch(d->latent_dtype, d->rank_k[j]);
+      t.pv[j] = pl->q4 ? 2 * t.rv[j] : (int)row_pitch(d->latent_dtype, d->rank_v[j]);
+    }
+    if (abs_supported(pl->key, t)) {
+      int64_t wsum = 0;
+      for (int j = 0; j < d->n_groups; ++j) wsum += t.rk[j] + t.rv[j] + kAbsTileRanks;
+      const int64_t tot = P * d->n_groups;
+      double frac[kMaxGroups];
+      int64_t given = 0;
+      for (int j = 0; j < d->n_groups; ++j) {
+        const double share = (double)tot * (double)(t.rk[j] + t.rv[j] + kAbsTileRanks) / (double)wsum;
+        int64_t n = (int64_t)share;
+        n = n < 1 ? 1 : n;
+        pl->Pg[j] = (int)n;
+        frac[j] = share - (double)n;
+        given += n;
+      }
+      for (; given < tot; ++given) {   // the remaining blocks by largest remainder
+        int best = 0;
+        for (int j = 1; j < d->n_groups; ++j) best = frac[j] > frac[best] ? j : best;
+        ++pl->Pg[best];
+        frac[best] -= 1.0;
+      }
+      P = 1;
+      for (int j = 0; j < d->n_groups; ++j) {
+        if (pl->Pg[j] > tiles_bound) pl->Pg[j] = (int)(tiles_bound > 1 ? tiles_bound : 1);
+        P = pl->Pg[j] > P ? pl->Pg[j] : P;
+      }
+    }
+  }
+  pl->gblk[0] = 0;
+  for (int j = 1; j < d->n_groups; ++j) pl->gblk[j] = pl->gblk[j - 1] + pl->Pg[j - 1];
+  pl->P = (int)P;
   pl->hdr_bytes = (size_t)roundup((int64_t)(batch + 1) * 4, 256);
   pl->rec_bytes = (size_t)roundup((int64_t)d->n_groups * (P + batch) * pl->nq * (2 + pl->rvp) * 4, 256);
   pl->qabs_bytes = d->use_rope ? 0 : (size_t)roundup((int64_t)batch * d->n_q_heads * pl->qabs_stride * 4, 256);
@@ -351,6 +402,10 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
   p.qabs = desc->use_rope ? nullptr : (const float*)(ws + pl.hdr_bytes + pl.rec_bytes);
   p.out = out;
   p.batch = batch; p.max_len = cache->max_len; p.H = desc->n_q_heads; p.G = desc->n_groups; p.P = pl.P;
+  for (int j = 0; j < desc->n_groups; ++j) {
+    p.Pg[j] = pl.Pg[j];
+    p.gblk[j] = pl.gblk[j];
+  }
   p.block_table = cache->block_table; p.page_shift = cache->page_shift; p.max_pages = cache->max_pages;
   p.rvp = pl.rvp; p.rec_stride = pl.nq * (2 + pl.rvp); p.qabs_stride = pl.qabs_stride;
   p.qscale = sm_scale * 1.4426950408889634f;

@@ -25,7 +25,12 @@ struct DecodeParams {
   int* hdr;                 // workspace: tile_start[batch + 1]
   float* rec;               // workspace: split records
   void* out;                // [batch][H][DH]
-  int batch, max_len, H, G, P;
+  int batch, max_len, H, G;
+  int P;                    // blocks per group (the largest Pg: split records are [G][P + batch])
+  // blocks of group g and the first block id of its range (the absorbed-query
+  // kernel weights them by the group's row bytes; the other kernels use P
+  // blocks per group, block id = p * G + g)
+  int Pg[kMaxGroups], gblk[kMaxGroups];
   int rec_stride;           // floats per record = NQ * (2 + rvp)
   int rvp;                  // record row length (max value rank rounded up to 16)
   int qabs_stride;

@@ -808,7 +808,7 @@ __global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeP
 
   // per-row record weights: 16 lanes per row
   const int total = p.hdr[p.batch];
-  const int tpb = cdiv(total, p.P);
+  const int tpb = cdiv(total, p.Pg[g]);
   if (tid == 0) maxrec = 0;
   __syncthreads();
   {

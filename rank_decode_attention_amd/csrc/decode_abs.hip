@@ -11,8 +11,10 @@
 //
 // Design (ours):
 //  * Block = 8 waves; block (g, p) takes the p-th equal share of the 32-token
-//    tiles of group g (the work split of palu_decode_kernel, same split
-//    records), with one barrier per tile.
+//    tiles of group g (the split records of palu_decode_kernel), with one
+//    barrier per tile.  Each group's blocks form one range of block ids, as
+//    many as the host gives it (in proportion to its time per tile, so that
+//    groups of mixed ranks end together).
 //  * Key and value rows of a tile stream HBM -> LDS through LDS DMA into a
 //    ring of three buffers, two tiles ahead.  Rows are padded (key rows 4
 //    banks apart, value rows 8) so that the MFMA operand reads and the
@@ -110,7 +112,11 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = l & 15, q = l >> 4;
-  const int g = blockIdx.x % p.G, pb = blockIdx.x / p.G;
+  // block -> (group g, share pb): each group's blocks form one range of
+  // block ids, as many as its share of the latent bytes
+  int g = 0;
+  for (int j = 1; j < p.G; ++j) g = (int)blockIdx.x >= p.gblk[j] ? j : g;
+  const int Pg = p.Pg[g], pb = (int)blockIdx.x - p.gblk[g];
   const int batch = p.batch;
 
   // ---------------------------------------------------------------- tile prefix sums
@@ -148,7 +154,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
       before += i < w ? wsum[i] : 0;
     }
     total = all;
-    const int nb0 = pb * cdiv(total, p.P);
+    const int nb0 = pb * cdiv(total, Pg);
     int run = before + incl - sacc;
     const bool hdr = (g == 0 && pb == 0);
 #pragma unroll
@@ -166,7 +172,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
     if (hdr && tid == C::NT - 1) p.hdr[batch] = total;
     __syncthreads();
   }
-  const int tpb = cdiv(total, p.P);
+  const int tpb = cdiv(total, Pg);
   const int n_begin = pb * tpb;
   const int n_end = min(total, n_begin + tpb);
   if (n_begin >= n_end) return;
@@ -468,7 +474,7 @@ bool abs_supported(const DecodeKey& k, const DecodeParams& p) {
 
 template <class LT, int RCAP, bool PAGED>
 static void launch_abs_t(const DecodeParams& p, int nq, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const dim3 grid(p.G * p.P), block(512);
+  const dim3 grid(p.gblk[p.G - 1] + p.Pg[p.G - 1]), block(512);
   if (t0 && t1)
     hipExtLaunchKernelGGL((palu_decode_abs_kernel<LT, RCAP, PAGED>), grid, block, 0, stream, t0, t1, 0, p, nq);
   else
