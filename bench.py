@@ -105,9 +105,15 @@ def setup(wl, page_size: int = 0):
         latent_bytes = int(sum(int(lens[b]) for b in range(wl.batch)) * row_bytes)
     else:
         latent_bytes = int(sum(int(lens[b]) * int(ranks.sum()) * 2 * esz for b in range(wl.batch)))
-    recon_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * sum(
-        2 * int(r) * wl.group_width for r in ranks)
-    pv_flops = int(sum(int(lens[b]) for b in range(wl.batch))) * wl.n_q_heads * 2 * int(ranks.max())
+    n_lat = int(sum(int(lens[b]) for b in range(wl.batch)))
+    nq = wl.n_q_heads // wl.n_groups
+    # score side: the key rebuild with RoPE, the absorbed query against the
+    # latent rows without; value side: P z_v of every query head
+    if wl.use_rope:
+        recon_flops = n_lat * sum(2 * int(r) * wl.group_width for r in ranks)
+    else:
+        recon_flops = n_lat * sum(2 * int(r) * nq for r in ranks)
+    pv_flops = n_lat * sum(2 * int(r) * nq for r in ranks)
     return dict(desc=desc, cache=cache, paged=bool(page_size), Bk=Bk, Bv=Bv, q=q, seq_lens=seq_lens, ws=ws, out=out,
                 sm_scale=1.0 / math.sqrt(wl.head_dim), latent_bytes=latent_bytes,
                 flops=recon_flops + pv_flops, lens=lens)
