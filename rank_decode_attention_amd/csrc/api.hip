@@ -133,8 +133,11 @@ struct DecodePlan {
 
 Elt elt_of(palu_dtype d) { return d == PALU_F32 ? Elt::F32 : d == PALU_F16 ? Elt::F16 : Elt::BF16; }
 
-// fixed time per tile of the absorbed-query kernel, in ranks of row bytes
-constexpr int kAbsTileRanks = 1024;
+// Fixed time per tile of the absorbed-query kernel, in ranks of row bytes.
+// Measured on MI355X at the GQA 8B shape (ranks 320/192/192/128): 0 (byte
+// weighting) 235 us, 256: 166 us, 384: 164 us, 512: 167 us, 1024: 174 us,
+// uniform split 177 us.
+constexpr int kAbsTileRanks = 384;
 
 palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodePlan* pl) {
   palu_status s = check_desc(d);
@@ -176,11 +179,9 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   for (int j = 0; j < d->n_groups; ++j) pl->Pg[j] = (int)P;
   if (!d->use_rope) {
     // The absorbed-query kernel's time per 32-token tile is a fixed part plus
-    // a part proportional to the row bytes: on MI355X about 0.85 us + 0.83 ns
-    // per rank of r_k + r_v, i.e. the fixed part weighs as much as 1024 ranks
-    // (GQA 8B shape: 1.38 us per tile at r_k + r_v = 640, 1.06 us at 256).
-    // The same total of blocks goes to the groups in proportion to
-    // r_k + r_v + 1024, so that groups of mixed ranks end together.
+    // a part that grows with the row bytes, so the same total of blocks goes
+    // to the groups in proportion to r_k + r_v + kAbsTileRanks, and groups of
+    // mixed ranks end together.
     DecodeParams t;
     memset(&t, 0, sizeof(t));
     t.G = d->n_groups;

@@ -34,6 +34,7 @@
 #include "decode.h"
 
 #include <hip/hip_ext.h>
+#include <type_traits>
 
 namespace palu {
 namespace {
@@ -57,7 +58,7 @@ struct AbsCfg {
   static constexpr int BUFB = (SLK + SLV + PADS) * 16;
   static constexpr int NNT4 = cdiv(RCAP / 16, 4);       // value n-tiles per wave (four waves per half)
   static constexpr int XB = 4 * NNT4 * 64 * 16 + 4 * 2 * 16 * 4;   // segment-end exchange
-  static_assert(RCAP % 32 == 0, "rank capacity");
+  static_assert(RCAP % 64 == 0, "rank capacity");
   static_assert(NB * BUFB + XB + 64 <= 160 * 1024, "LDS");
 };
 
@@ -88,6 +89,18 @@ __device__ __forceinline__ void dma16o(const void* base, unsigned voff, unsigned
                :
                : "s"(lds), "v"(voff), "s"(sb)
                : "memory", "m0");
+}
+
+// f(integral_constant<N>) for the smallest N in [N0, MAX] with n <= N (MAX if
+// none): a wave-uniform choice between fully unrolled, branch-free bodies.
+template <int N0, int MAX, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N0 >= MAX) {
+    f(std::integral_constant<int, MAX>{});
+  } else {
+    if (n <= N0) f(std::integral_constant<int, N0>{});
+    else with_count<N0 + 1, MAX>(n, f);
+  }
 }
 
 // x + the value of lane (l + 8) mod 16 of the same 16-lane row (DPP row_ror:8)
@@ -178,6 +191,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
   if (n_begin >= n_end) return;
 
   const int rv = p.rv[g];
+  const int nkc = cdiv(p.rk[g], 32);              // 32-deep chunks of the group's keys
   const int pk = p.pk[g], pv = p.pv[g];
   const int cprk = pk >> 4, cprv = pv >> 4;
   const int nnt = cdiv(rv, 16);
@@ -376,6 +390,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
     if (n_begin + 2 < n_end) advance(cd);
   }
 
+  // The tile loop is instantiated per chunk count NK (the group's 32-deep
+  // key chunks, rounded up to even), chosen once per block: inside, every
+  // loop is fully unrolled and branch-free (a runtime bound inside the loop
+  // puts each operand read and its MFMA in a block of its own).  NR = the
+  // value n-tile rounds of a wave at capacity (rounds past the rank repeat
+  // the last n-tile and are never recorded).
+  auto tile_loop = [&](auto nk_t, auto nr_t) __attribute__((always_inline)) {
+  constexpr int NK = decltype(nk_t)::value, NR = decltype(nr_t)::value;
   for (int n = n_begin; n < n_end; ++n) {
     if (n + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
     barrier();   // tile n landed for every wave; tile n - 1's buffer is free
@@ -393,14 +415,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
     const uint8_t* zvt = zkt + C::SLK * 16;
 
     // ---- scores of this wave's 16 tokens: D[token 16 u + 4 q + i][head
-    // row s], two accumulators (even and odd chunks).  Every chunk up to the
-    // capacity runs (branch-free, so the operand reads go out ahead of the
-    // MFMAs): past a group's rank the query is zero and the LDS slots hold
-    // finite copies of real chunks.
+    // row s], two accumulators (even and odd chunks).  The group's chunk
+    // count picks one fully unrolled loop (branch-free inside, so the operand
+    // reads go out ahead of the MFMAs); past the rank inside the last chunk
+    // the query is zero.
     f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint8_t* arow = zkt + ((16 * u + s) * C::PITK + q) * 16;
 #pragma unroll
-    for (int kc = 0; kc < C::NKC; ++kc) {
+    for (int kc = 0; kc < NK; ++kc) {
       if (kc & 1) sc1 = mfma16x16x32(*(const op_t*)(arow + 64 * kc), aq[kc], sc1);
       else sc0 = mfma16x16x32(*(const op_t*)(arow + 64 * kc), aq[kc], sc0);
     }
@@ -445,11 +467,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
     const op4_t pa = __builtin_bit_cast(op4_t, pl);
 
     // ---- acc += P z_v over the wave's 16 tokens: B[k = 4 q + j][rank
-    // 16 nt + s] = z_v[16 u + 4 q + j] (one transposed read).  Branch-free:
-    // n-tiles past the capacity repeat the last one, and n-tiles past the
-    // rank are never recorded.
+    // 16 nt + s] = z_v[16 u + 4 q + j] (one transposed read), for the wave's
+    // n-tiles grp + 4 i below the group's rank (one unrolled loop per count)
 #pragma unroll
-    for (int i = 0; i < C::NNT4; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const int nt = min(grp + 4 * i, C::RCAP / 16 - 1);
       const int row = 16 * u + 4 * q + (s >> 2);
       const i16x4 vb = ds_read_tr16(zvt + row * C::PITV * 16 + (16 * nt + 4 * (s & 3)) * 2);
@@ -460,6 +481,11 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
     i_c = i_a;
     i_a = i_d;
   }
+  };
+  // (chunk counts rounded up to even: the extra chunk meets a zero query)
+  with_count<1, C::NKC / 2>(cdiv(nkc, 2), [&](auto nk2_t) __attribute__((always_inline)) {
+    tile_loop(std::integral_constant<int, 2 * decltype(nk2_t)::value>{}, std::integral_constant<int, C::NNT4>{});
+  });
 }
 
 bool abs_supported(const DecodeKey& k, const DecodeParams& p) {
