@@ -46,6 +46,15 @@ SMALL = [
                               fixed_lengths=(200, 45)), None),
     ("int4_mixed_ranks", _small("int4", rank=None, rank_choices=(70, 154, 200), batch=2, max_len=260,
                                 fixed_lengths=(260, 31)), None),
+    # absorbed-query kernel (no RoPE, 16-bit): histories of at most 16 tokens
+    # leave the second token half of every tile masked (its stream never sees
+    # a token), an empty sequence, tile boundaries, odd ranks (chunk counts
+    # rounded up to even), and capacity 256 with ranks below it
+    ("gqa_norope_short", _small("gqa_norope", batch=6, max_len=70, fixed_lengths=(1, 16, 0, 17, 33, 70)), None),
+    ("gqa_norope_odd_ranks", _small("gqa_norope", rank=None, rank_choices=(90, 150, 200, 300), batch=3,
+                                    max_len=150, fixed_lengths=(150, 9, 64)), None),
+    ("7b_norope_short", _small("llama2_7b", use_rope=False, rank=None, rank_choices=(64, 96, 256), batch=4,
+                               max_len=100, fixed_lengths=(16, 100, 1, 48)), None),
 ]
 
 
