@@ -46,8 +46,8 @@ def _hipcc() -> str:
 
 # per-file code-generation options
 FILE_FLAGS = {
-    # MFMA accumulators in VGPRs: the one-wave-per-kv-head kernel keeps its
-    # B_k^T operands (256 registers) in the AGPR file
+    # MFMA accumulators in VGPRs: the MHA head-group kernel keeps its B_k^T
+    # operands (128 registers per lane) in the AGPR file
     "decode_mha.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
