@@ -235,7 +235,9 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  * I4 latents (act_dtype F16 or BF16): the decode consumes the
  * dequantised latent code * scale (PALU page, section "Rollout", route C:
  * quantization on top of the low-rank cache), formed exactly in binary32 and
- * rounded to nearest even into act_dtype; the rows [0, L_b) of every
+ * rounded to nearest even into act_dtype.  On MHA head-group shapes (4 kv
+ * heads per group, one query head each, head_dim 128, RoPE) the decode kernel
+ * expands the int4 tiles on chip; on other shapes the rows [0, L_b) of every
  * sequence are first expanded into the workspace (16-bit rows of the rank
  * rounded up to 32, zero past the rank), then attended as above.
  *   q          device [batch][H][d_h] act_dtype
@@ -249,8 +251,9 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  *   out        device [batch][H][d_h] act_dtype
  *   workspace  device, at least palu_decode_workspace_bytes(desc, batch,
  *              cache->max_len) bytes, 256-byte aligned; contents are scratch
- *              (for I4 it includes batch * max_len * sum_j 2 * (ceil32(r_k^j)
- *              + ceil32(r_v^j)) bytes of expanded latents)
+ *              (for I4 on shapes expanded into the workspace it includes
+ *              batch * max_len * sum_j 2 * (ceil32(r_k^j) + ceil32(r_v^j))
+ *              bytes of expanded latents)
  * batch == 0 is a no-op after the descriptor checks (pointers may be NULL).
  * Errors: INVALID_ARG for null pointers, batch < 0, head counts that do not
  * divide, odd head_dim, rank <= 0, max_len <= 0, non-finite sm_scale,
@@ -314,7 +317,8 @@ size_t palu_decode_chunk_workspace_bytes(const palu_attn_desc* desc, int32_t bat
 /*
  * palu_profile_events - timing hook for benchmark harnesses (not part of the
  * method).  When both are set (non-NULL), every later palu_decode_attn call
- * on the calling thread launches its main split-attention kernel with
+ * on the calling thread launches its main decode kernel (the one that reads
+ * the latent cache, before the merge) with
  * hipExtLaunchKernel, which stamps `before_main` at the kernel's start and
  * `after_main` at its end, so that hipEventElapsedTime gives that kernel's
  * duration.  The caller owns the events (hipEventCreate) and must keep them
