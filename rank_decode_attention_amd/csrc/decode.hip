@@ -123,6 +123,8 @@ struct DecState {
   op_t breg[C::ROPE ? C::RT : 1][C::ROPE ? C::NKC : 1];   // B_k^T operand (RoPE path)
   op_t aq[C::ROPE ? 1 : C::NKC];                          // absorbed query operand (no-RoPE path)
   float cs[4], sn[4];                                     // angle at the current tile (u = 0)
+  // rotated, pre-scaled query of the lane's rows (one kv head per wave)
+  f32x4 qr[C::ROPE && C::PPW * C::QPK <= 4 ? C::PPW * C::QPK * 2 : 1];
   f32x4 acc[C::NNTW];                                     // P z_v accumulators
   float m_run, l_run;
   int L;                                                  // history length of the current sequence
@@ -409,8 +411,24 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
         float qc[4], qs[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sincos_angle((double)pos, rope_theta(16 * jf + 4 * (l >> 4) + e), &qc[e], &qs[e]);
-        // lanes of one row group share their frequency rows: lane 16*kq writes them
-        if ((l & 15) == 0) {
+        if constexpr (C::PPW * C::QPK <= 4) {
+          // every lane keeps its rows' rotated query in registers for the segment
+#pragma unroll
+          for (int x = 0; x < C::PPW; ++x)
+#pragma unroll
+            for (int qq = 0; qq < C::QPK; ++qq) {
+              const int h = (g * C::NG + cbase + x) * C::QPK + qq;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int f = 16 * jf + 4 * (l >> 4) + e;
+                float qlo = to_f32(qb[h * C::DH + f]);
+                float qhi = to_f32(qb[h * C::DH + f + C::DH / 2]);
+                st.qr[(x * C::QPK + qq) * 2][e] = (qlo * qc[e] - qhi * qs[e]) * p.qscale;
+                st.qr[(x * C::QPK + qq) * 2 + 1][e] = (qlo * qs[e] + qhi * qc[e]) * p.qscale;
+              }
+            }
+        } else if ((l & 15) == 0) {
+          // lanes of one row group share their frequency rows: lane 16*kq writes them
 #pragma unroll
           for (int x = 0; x < C::PPW; ++x)
 #pragma unroll
@@ -515,8 +533,15 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
           }
 #pragma unroll
           for (int qq = 0; qq < C::QPK; ++qq) {
-            const f32x4* qt = qtab + ((w * 4 + kq) * C::PPW * C::QPK + x * C::QPK + qq) * 2;
-            const f32x4 qlo = qt[0], qhi = qt[1];
+            f32x4 qlo, qhi;
+            if constexpr (C::PPW * C::QPK <= 4) {
+              qlo = st.qr[(x * C::QPK + qq) * 2];
+              qhi = st.qr[(x * C::QPK + qq) * 2 + 1];
+            } else {
+              const f32x4* qt = qtab + ((w * 4 + kq) * C::PPW * C::QPK + x * C::QPK + qq) * 2;
+              qlo = qt[0];
+              qhi = qt[1];
+            }
             float part = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
