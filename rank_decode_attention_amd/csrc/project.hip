@@ -109,22 +109,24 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
         // 16-bit: chunk 4*kc + kq holds k = 32 kc + 8 kq .. +7; fp32: 4 floats
         xa[a] = *(const op_t*)(buf + row * C::PIT + 4 * kc + kq);
       }
+      // Every n-tile runs (branch-free, so the operand reads go out ahead of
+      // the MFMAs; a runtime bound here puts each read and its MFMAs in a
+      // basic block of its own): rows of A^T past the valid channels are
+      // copies of the last valid row in LDS, and their columns are not stored.
 #pragma unroll
       for (int b = 0; b < C::NTL; ++b) {
-        if (b < ntl) {
-          const op_t bv = *(const op_t*)(buf + C::SX + (16 * b + rr) * C::PIT + 4 * kc + kq);
+        const op_t bv = *(const op_t*)(buf + C::SX + (16 * b + rr) * C::PIT + 4 * kc + kq);
 #pragma unroll
-          for (int a = 0; a < C::MT; ++a) {
-            if constexpr (C::F32) {
-              f32x4 c = acc[a][b];
-              c = mfma16x16x4(xa[a][0], bv[0], c);
-              c = mfma16x16x4(xa[a][1], bv[1], c);
-              c = mfma16x16x4(xa[a][2], bv[2], c);
-              c = mfma16x16x4(xa[a][3], bv[3], c);
-              acc[a][b] = c;
-            } else {
-              acc[a][b] = mfma16x16x32(xa[a], bv, acc[a][b]);
-            }
+        for (int a = 0; a < C::MT; ++a) {
+          if constexpr (C::F32) {
+            f32x4 c = acc[a][b];
+            c = mfma16x16x4(xa[a][0], bv[0], c);
+            c = mfma16x16x4(xa[a][1], bv[1], c);
+            c = mfma16x16x4(xa[a][2], bv[2], c);
+            c = mfma16x16x4(xa[a][3], bv[3], c);
+            acc[a][b] = c;
+          } else {
+            acc[a][b] = mfma16x16x32(xa[a], bv, acc[a][b]);
           }
         }
       }
