@@ -397,90 +397,90 @@ __global__ void __launch_bounds__(512, 1) palu_decode_abs_kernel(const DecodePar
   // value n-tile rounds of a wave at capacity (rounds past the rank repeat
   // the last n-tile and are never recorded).
   auto tile_loop = [&](auto nk_t, auto nr_t) __attribute__((always_inline)) {
-  constexpr int NK = decltype(nk_t)::value, NR = decltype(nr_t)::value;
-  for (int n = n_begin; n < n_end; ++n) {
-    if (n + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
-    barrier();   // tile n landed for every wave; tile n - 1's buffer is free
-    int i_d = 0;
-    if (n + 2 < n_end) {
-      i_d = info_of(cd);
-      issue(cd, n + 2);
-      if (n + 3 < n_end) advance(cd);
-    }
-    // a segment's first tile: its absorbed query (loaded after this step's
-    // DMA went out)
-    if (i_c & F_START) load_query(i_c & 0xFFFF);
-
-    const uint8_t* zkt = (const uint8_t*)&ring[n % C::NB][0];
-    const uint8_t* zvt = zkt + C::SLK * 16;
-
-    // ---- scores of this wave's 16 tokens: D[token 16 u + 4 q + i][head
-    // row s], two accumulators (even and odd chunks).  The group's chunk
-    // count picks one fully unrolled loop (branch-free inside, so the operand
-    // reads go out ahead of the MFMAs); past the rank inside the last chunk
-    // the query is zero.
-    f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* arow = zkt + ((16 * u + s) * C::PITK + q) * 16;
-#pragma unroll
-    for (int kc = 0; kc < NK; ++kc) {
-      if (kc & 1) sc1 = mfma16x16x32(*(const op_t*)(arow + 64 * kc), aq[kc], sc1);
-      else sc0 = mfma16x16x32(*(const op_t*)(arow + 64 * kc), aq[kc], sc0);
-    }
-    // hi + lo rows (lanes s and s ^ 8 of a row hold the same sum); tokens
-    // past the history masked
-    float x[4];
-    const int nv = (i_c >> 16) & 63;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = add_ror8(sc0[i] + sc1[i]);
-    if (nv < C::TT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = 16 * u + 4 * q + i < nv ? x[i] : -INFINITY;
-    }
-
-    // ---- online softmax (lazy maximum)
-    bool up = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) up |= x[i] > m_run + kAbsTau;
-    if (__builtin_amdgcn_ballot_w64(up)) {
-      const float tmax = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-      const float mnew = tmax > m_run + kAbsTau ? tmax : m_run;
-      // (alpha is exactly 1 for a head whose maximum stays)
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-      m_run = mnew;
-      l_lane *= alpha;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ae = shfl(alpha, 4 * q + e);   // accumulator row 4 q + e
-#pragma unroll
-        for (int i = 0; i < C::NNT4; ++i) acc[i][e] *= ae;
+    constexpr int NK = decltype(nk_t)::value, NR = decltype(nr_t)::value;
+    for (int n = n_begin; n < n_end; ++n) {
+      if (n + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
+      barrier();   // tile n landed for every wave; tile n - 1's buffer is free
+      int i_d = 0;
+      if (n + 2 < n_end) {
+        i_d = info_of(cd);
+        issue(cd, n + 2);
+        if (n + 3 < n_end) advance(cd);
       }
-    }
-    lt4_t pl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pj = __builtin_amdgcn_exp2f(x[i] - m_run);
-      l_lane += pj;
-      const LT hi = (LT)pj;
-      const LT lo = (LT)(pj - (float)hi);
-      pl[i] = s < 8 ? hi : lo;
-    }
-    const op4_t pa = __builtin_bit_cast(op4_t, pl);
+      // a segment's first tile: its absorbed query (loaded after this step's
+      // DMA went out)
+      if (i_c & F_START) load_query(i_c & 0xFFFF);
 
-    // ---- acc += P z_v over the wave's 16 tokens: B[k = 4 q + j][rank
-    // 16 nt + s] = z_v[16 u + 4 q + j] (one transposed read), for the wave's
-    // n-tiles grp + 4 i below the group's rank (one unrolled loop per count)
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int nt = min(grp + 4 * i, C::RCAP / 16 - 1);
-      const int row = 16 * u + 4 * q + (s >> 2);
-      const i16x4 vb = ds_read_tr16(zvt + row * C::PITV * 16 + (16 * nt + 4 * (s & 3)) * 2);
-      acc[i] = mfma16x16x16(pa, __builtin_bit_cast(op4_t, vb), acc[i]);
-    }
+      const uint8_t* zkt = (const uint8_t*)&ring[n % C::NB][0];
+      const uint8_t* zvt = zkt + C::SLK * 16;
 
-    if ((i_c & F_END) || n + 1 == n_end) record(i_c);
-    i_c = i_a;
-    i_a = i_d;
-  }
+      // ---- scores of this wave's 16 tokens: D[token 16 u + 4 q + i][head
+      // row s], two accumulators (even and odd chunks).  The group's chunk
+      // count picks one fully unrolled loop (branch-free inside, so the operand
+      // reads go out ahead of the MFMAs); past the rank inside the last chunk
+      // the query is zero.
+      f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* arow = zkt + ((16 * u + s) * C::PITK + q) * 16;
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) {
+        if (kc & 1) sc1 = mfma16x16x32(*(const op_t*)(arow + 64 * kc), aq[kc], sc1);
+        else sc0 = mfma16x16x32(*(const op_t*)(arow + 64 * kc), aq[kc], sc0);
+      }
+      // hi + lo rows (lanes s and s ^ 8 of a row hold the same sum); tokens
+      // past the history masked
+      float x[4];
+      const int nv = (i_c >> 16) & 63;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = add_ror8(sc0[i] + sc1[i]);
+      if (nv < C::TT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = 16 * u + 4 * q + i < nv ? x[i] : -INFINITY;
+      }
+
+      // ---- online softmax (lazy maximum)
+      bool up = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up |= x[i] > m_run + kAbsTau;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float tmax = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float mnew = tmax > m_run + kAbsTau ? tmax : m_run;
+        // (alpha is exactly 1 for a head whose maximum stays)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+        m_run = mnew;
+        l_lane *= alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = shfl(alpha, 4 * q + e);   // accumulator row 4 q + e
+#pragma unroll
+          for (int i = 0; i < C::NNT4; ++i) acc[i][e] *= ae;
+        }
+      }
+      lt4_t pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pj = __builtin_amdgcn_exp2f(x[i] - m_run);
+        l_lane += pj;
+        const LT hi = (LT)pj;
+        const LT lo = (LT)(pj - (float)hi);
+        pl[i] = s < 8 ? hi : lo;
+      }
+      const op4_t pa = __builtin_bit_cast(op4_t, pl);
+
+      // ---- acc += P z_v over the wave's 16 tokens: B[k = 4 q + j][rank
+      // 16 nt + s] = z_v[16 u + 4 q + j] (one transposed read), for the wave's
+      // n-tiles grp + 4 i below the group's rank (one unrolled loop per count)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int nt = min(grp + 4 * i, C::RCAP / 16 - 1);
+        const int row = 16 * u + 4 * q + (s >> 2);
+        const i16x4 vb = ds_read_tr16(zvt + row * C::PITV * 16 + (16 * nt + 4 * (s & 3)) * 2);
+        acc[i] = mfma16x16x16(pa, __builtin_bit_cast(op4_t, vb), acc[i]);
+      }
+
+      if ((i_c & F_END) || n + 1 == n_end) record(i_c);
+      i_c = i_a;
+      i_a = i_d;
+    }
   };
   // (chunk counts rounded up to even: the extra chunk meets a zero query)
   with_count<1, C::NKC / 2>(cdiv(nkc, 2), [&](auto nk2_t) __attribute__((always_inline)) {
