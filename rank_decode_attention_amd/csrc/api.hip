@@ -403,10 +403,6 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
   p.qabs = desc->use_rope ? nullptr : (const float*)(ws + pl.hdr_bytes + pl.rec_bytes);
   p.out = out;
   p.batch = batch; p.max_len = cache->max_len; p.H = desc->n_q_heads; p.G = desc->n_groups; p.P = pl.P;
-  for (int j = 0; j < desc->n_groups; ++j) {
-    p.Pg[j] = pl.Pg[j];
-    p.gblk[j] = pl.gblk[j];
-  }
   p.block_table = cache->block_table; p.page_shift = cache->page_shift; p.max_pages = cache->max_pages;
   p.rvp = pl.rvp; p.rec_stride = pl.nq * (2 + pl.rvp); p.qabs_stride = pl.qabs_stride;
   p.qscale = sm_scale * 1.4426950408889634f;
@@ -437,6 +433,14 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
       p.pk[j] = (int)pl.dk_pitch[j]; p.pv[j] = (int)pl.dv_pitch[j];
     }
     p.zero_padded = 1;
+  }
+  // blocks per group: the plan's weighted counts where the absorbed-query
+  // kernel runs (the same test launch_decode applies), else P for every group
+  // (the kernels that take block id = p * G + g); the merge reads them
+  const bool weighted = !desc->use_rope && abs_supported(pl.key, p);
+  for (int j = 0; j < desc->n_groups; ++j) {
+    p.Pg[j] = weighted ? pl.Pg[j] : pl.P;
+    p.gblk[j] = weighted ? pl.gblk[j] : j * pl.P;
   }
   hipError_t e;
   if (!desc->use_rope) {
