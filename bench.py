@@ -485,8 +485,8 @@ def main():
         record_traffic(args.record_traffic, args.workload, 1 << 30, args.traffic_out)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the method's hot path here is "
-              f"single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode hot path measured "
+              f"here runs on one GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch

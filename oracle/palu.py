@@ -21,7 +21,7 @@ What is computed here is the plain definition: rebuild full K and V in fp64,
 apply RoPE to the rebuilt keys and to the query, run naive softmax attention.
 Fusion on the GPU is a speed claim only and must not change this result.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * RoPE: theta_i = base^(-2i/d_h), i < d_h/2, pairs (i, i + d_h/2)
   ("half-split"); keys rotate by their cache index t, the query by its

@@ -8,7 +8,7 @@ them to the stored number formats; it holds none of the method's arithmetic
 Workloads follow the shapes named for the method's hot path: a tiny fp32
 layer, a Llama-2-7B-shaped layer, long-context ragged batches, a GQA
 Llama-3-8B-shaped layer pair (RoPE / no-RoPE) and an int4 layer with its
-prefill chunk.  Distributions (one reading, stated in the design doc):
+prefill chunk.  Distributions (the pages give none; one plain reading):
 
 * factor matrices A (d_model x r) and B (r x w) are Gaussian with standard
   deviation 1/sqrt(fan_in) (fan_in = d_model for A, r for B);

@@ -2,7 +2,7 @@
 from the seeded generators, run the library through its binding, build the
 matching fp64 oracle inputs, and compare.
 
-Tolerances (from the spec bar, stated in the design doc):
+Tolerances (the accuracy bar of the decode outputs):
   fp16 / bf16 outputs: max |gpu - ref| <= 2e-3 + half an ulp of the output
   format at |ref| (the output is stored in that format), and
   ||gpu - ref||_2 / ||ref||_2 <= 1e-2;

@@ -56,7 +56,7 @@ def _sdpa(q, K, V, scale):
 # ------------------------------------------------------------------ pins
 def pin_identity_vs_sdpa(use_rope):
     """A = W, B = I, r = w: the method reduces to standard attention over
-    K = x W_k, V = x W_v (spec check (a)); reference: torch SDPA fp64."""
+    K = x W_k, V = x W_v; reference: torch SDPA fp64."""
     rng = np.random.default_rng(7)
     batch, H, Hkv, d_h, G, D, L = 2, 6, 2, 8, 2, 12, 9
     n_g = Hkv // G
@@ -88,8 +88,7 @@ def pin_identity_vs_sdpa(use_rope):
 
 def pin_absorbed_and_fused_value():
     """No-RoPE heads: attention through the absorbed query (q . B_k^T) against
-    z_k and values through (P . z_v) . B_v equal the rebuilt-K/V result
-    (spec check (b))."""
+    z_k and values through (P . z_v) . B_v equal the rebuilt-K/V result."""
     rng = np.random.default_rng(11)
     q, zk, zv, Bk, Bv, lens = _rand_case(rng, batch=3, H=8, Hkv=4, d_h=6, G=2, r=4, L=11)
     batch, H, d_h = q.shape
@@ -112,7 +111,7 @@ def pin_absorbed_and_fused_value():
 
 def pin_mpmath_bruteforce():
     """Scalar evaluation of every sum at 50 digits (mpmath) on tiny shapes
-    (spec check (c), brute force)."""
+    (brute force)."""
     import mpmath as mp
     mp.mp.dps = 50
     rng = np.random.default_rng(3)
