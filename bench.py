@@ -267,7 +267,7 @@ def cpu_baseline(wl, n_seq: int, reps: int = 3):
     def lat(which, b, j):
         if wl.latent == "i4":
             packed, scales = PI.latent_int4(wl, which, b, j, n=int(lens[b]))
-            return oracle.int4_latent(packed, scales, int(PI.ranks(wl)[j]), wl.act)
+            return oracle.int4_latent(packed, scales, int(PI.ranks(wl)[j]))
         return oracle.upcast(PI.latent(wl, which, b, j, n=int(lens[b])), wl.latent)
     zk = [[lat("k", b, j) for b in range(n_seq)] for j in range(wl.n_groups)]
     zv = [[lat("v", b, j) for b in range(n_seq)] for j in range(wl.n_groups)]

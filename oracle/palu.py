@@ -36,10 +36,13 @@ Readings where the pages are silent:
   s16 == 0; the last chunk of a row whose rank is not a multiple of 32 is
   short; codes are 4-bit two's complement, element 2i in the low nibble of
   byte i, rows padded with zero nibbles to a 16-byte multiple.
-* int4 decode: the attention consumes the dequantised latent code * scale
-  rounded once, to nearest even, into the activation format (fp16 or
-  bf16), as the GPU's matrix units take it; everything after that is the
-  plain definition above.
+* int4 decode: the attention consumes the dequantised latent
+  z_hat = code * scale exactly (a 4-bit integer times a binary16 scale has at
+  most 14 significant bits, so the product is exact in fp64 and in fp32);
+  everything after that is the plain definition above.  The 16-bit rows of
+  the library's stand-alone expansion call are that product rounded once, to
+  nearest even, into fp16 or bf16 (int4_rows16); the decode never reads
+  them.
 
 Pins (tests/test_oracle_pins.py): standard attention through
 torch.nn.functional.scaled_dot_product_attention (float64, CPU) in the
@@ -59,7 +62,7 @@ import numpy as np
 __all__ = [
     "upcast", "rope_theta", "rope", "reconstruct", "attend", "attend_partial", "merge_partials",
     "decode_attention", "project", "quant_int4", "pack_int4", "unpack_int4", "dequant_int4",
-    "chunks_per_row", "round_to", "int4_latent", "chunk_attention",
+    "chunks_per_row", "round_to", "int4_latent", "int4_rows16", "chunk_attention",
 ]
 
 QUANT_GROUP = 32
@@ -100,12 +103,17 @@ def round_to(x: np.ndarray, fmt: str) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(m, p)), e - p)
 
 
-def int4_latent(packed: np.ndarray, scales: np.ndarray, r: int, act: str) -> np.ndarray:
+def int4_latent(packed: np.ndarray, scales: np.ndarray, r: int) -> np.ndarray:
     """Latent rows a decode step attends over when the cache holds int4
-    codes: unpack, z_hat = code * scale (exact), rounded to the activation
-    format (the reading stated in the module docstring)."""
-    z = dequant_int4(unpack_int4(packed, r), scales)
-    return round_to(z, act) if act in _SIG_BITS else z
+    codes: unpack, then z_hat = code * scale, exact in fp64 (the reading
+    stated in the module docstring)."""
+    return dequant_int4(unpack_int4(packed, r), scales)
+
+
+def int4_rows16(packed: np.ndarray, scales: np.ndarray, r: int, fmt: str) -> np.ndarray:
+    """16-bit rows of the stand-alone int4 expansion: the exact z_hat rounded
+    once, to nearest even, into fmt ('f16' or 'bf16')."""
+    return round_to(int4_latent(packed, scales, r), fmt)
 
 
 # ------------------------------------------------------------------ RoPE

@@ -69,7 +69,7 @@ class LazyLatents:
         L = int(self.lens[b])
         if self.wl.latent == "i4":
             packed, scales = PI.latent_int4(self.wl, self.which, b, self.j, n=max(L, 1))
-            return oracle.int4_latent(packed, scales, int(PI.ranks(self.wl)[self.j]), self.wl.act)
+            return oracle.int4_latent(packed, scales, int(PI.ranks(self.wl)[self.j]))
         a = PI.latent(self.wl, self.which, b, self.j, n=max(L, 1))
         return oracle.upcast(a, self.wl.latent)
 

@@ -1,7 +1,6 @@
-"""GPU: palu_dequant_latent (the int4 -> 16-bit expansion that palu_decode_attn
-applies to int4 caches) is bit-exact against the oracle's reading of int4
-latents (code * scale, exact, rounded once to the activation format; zero past
-the rank), through the C ABI."""
+"""GPU: palu_dequant_latent (int4 rows -> 16-bit rows) is bit-exact against
+the oracle's 16-bit rows of int4 latents (code * scale, exact, rounded once to
+fp16 / bf16; zero past the rank), through the C ABI."""
 import numpy as np
 import pytest
 
@@ -36,7 +35,7 @@ def test_dequant_bit_exact(fmt, r, n):
     wl = PI.scaled("int4", rank=r, act=fmt)
     packed, scales = PI.latent_int4(wl, "k", 0, 0, n=n)
     got = _expand(packed, scales, r, fmt)
-    want = oracle.int4_latent(packed, scales, r, fmt)
+    want = oracle.int4_rows16(packed, scales, r, fmt)
     assert np.array_equal(got[:, :r], _bits(want, fmt))
     assert np.all(got[:, r:] == 0)
 
@@ -57,6 +56,6 @@ def test_dequant_every_code_and_odd_scales(fmt):
     s[3] = np.float16(4096.0)          # large
     s[4] = np.float16(-0.75)           # negative (never written by the quantiser; still code * scale)
     got = _expand(packed, s, r, fmt)
-    want = oracle.int4_latent(packed, s, r, fmt)
+    want = oracle.int4_rows16(packed, s, r, fmt)
     assert np.array_equal(got[:, :r], _bits(want, fmt))
     assert np.all(got[:, r:] == 0)

@@ -355,31 +355,68 @@ def pin_round_to():
 
 
 def pin_int4_latent():
-    """int4_latent over every code and a sweep of binary16 scales, against
-    the library conversion of the exact product; the byte layout against a
-    hand-packed row (codes 1..7, -1..-7, 0 in the documented nibble order)."""
-    import torch
+    """int4_latent is the exact product code * scale: every code against a
+    sweep of binary16 scales, compared with exact rational arithmetic
+    (fractions.Fraction); the byte layout against a hand-packed row (codes
+    1..7, -1..-7, 0 in the documented nibble order)."""
+    from fractions import Fraction
     codes = np.arange(-7, 8, dtype=np.int8)                       # 15 codes
     rng = np.random.default_rng(5)
     s = rng.uniform(0.01, 3.0, 64).astype(np.float16)
-    grid_c = np.tile(codes, 64).reshape(64, 15)
-    # pad each row of 15 codes to a 32-element chunk of zeros
+    s[:4] = [1 + 2.0 ** -10, 2.0 ** -20, 65504.0, 0.0]             # 11 significant bits, subnormal, max, zero
     full = np.zeros((64, 32), dtype=np.int8)
-    full[:, :15] = grid_c
-    packed = O.pack_int4(full)
-    exact = full.astype(np.float64) * s.astype(np.float64)[:, None]
-    got16 = O.int4_latent(packed, s[:, None], 32, "f16")
-    assert np.array_equal(got16, exact.astype(np.float16).astype(np.float64))
-    gotb = O.int4_latent(packed, s[:, None], 32, "bf16")
-    wantb = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
-    assert np.array_equal(gotb, wantb)
-    # hand-packed row: element 2i in the low nibble of byte i, two's complement
+    full[:, :15] = np.tile(codes, 64).reshape(64, 15)
+    got = O.int4_latent(O.pack_int4(full), s[:, None], 32)
+    for i in range(64):
+        for k in range(15):
+            assert Fraction(float(got[i, k])) == Fraction(int(full[i, k])) * Fraction(float(s[i]))
+    assert not got[:, 15:].any()
+    # 7 * (1 + 2^-10) has 14 significant bits: kept exactly (binary16 would round it)
+    assert got[0, 14] == 7 * (1 + 2.0 ** -10)
     row = bytes([0x21, 0x43, 0x65, 0xF7, 0xDE, 0xBC, 0x9A, 0x00] + [0] * 8)
     want = [1, 2, 3, 4, 5, 6, 7, -1, -2, -3, -4, -5, -6, -7, 0, 0]
-    got = O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[1.0]], np.float16), 16, "f16")
+    got = O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[1.0]], np.float16), 16)
     assert got[0].tolist() == want
     # rank shorter than the chunk: only the first r elements come back
-    assert O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[0.5]], np.float16), 3, "f16").shape == (1, 3)
+    assert O.int4_latent(np.frombuffer(row, np.uint8)[None], np.array([[0.5]], np.float16), 3).shape == (1, 3)
+
+
+def pin_int4_rows16():
+    """int4_rows16 (the stand-alone expansion's 16-bit rows) against the
+    library conversions of the exact product: numpy float64 -> float16 and
+    torch float32 -> bfloat16."""
+    import torch
+    rng = np.random.default_rng(6)
+    full = rng.integers(-7, 8, size=(64, 32)).astype(np.int8)
+    s = rng.uniform(0.01, 3.0, 64).astype(np.float16)
+    exact = full.astype(np.float64) * s.astype(np.float64)[:, None]
+    got16 = O.int4_rows16(O.pack_int4(full), s[:, None], 32, "f16")
+    assert np.array_equal(got16, exact.astype(np.float16).astype(np.float64))
+    gotb = O.int4_rows16(O.pack_int4(full), s[:, None], 32, "bf16")
+    wantb = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(gotb, wantb)
+
+
+def pin_int4_decode_golden():
+    """A decode step over an int4 cache against its hand-worked closed form
+    (tests/golden/int4_decode_worked.json); the latent 7 * (1 + 2^-10) is
+    only exact when the code * scale product is not rounded to 16 bits."""
+    with open(os.path.join(GOLDEN, "int4_decode_worked.json")) as f:
+        fx = json.load(f)
+    r = fx["rank"]
+
+    def rows(key):
+        packed = np.stack([np.frombuffer(bytes.fromhex(h), np.uint8) for h in fx[key + "_packed_hex"]])
+        scales = np.array(fx[key + "_scale_bits"], dtype=np.uint16).view(np.float16)[:, None]
+        return O.int4_latent(packed, scales, r)[None]          # [batch 1][L][r]
+    q = np.array(fx["q"], dtype=np.float64)[None, None]
+    out = O.decode_attention(q, [rows("zk")], [rows("zv")], [np.eye(2)], [np.eye(2)], [2], n_kv_heads=1,
+                             use_rope=False, sm_scale=fx["sm_scale"])
+    s = 1 + 2.0 ** -10
+    a = 7 * s
+    p0, p1 = 1.0 / (1.0 + math.exp(-a)), 1.0 / (1.0 + math.exp(a))
+    want = np.array([p0 * s, -7 * s * p0 + 3.5 * p1])
+    np.testing.assert_allclose(out[0, 0], want, rtol=0, atol=1e-14)
 
 
 def pin_chunk_attention():
@@ -417,7 +454,8 @@ def pin_chunk_attention():
 
 PINS = [pin_absorbed_and_fused_value, pin_mpmath_bruteforce, pin_softmax_closed_forms, pin_rope, pin_gqa,
         pin_split_merge, pin_golden_decode, pin_rope_closed_form_d2, pin_project, pin_int4_golden,
-        pin_int4_properties, pin_upcast, pin_round_to, pin_int4_latent, pin_chunk_attention]
+        pin_int4_properties, pin_upcast, pin_round_to, pin_int4_latent, pin_int4_rows16, pin_int4_decode_golden,
+        pin_chunk_attention]
 
 
 @pytest.mark.parametrize("use_rope", [False, True])
@@ -483,6 +521,10 @@ def _round_f16_as_bf16(x, fmt):
     return O.__dict__["_orig_round"](x, "bf16")
 
 
+def _int4_latent_rounded_f16(packed, scales, r):
+    return O.round_to(O.dequant_int4(O.unpack_int4(packed, r), scales), "f16")
+
+
 def _unpack_nibbles_swapped(packed, r):
     p = np.asarray(packed, dtype=np.uint8)
     return O.__dict__["_orig_unpack"](((p << 4) | (p >> 4)).astype(np.uint8), r)
@@ -499,6 +541,7 @@ MUTANTS = [
     ("round_to", _round_truncate),
     ("round_to", _round_f16_as_bf16),
     ("unpack_int4", _unpack_nibbles_swapped),
+    ("int4_latent", _int4_latent_rounded_f16),
 ]
 
 
