@@ -165,8 +165,10 @@ palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows,
 
 /*
  * palu_dequant_latent - int4 latent rows to 16-bit rows (quantization on top
- * of the low-rank cache: PALU page, section "Rollout", route C).  The same
- * expansion palu_decode_attn applies to an I4 cache before attending.
+ * of the low-rank cache: PALU page, section "Rollout", route C), for callers
+ * that want a 16-bit copy of an int4 cache.  The values are rounded to the
+ * 16-bit format; palu_decode_attn does not use this rounding (it attends over
+ * the exact code * scale).
  *   codes    device [n_rows][16 * ceil(r/32)] bytes (layout of PALU_I4 above)
  *   scales   device [n_rows][ceil(r/32)] binary16
  *   out      device [n_rows][32 * ceil(r/32)] out_dtype (output): element e of
@@ -232,14 +234,21 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  * Without RoPE the score uses the absorbed query (q_h B_k^T) against z_k and,
  * in all cases, values enter as (softmax . z_v) . B_v; both equal the formula
  * up to rounding.  Arithmetic is binary32 throughout.
- * I4 latents (act_dtype F16 or BF16): the decode consumes the
+ * I4 latents (act_dtype F16 or BF16): the decode attends over the
  * dequantised latent code * scale (PALU page, section "Rollout", route C:
- * quantization on top of the low-rank cache), formed exactly in binary32 and
- * rounded to nearest even into act_dtype.  On MHA head-group shapes (4 kv
- * heads per group, one query head each, head_dim 128, RoPE) the decode kernel
- * expands the int4 tiles on chip; on other shapes the rows [0, L_b) of every
- * sequence are first expanded into the workspace (16-bit rows of the rank
- * rounded up to 32, zero past the rank), then attended as above.
+ * quantization on top of the low-rank cache) exactly, never rounded to a
+ * 16-bit format.  On MHA head-group shapes (4 kv heads per group, one query
+ * head each, head_dim 128, RoPE, ranks <= 256) the decode kernel feeds the
+ * codes to the matrix units as exact integers and applies each 32-element
+ * chunk's scale afterwards (to the chunk's partial key product, and to the
+ * attention weights before they meet the value codes); with F16 activations
+ * the scaled weights must stay in the binary16 range, which holds for scales
+ * up to 255 (latent magnitudes up to ~1785).  On other shapes the rows
+ * [0, L_b) of every sequence are first expanded into the workspace as exact
+ * hi + lo pairs of 16-bit values (each 32-element chunk becomes 64 values,
+ * rank r -> 64 ceil(r/32)) and attended against B_k / B_v with every row
+ * duplicated to match; that doubled rank must fit a decode kernel (no RoPE:
+ * up to 320; GQA groups of 2 kv heads with RoPE: up to 320; else UNSUPPORTED).
  *   q          device [batch][H][d_h] act_dtype
  *   cache      latent buffers; rows [0, L_b) of each (b, j) are read
  *   B_k, B_v   device, layout above, act_dtype
@@ -252,8 +261,8 @@ size_t palu_decode_workspace_bytes(const palu_attn_desc* desc, int32_t batch, in
  *   workspace  device, at least palu_decode_workspace_bytes(desc, batch,
  *              cache->max_len) bytes, 256-byte aligned; contents are scratch
  *              (for I4 on shapes expanded into the workspace it includes
- *              batch * max_len * sum_j 2 * (ceil32(r_k^j) + ceil32(r_v^j))
- *              bytes of expanded latents)
+ *              batch * max_len * sum_j 4 * (ceil32(r_k^j) + ceil32(r_v^j))
+ *              bytes of hi/lo latents and the duplicated factors)
  * batch == 0 is a no-op after the descriptor checks (pointers may be NULL).
  * Errors: INVALID_ARG for null pointers, batch < 0, head counts that do not
  * divide, odd head_dim, rank <= 0, max_len <= 0, non-finite sm_scale,

@@ -123,12 +123,15 @@ struct DecodePlan {
   int P, rvp, qabs_stride, nq;
   int Pg[kMaxGroups], gblk[kMaxGroups];   // blocks of each group and the first block id of its range
   size_t hdr_bytes, rec_bytes, qabs_bytes, total;
-  // int4 latents: the decode runs on a 16-bit copy of the cache in the
-  // workspace (ranks rounded up to 32, rows zero-padded), expanded first
-  bool q4, fused4;   // fused4: the MHA kernel reads the int4 codes itself (no expansion pass)
-  size_t dense_k_bytes, dense_v_bytes;
+  // int4 latents: the MHA kernel reads the codes itself (fused4); on other
+  // shapes the decode runs on an exact 16-bit copy of the cache in the
+  // workspace, every 32-element chunk expanded to hi and lo chunks (rank
+  // r' = 64 ceil(r/32)), against factors whose rows are duplicated to match
+  bool q4, fused4;
+  size_t dense_k_bytes, dense_v_bytes, dup_k_bytes, dup_v_bytes;
   int64_t dk_pitch[kMaxGroups], dv_pitch[kMaxGroups], dk_goff[kMaxGroups], dv_goff[kMaxGroups];
   int64_t dk_seq, dv_seq;
+  int drk[kMaxGroups], drv[kMaxGroups];   // ranks the decode kernels see
 };
 
 Elt elt_of(palu_dtype d) { return d == PALU_F32 ? Elt::F32 : d == PALU_F16 ? Elt::F16 : Elt::BF16; }
@@ -150,17 +153,52 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
     return fail(PALU_ERR_UNSUPPORTED, "int4 latents need act_dtype F16 or BF16");
   if (!pl->q4 && d->latent_dtype != d->act_dtype)
     return fail(PALU_ERR_UNSUPPORTED, "latent_dtype must equal act_dtype for float latents");
-  // (int4: the kernels see 16-bit rows of 32-rounded rank, zero past the rank)
-  auto dense_rank = [&](int r) { return pl->q4 ? (int)roundup(r, 32) : r; };
+  const int ng = d->n_kv_heads / d->n_groups, qpk = d->n_q_heads / d->n_kv_heads;
+  // int4: the MHA kernel reads the codes (ranks rounded up to 32) where it
+  // applies; elsewhere the kernels see hi/lo rows of twice that rank
+  pl->fused4 = false;
+  if (pl->q4) {
+    int r32k = 0, r32v = 0;
+    for (int j = 0; j < d->n_groups; ++j) {
+      r32k = (int)std::max<int64_t>(r32k, roundup(d->rank_k[j], 32));
+      r32v = (int)std::max<int64_t>(r32v, roundup(d->rank_v[j], 32));
+    }
+    if (r32k > 1024 || r32v > 1024) return fail(PALU_ERR_UNSUPPORTED, "int4 latents: rank above 1024");
+    const DecodeKey k32{elt_of(d->act_dtype), d->head_dim, ng, qpk, r32k, r32v, d->use_rope != 0};
+    int ck = 0, cv = 0;
+    if (decode_supported(k32, &ck, &cv)) {
+      DecodeParams t;
+      memset(&t, 0, sizeof(t));
+      t.G = d->n_groups;
+      t.q4 = 1;
+      t.rvp = (int)roundup(cv, 16);
+      for (int j = 0; j < d->n_groups; ++j) {
+        t.rk[j] = d->rank_k[j];
+        t.rv[j] = d->rank_v[j];
+        t.pk[j] = (int)row_pitch(PALU_I4, d->rank_k[j]);
+        t.pv[j] = (int)row_pitch(PALU_I4, d->rank_v[j]);
+      }
+      pl->fused4 = mha_supported(k32, t);
+    }
+  }
+  auto dense_rank = [&](int r) {
+    return pl->q4 ? (int)(pl->fused4 ? roundup(r, 32) : 2 * roundup(r, 32)) : r;
+  };
   int rk_max = 0, rv_max = 0;
   for (int j = 0; j < d->n_groups; ++j) {
-    rk_max = dense_rank(d->rank_k[j]) > rk_max ? dense_rank(d->rank_k[j]) : rk_max;
-    rv_max = dense_rank(d->rank_v[j]) > rv_max ? dense_rank(d->rank_v[j]) : rv_max;
+    pl->drk[j] = dense_rank(d->rank_k[j]);
+    pl->drv[j] = dense_rank(d->rank_v[j]);
+    rk_max = pl->drk[j] > rk_max ? pl->drk[j] : rk_max;
+    rv_max = pl->drv[j] > rv_max ? pl->drv[j] : rv_max;
   }
-  if (pl->q4 && (rk_max > 1024 || rv_max > 1024)) return fail(PALU_ERR_UNSUPPORTED, "int4 latents: rank above 1024");
-  const int ng = d->n_kv_heads / d->n_groups, qpk = d->n_q_heads / d->n_kv_heads;
   pl->key = DecodeKey{elt_of(d->act_dtype), d->head_dim, ng, qpk, rk_max, rv_max, d->use_rope != 0};
   int rk_cap = 0, rv_cap = 0;
+  if (pl->q4 && !pl->fused4 && !decode_supported(pl->key, &rk_cap, &rv_cap))
+    return fail(PALU_ERR_UNSUPPORTED,
+                "int4 latents on this shape are attended as exact hi/lo 16-bit rows of twice the rank rounded "
+                "up to 32 (%d, %d), which no decode kernel covers; the MHA head-group shape (4 kv heads per "
+                "group, one query head each, head_dim 128, RoPE, ranks <= 256) reads int4 codes directly",
+                rk_max, rv_max);
   if (!decode_supported(pl->key, &rk_cap, &rv_cap))
     return fail(PALU_ERR_UNSUPPORTED,
                 "no decode kernel for dtype %d, head_dim %d, %d kv heads per group, %d query heads per kv head, "
@@ -187,8 +225,8 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
     t.G = d->n_groups;
     t.qabs_stride = pl->qabs_stride;
     for (int j = 0; j < d->n_groups; ++j) {
-      t.rk[j] = dense_rank(d->rank_k[j]);
-      t.rv[j] = dense_rank(d->rank_v[j]);
+      t.rk[j] = pl->drk[j];
+      t.rv[j] = pl->drv[j];
       t.pk[j] = pl->q4 ? 2 * t.rk[j] : (int)row_pitch(d->latent_dtype, d->rank_k[j]);
       t.pv[j] = pl->q4 ? 2 * t.rv[j] : (int)row_pitch(d->latent_dtype, d->rank_v[j]);
     }
@@ -225,36 +263,28 @@ palu_status plan_decode(const palu_attn_desc* d, int batch, int max_len, DecodeP
   pl->hdr_bytes = (size_t)roundup((int64_t)(batch + 1) * 4, 256);
   pl->rec_bytes = (size_t)roundup((int64_t)d->n_groups * (P + batch) * pl->nq * (2 + pl->rvp) * 4, 256);
   pl->qabs_bytes = d->use_rope ? 0 : (size_t)roundup((int64_t)batch * d->n_q_heads * pl->qabs_stride * 4, 256);
-  pl->dense_k_bytes = pl->dense_v_bytes = 0;
+  pl->dense_k_bytes = pl->dense_v_bytes = pl->dup_k_bytes = pl->dup_v_bytes = 0;
   pl->dk_seq = pl->dv_seq = 0;
-  pl->fused4 = false;
-  if (pl->q4) {
-    DecodeParams t;
-    memset(&t, 0, sizeof(t));
-    t.G = d->n_groups;
-    t.q4 = 1;
-    t.rvp = pl->rvp;
-    for (int j = 0; j < d->n_groups; ++j) {
-      t.rk[j] = d->rank_k[j];
-      t.rv[j] = d->rank_v[j];
-      t.pk[j] = (int)row_pitch(PALU_I4, d->rank_k[j]);
-      t.pv[j] = (int)row_pitch(PALU_I4, d->rank_v[j]);
-    }
-    pl->fused4 = mha_supported(pl->key, t);
-  }
   if (pl->q4 && !pl->fused4) {
+    const int64_t w = (int64_t)ng * d->head_dim;
+    int64_t bk = 0, bv = 0;
     for (int j = 0; j < d->n_groups; ++j) {
-      pl->dk_pitch[j] = 2 * roundup(d->rank_k[j], 32);
-      pl->dv_pitch[j] = 2 * roundup(d->rank_v[j], 32);
+      pl->dk_pitch[j] = 2 * (int64_t)pl->drk[j];
+      pl->dv_pitch[j] = 2 * (int64_t)pl->drv[j];
       pl->dk_goff[j] = pl->dk_seq;
       pl->dv_goff[j] = pl->dv_seq;
       pl->dk_seq += (int64_t)max_len * pl->dk_pitch[j];
       pl->dv_seq += (int64_t)max_len * pl->dv_pitch[j];
+      bk += (int64_t)pl->drk[j] * w * 2;
+      bv += (int64_t)pl->drv[j] * w * 2;
     }
     pl->dense_k_bytes = (size_t)roundup((int64_t)batch * pl->dk_seq, 256);
     pl->dense_v_bytes = (size_t)roundup((int64_t)batch * pl->dv_seq, 256);
+    pl->dup_k_bytes = (size_t)roundup(bk, 256);
+    pl->dup_v_bytes = (size_t)roundup(bv, 256);
   }
-  pl->total = pl->hdr_bytes + pl->rec_bytes + pl->qabs_bytes + pl->dense_k_bytes + pl->dense_v_bytes;
+  pl->total = pl->hdr_bytes + pl->rec_bytes + pl->qabs_bytes + pl->dense_k_bytes + pl->dense_v_bytes +
+              pl->dup_k_bytes + pl->dup_v_bytes;
   return PALU_OK;
 }
 // Latent storage one prefill writes (contiguous, or paged through a block table).
@@ -364,8 +394,12 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
   make_layout(desc, cache->layout_len, &L);
   uint8_t* const dense_k = (uint8_t*)workspace + pl.hdr_bytes + pl.rec_bytes + pl.qabs_bytes;
   uint8_t* const dense_v = dense_k + pl.dense_k_bytes;
+  uint8_t* const dup_k = dense_v + pl.dense_v_bytes;
+  uint8_t* const dup_v = dup_k + pl.dup_k_bytes;
+  const int w = (desc->n_kv_heads / desc->n_groups) * desc->head_dim;
   if (pl.q4 && !pl.fused4) {
-    // int4 latents -> 16-bit rows (the history of every sequence, keys and values)
+    // int4 latents -> exact hi/lo 16-bit rows (the history of every sequence,
+    // keys and values), and the factors with every row duplicated to match
     static_assert(kDqMaxGroups >= kMaxGroups, "group arrays");
     DequantParams dp;
     memset(&dp, 0, sizeof(dp));
@@ -390,8 +424,24 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
       }
     }
     dp.n_sides = 2;
+    dp.split = 1;
     hipError_t e = launch_dequant(desc->act_dtype == PALU_F16 ? 1 : 2, dp, stream);
     if (e != hipSuccess) return hip_fail(e, "int4 expansion launch");
+    DupParams up;
+    memset(&up, 0, sizeof(up));
+    up.src[0] = B_k; up.src[1] = B_v; up.dst[0] = dup_k; up.dst[1] = dup_v;
+    up.G = desc->n_groups; up.w = w;
+    int64_t so[2] = {0, 0}, dof[2] = {0, 0};
+    for (int j = 0; j < desc->n_groups; ++j) {
+      const int r[2] = {desc->rank_k[j], desc->rank_v[j]}, rr[2] = {pl.drk[j], pl.drv[j]};
+      for (int side = 0; side < 2; ++side) {
+        up.soff[side][j] = so[side]; up.doff[side][j] = dof[side]; up.rank[side][j] = r[side];
+        so[side] += (int64_t)r[side] * w; dof[side] += (int64_t)rr[side] * w;
+        up.max_rows = rr[side] > up.max_rows ? rr[side] : up.max_rows;
+      }
+    }
+    e = launch_dup_factor(up, stream);
+    if (e != hipSuccess) return hip_fail(e, "factor duplication launch");
   }
   DecodeParams p;
   memset(&p, 0, sizeof(p));
@@ -408,7 +458,6 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
   p.qscale = sm_scale * 1.4426950408889634f;
   p.rope_base = desc->rope_base;
   p.seq_bytes_k = L.seq_k; p.seq_bytes_v = L.seq_v;
-  const int w = (desc->n_kv_heads / desc->n_groups) * desc->head_dim;
   int64_t bk = 0, bv = 0;
   for (int j = 0; j < desc->n_groups; ++j) {
     p.goff_k[j] = L.goff_k[j]; p.goff_v[j] = L.goff_v[j];
@@ -427,10 +476,15 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
     }
   } else if (pl.q4) {
     p.zk = dense_k; p.zv = dense_v;
+    p.Bk = dup_k; p.Bv = dup_v;
     p.seq_bytes_k = pl.dk_seq; p.seq_bytes_v = pl.dv_seq;
+    int64_t dk = 0, dv = 0;
     for (int j = 0; j < desc->n_groups; ++j) {
       p.goff_k[j] = pl.dk_goff[j]; p.goff_v[j] = pl.dv_goff[j];
       p.pk[j] = (int)pl.dk_pitch[j]; p.pv[j] = (int)pl.dv_pitch[j];
+      p.rk[j] = pl.drk[j]; p.rv[j] = pl.drv[j];
+      p.boff_k[j] = dk; p.boff_v[j] = dv;
+      dk += (int64_t)pl.drk[j] * w; dv += (int64_t)pl.drv[j] * w;
     }
     p.zero_padded = 1;
   }

@@ -1018,9 +1018,23 @@ static const Entry* find_entry(const DecodeKey& k) {
   return best;
 }
 
+// 16-bit latents without RoPE that no split-kernel instance covers (ranks
+// up to 320 with groups of 4 kv heads) are left to the absorbed-query kernel
+// alone (at most 8 query heads per group; the absorbed query and the merge
+// take head_dim 64 or 128).
+static bool abs_only(const DecodeKey& k) {
+  return !k.rope && (k.elt == Elt::F16 || k.elt == Elt::BF16) && k.kv_per_group * k.q_per_kv <= 8 &&
+         k.rk_max <= 320 && k.rv_max <= 320 && (k.head_dim == 64 || k.head_dim == 128);
+}
+
 bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap) {
   const Entry* e = find_entry(k);
-  if (!e) return false;
+  if (!e) {
+    if (!abs_only(k)) return false;
+    if (rk_cap) *rk_cap = 320;
+    if (rv_cap) *rv_cap = 320;
+    return true;
+  }
   if (rk_cap) *rk_cap = e->key.rk_max;
   if (rv_cap) *rv_cap = e->key.rv_max;
   return true;
@@ -1028,10 +1042,10 @@ bool decode_supported(const DecodeKey& k, int* rk_cap, int* rv_cap) {
 
 hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t stream, hipEvent_t t0,
                          hipEvent_t t1) {
-  const Entry* e = find_entry(k);
-  if (!e) return hipErrorInvalidValue;
   if (mha_supported(k, p)) return launch_decode_mha(k, p, stream, t0, t1);
   if (abs_supported(k, p)) return launch_decode_abs(k, p, stream, t0, t1);
+  const Entry* e = find_entry(k);
+  if (!e) return hipErrorInvalidValue;
   return e->decode(p, stream, t0, t1);
 }
 

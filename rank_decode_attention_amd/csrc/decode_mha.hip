@@ -63,7 +63,15 @@ struct MhaCfg {
   // (int4) are expanded into the ring one step ahead
   static constexpr int NKB = Q4 ? 2 : 3, NVB = Q4 ? 3 : 4;
   static constexpr int NSTG = Q4 ? 2 : 3;      // B_k staging slots
+  // B_k^T operands in VGPRs (int4 instances up to 5 key chunks, whose other
+  // registers fit beside them) or in AGPRs (everything else)
+  static constexpr bool BREG_V = Q4 && NKC <= 5;
   static constexpr int AP = 17;                // angle-table row pitch in 16-byte units (68 floats)
+  // int4: per-token scales of a tile's 32-rank chunks, fp32, [slot][row][SCP]
+  // (the pitch keeps the two 16-byte reads of a row aligned and spreads rows
+  // over the banks)
+  static constexpr int SCP = 12;
+  static constexpr int NSK = Q4 ? NKB : 1, NSV = Q4 ? NVB : 1;
   static constexpr int STGB = 32 * DH * NH * 2;   // bytes of one staged B_k chunk (32 ranks x 512 columns)
   static_assert(NDT * 16 * NT == TILEB, "tile DMA");
   static_assert(NT / 32 == 16, "one DMA instruction covers 16 rows");
@@ -134,6 +142,8 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   __shared__ float sp[2][C::NH][2][C::TT];        // partial scores [tile parity][head][frequency half][token]
   __shared__ uint4 pst[C::NW][2 * C::NH * C::TT * 2 / 16];   // per wave: P (hi, lo) of the previous tile, [part][head][token]
   __shared__ uint4 pzero[C::TT * 2 / 16];          // zero rows of the P operand
+  __shared__ f32x4 sck[C::NSK * C::TT * C::SCP / 4];   // int4: key scales [slot][row][chunk]
+  __shared__ f32x4 scv[C::NSV * C::TT * C::SCP / 4];   // int4: value scales [slot][row][chunk]
   __shared__ double theta[C::DH / 2];             // rotation frequencies in turns per token
   __shared__ f32x4 stpc[C::DH / 8], stps[C::DH / 8];   // rotation by 32 tokens per frequency
   __shared__ int wsum[C::NW];
@@ -257,7 +267,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
         const s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         // move the operand into the AGPR file once; it stays there
         op_t v = __builtin_bit_cast(op_t, both), av;
-        asm volatile("" : "=a"(av) : "0"(v));
+        if constexpr (C::BREG_V) av = v; else asm volatile("" : "=a"(av) : "0"(v));
         breg[kc][mt] = av;
       }
     };
@@ -285,7 +295,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
 #pragma unroll
         for (int mt = 0; mt < C::NMT; ++mt) {
           op_t z = op_t{}, az;
-          asm volatile("" : "=a"(az) : "0"(z));
+          if constexpr (C::BREG_V) az = z; else asm volatile("" : "=a"(az) : "0"(z));
           breg[kc][mt] = az;
         }
       }
@@ -299,6 +309,13 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       for (int i = tid; i < NZ; i += C::NT) {
         uint4* dst = i < C::NKB * C::TILEB / 16 ? zkb + i : zvb + (i - C::NKB * C::TILEB / 16);
         *dst = uint4{0u, 0u, 0u, 0u};
+      }
+      // (and the scales of chunks past a group's ranks: zero codes times a
+      // zero scale)
+      constexpr int NZS = (C::NSK + C::NSV) * C::TT * C::SCP / 4;
+      for (int i = tid; i < NZS; i += C::NT) {
+        f32x4* dst = i < C::NSK * C::TT * C::SCP / 4 ? sck + i : scv + (i - C::NSK * C::TT * C::SCP / 4);
+        *dst = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       wait_lgkm0();
       barrier();
@@ -447,9 +464,13 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // for tid < 32 nchk (row tid / nchk), values for the next 32 nchv lanes.
   // Its 16 bytes of codes and its scale are loaded into registers one step
   // ahead (rows past the history repeat its last row); the expansion writes
-  // the chunk's four 16-byte pieces into the tile ring in the swizzled layout
-  // the DMA would have produced, zero past the rank and on rows past the
-  // history.
+  // the chunk's codes, as exact 16-bit integers, in four 16-byte pieces into
+  // the tile ring in the swizzled layout the DMA would have produced (zero
+  // past the rank and on rows past the history), and its scale, as fp32,
+  // into the ring's scale array (zero on rows past the history).  The scale
+  // is applied after the matrix products: to each 32-deep partial of the key
+  // rebuild, and to P before P z_v, so the latent code * scale enters the
+  // attention exactly.
   const int nchk = pk >> 4, nchv = pv >> 4;
   const int magk = (65536 + nchk - 1) / nchk, magv = (65536 + nchv - 1) / nchv;
   struct Q4It { int row, ch; bool isv, ok; };
@@ -494,11 +515,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     uint8_t* rowp = it.isv ? (uint8_t*)zvb + (m % C::NVB) * C::TILEB + it.row * C::ROWB
                            : (uint8_t*)zkb + (m % C::NKB) * C::TILEB + it.row * C::ROWB;
     const int swz = it.isv ? 2 * vswz(it.row) : (it.row & 15);
-    const float sf = (float)__builtin_bit_cast(_Float16, (unsigned short)q4s);
+    const float sf = it.row < nvalid ? (float)__builtin_bit_cast(_Float16, (unsigned short)q4s) : 0.f;
+    float* scrow = it.isv ? (float*)scv + ((m % C::NVB) * C::TT + it.row) * C::SCP
+                          : (float*)sck + ((m % C::NKB) * C::TT + it.row) * C::SCP;
+    scrow[it.ch] = sf;
     const unsigned cw[4] = {q4c[0], q4c[1], q4c[2], q4c[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 o = expand8<LT>(cw[i], sf);
+      uint4 o = codes8<LT>(cw[i]);
       const int nv8 = tail - 8 * i;
       if (nv8 < 8) {
         o.x &= q4_mask(0, nv8);
@@ -583,9 +607,17 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // than kTau: the common path forms P with the current maximum and flags
   // such lanes; softmax_fix (rare) then raises the maxima, rescales and forms
   // P again.
-  struct Sm { float x0, x1, p0, p1; bool up; };
+  // (int4: v0, v1 = the value scales of this wave's 32-rank chunk at the
+  // lane's two tokens; P enters P z_v multiplied by them)
+  struct Sm { float x0, x1, p0, p1, v0, v1; bool up; };
+  auto vscales = [&](int m, Sm& sm, const Lane& ln) __attribute__((always_inline)) {
+    const float* sv = (const float*)scv + ((m % C::NVB) * C::TT + ln.s) * C::SCP + w;
+    sm.v0 = sv[0];
+    sm.v1 = sv[16 * C::SCP];
+  };
   auto softmax_fast = [&](int m, int info, Sm& sm, const Lane& ln) __attribute__((always_inline)) {
     const int s = ln.s;
+    if constexpr (C::Q4) vscales(m, sm, ln);
     const float* sq = &sp[m & 1][ln.kq][0][0];
     const float x0 = sq[s] + sq[C::TT + s];
     const float x1 = sq[16 + s] + sq[C::TT + 16 + s];
@@ -595,7 +627,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     sm.up = fmaxf(sm.x0, sm.x1) > m_run + kTau;
     sm.p0 = __builtin_amdgcn_exp2f(sm.x0 - m_run);
     sm.p1 = __builtin_amdgcn_exp2f(sm.x1 - m_run);
-    store_p(ln, sm.p0, sm.p1);
+    if constexpr (C::Q4) store_p(ln, sm.p0 * sm.v0, sm.p1 * sm.v1); else store_p(ln, sm.p0, sm.p1);
   };
   auto softmax_fix = [&](Sm& sm, const Lane& ln) __attribute__((always_inline)) {
     const float tmax = max16(fmaxf(sm.x0, sm.x1));
@@ -612,7 +644,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     }
     sm.p0 = __builtin_amdgcn_exp2f(sm.x0 - mnew);
     sm.p1 = __builtin_amdgcn_exp2f(sm.x1 - mnew);
-    store_p(ln, sm.p0, sm.p1);
+    if constexpr (C::Q4) store_p(ln, sm.p0 * sm.v0, sm.p1 * sm.v1); else store_p(ln, sm.p0, sm.p1);
   };
 
   // P z_v of the previous tile on MFMA: A = P (rows 0-3 = heads, rows 4-15
@@ -765,6 +797,48 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     }
     Sm sm;
     f32x4 k0[C::NMT], k1[C::NMT];
+    float part0 = 0.f;    // int4: partial score of tokens 0-15 (window A)
+    // int4: the key of token t is sum_c s_c(t) T_c(t), T_c the 32-deep MFMA
+    // partial of chunk c over the integer codes.  RoPE and the query dot are
+    // linear in the key, so the query is rotated back to the token instead,
+    // u = R(t)^T q (per lane: its eight frequency pairs), each partial T_c is
+    // dotted with u as soon as it is ready, and the dot is scaled by s_c(t):
+    // no key is held, and code * scale enters exactly.
+    f32x4 kt[C::NMT];
+    float ks[2];          // scales of chunks kc - 1 and kc at this lane's token
+    f32x4 qu[C::NMT];     // rotated query: M-tile 2j pairs with 2j + 1
+    const float* ksrow = (const float*)sck + (n % C::NKB) * C::TT * C::SCP + ln.s * C::SCP;
+    auto qrot = [&](const f32x4 (&cj)[2], const f32x4 (&sj)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float cv = cj[j][e], sv = sj[j][e];
+          qu[2 * j][e] = fmaf(qlo[j][e], cv, qhi[j][e] * sv);
+          qu[2 * j + 1][e] = fmaf(qhi[j][e], cv, -(qlo[j][e] * sv));
+        }
+    };
+    // the dot of chunk kc's partial (M-tile mt) with the rotated query; after
+    // the last M-tile of a chunk, scaled into the half-tile's partial score
+    float dc = 0.f;
+    auto kdot = [&](float& part, int kc, int mt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dc = fmaf(qu[mt][e], kt[mt][e], dc);
+      if (mt == C::NMT - 1) {
+        part = kc == 0 ? ks[0] * dc : fmaf(ks[kc & 1], dc, part);
+        dc = 0.f;
+      }
+    };
+    // The partials' MFMAs do not depend on each other: an empty asm that
+    // takes the running dot and hands on the next MFMA's B_k operand keeps
+    // each MFMA after the dot of the partial whose registers it reuses (else
+    // they are all issued first and their results pile up in registers).
+    auto kord = [&](int kc, int mt, float part) __attribute__((always_inline)) {
+      if constexpr (C::BREG_V)
+        asm volatile("" : "+v"(breg[kc][mt]) : "v"(dc), "v"(part));
+      else
+        asm volatile("" : "+a"(breg[kc][mt]) : "v"(dc), "v"(part));
+    };
     const uint8_t* zk = (const uint8_t*)zkb + (n % C::NKB) * C::TILEB;
     const int kbase = kbase_of(ln);
     // key operand of chunk kc of token half u (read two chunks ahead)
@@ -781,7 +855,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     if (HAVE) {
       // window A: keys of tokens 0-15 beside the softmax of the previous tile
       // and the angle table of the next one
-      float ra0, rb0, ra1, rb1;
+      float ra0, rb0, ra1, rb1, ps0, ps1;
       f32x4 apc, aps, arc, ars, oc, os;
       LT h0, h1, g0, g1;
       const float* sq = &sp[(n - 1) & 1][ln.kq][0][0];
@@ -796,6 +870,9 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
             ra1 = sq[16 + ln.s];
             rb1 = sq[C::TT + 16 + ln.s];
           }
+          if constexpr (C::Q4) {
+            if (slot == 2) vscales(n - 1, sm, ln);
+          }
           if (slot == 8) { sm.x0 = ra0 + rb0; sm.x1 = ra1 + rb1; }
           if (slot == 9) {
             sm.x0 = ln.s < nv ? sm.x0 : -INFINITY;
@@ -804,9 +881,19 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
           if (slot == 10) sm.up = fmaxf(sm.x0, sm.x1) > m_run + kTau;
           if (slot == 11) sm.p0 = __builtin_amdgcn_exp2f(sm.x0 - m_run);
           if (slot == 12) sm.p1 = __builtin_amdgcn_exp2f(sm.x1 - m_run);
-          if (slot == 13) { h0 = (LT)sm.p0; h1 = (LT)sm.p1; }
-          if (slot == 14) g0 = (LT)(sm.p0 - (float)h0);
-          if (slot == 15) g1 = (LT)(sm.p1 - (float)h1);
+          if (slot == 13) {
+            if constexpr (C::Q4) {
+              ps0 = sm.p0 * sm.v0;
+              ps1 = sm.p1 * sm.v1;
+            } else {
+              ps0 = sm.p0;
+              ps1 = sm.p1;
+            }
+            h0 = (LT)ps0;
+            h1 = (LT)ps1;
+          }
+          if (slot == 14) g0 = (LT)(ps0 - (float)h0);
+          if (slot == 15) g1 = (LT)(ps1 - (float)h1);
           if (slot == 16) {
             pt[ln.s] = h0;
             pt[16 + ln.s] = h1;
@@ -832,26 +919,48 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
           angc[((n + 1) & 1) * (C::TT * C::AP) + ae] = oc;
           angs[((n + 1) & 1) * (C::TT * C::AP) + ae] = os;
         }
-        // angles of tokens 0-15 for window B
         if constexpr (C::Q4) {
           if (slot == 3 && load2) q4_load(q4p, ln);
         } else {
           if (slot % 6 == 3 && slot / 6 < 2 * C::NDT && load2) dma_piece(dq, slot / 6);
         }
-        if (slot == 24) ca0[0] = tc[0];
-        if (slot == 25) sa0[0] = ts[0];
-        if (slot == 26) ca0[1] = tc[4];
-        if (slot == 27) sa0[1] = ts[4];
+        // angles of tokens 0-15 for window B (int4: of tokens 16-31, window
+        // A took its own before the chunks)
+        if constexpr (C::Q4) {
+          if (slot == 24) ca1[0] = tc[16 * C::AP];
+          if (slot == 25) sa1[0] = ts[16 * C::AP];
+          if (slot == 26) ca1[1] = tc[16 * C::AP + 4];
+          if (slot == 27) sa1[1] = ts[16 * C::AP + 4];
+        } else {
+          if (slot == 24) ca0[0] = tc[0];
+          if (slot == 25) sa0[0] = ts[0];
+          if (slot == 26) ca0[1] = tc[4];
+          if (slot == 27) sa0[1] = ts[4];
+        }
       };
       op_t bq[3];
       bq[0] = bload(0, 0);
       bq[1] = bload(0, 1);
+      if constexpr (C::Q4) {
+        ca0[0] = tc[0];
+        sa0[0] = ts[0];
+        ca0[1] = tc[4];
+        sa0[1] = ts[4];
+        qrot(ca0, sa0);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kc = 0; kc < C::NKC; ++kc) {
 #pragma unroll
         for (int mt = 0; mt < C::NMT; ++mt) {
-          k0[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k0[mt]);
+          if constexpr (C::Q4) {
+            if (kc > 0) kdot(part0, kc - 1, mt);
+            kord(kc, mt, part0);
+            kt[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], f32x4{0.f, 0.f, 0.f, 0.f});
+            if (mt == 0) ks[kc & 1] = ksrow[0 * C::SCP + kc];
+          } else {
+            k0[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k0[mt]);
+          }
           if (mt == 0 && kc + 2 < C::NKC) bq[(kc + 2) % 3] = bload(0, kc + 2);
           work(4 * kc + mt);
           __builtin_amdgcn_sched_barrier(0);
@@ -860,6 +969,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       // (ranks below 256: the pieces laid out for chunks NKC..7 follow)
 #pragma unroll
       for (int slot = 4 * C::NKC; slot < 32; ++slot) work(slot);
+      if constexpr (C::Q4) {
+#pragma unroll
+        for (int mt = 0; mt < C::NMT; ++mt) kdot(part0, C::NKC - 1, mt);
+      }
     } else if (HAD) {
       softmax_fast(n - 1, i_p, sm, ln);
     }
@@ -869,20 +982,25 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     }
     if (HAVE) {
       // window B: keys of tokens 16-31 beside RoPE + dot of tokens 0-15
+      // (int4: tokens 0-15 were scored in window A; the query is rotated to
+      // tokens 16-31 and their chunk partials are scored here)
       float part = 0.f;
       float klo, khi;
       op_t bq[3];
       bq[0] = bload(1, 0);
       bq[1] = bload(1, 1);
+      if constexpr (C::Q4) qrot(ca1, sa1);
       // piece (kc, mt): RoPE and query dot of rotation pair kc of tokens
       // 0-15 (eight pairs per lane), and the angles of tokens 16-31
       auto wb = [&](int kc, int mt) __attribute__((always_inline)) {
         const int j = kc >> 2, e = kc & 3;
-        const float ka = k0[2 * j][e], kb = k0[2 * j + 1][e];
-        if (mt == 0) klo = ka * ca0[j][e] - kb * sa0[j][e];
-        if (mt == 1) khi = ka * sa0[j][e] + kb * ca0[j][e];
-        if (mt == 2) part = fmaf(qhi[j][e], khi, fmaf(qlo[j][e], klo, part));
-        if (mt == 3 && kc >= 4) {
+        if constexpr (!C::Q4) {
+          const float ka = k0[2 * j][e], kb = k0[2 * j + 1][e];
+          if (mt == 0) klo = ka * ca0[j][e] - kb * sa0[j][e];
+          if (mt == 1) khi = ka * sa0[j][e] + kb * ca0[j][e];
+          if (mt == 2) part = fmaf(qhi[j][e], khi, fmaf(qlo[j][e], klo, part));
+        }
+        if (!C::Q4 && mt == 3 && kc >= 4) {
           if (kc == 4) ca1[0] = tc[16 * C::AP];
           if (kc == 5) sa1[0] = ts[16 * C::AP];
           if (kc == 6) ca1[1] = tc[16 * C::AP + 4];
@@ -894,7 +1012,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       for (int kc = 0; kc < C::NKC; ++kc) {
 #pragma unroll
         for (int mt = 0; mt < C::NMT; ++mt) {
-          k1[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k1[mt]);
+          if constexpr (C::Q4) {
+            if (kc > 0) kdot(part, kc - 1, mt);
+            kord(kc, mt, part);
+            kt[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], f32x4{0.f, 0.f, 0.f, 0.f});
+            if (mt == 0) ks[kc & 1] = ksrow[16 * C::SCP + kc];
+          } else {
+            k1[mt] = mfma16x16x32(breg[kc][mt], bq[kc % 3], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : k1[mt]);
+          }
           wb(kc, mt);
           if (mt == 3 && kc + 2 < C::NKC) bq[(kc + 2) % 3] = bload(1, kc + 2);
           __builtin_amdgcn_sched_barrier(0);
@@ -905,9 +1030,18 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
 #pragma unroll
         for (int mt = 0; mt < C::NMT; ++mt) wb(kc, mt);
       }
-      const float sc0 = rows4_sum(part);
-      if (HAD) pv_mfma((const uint8_t*)zvb + ((n - 1) % C::NVB) * C::TILEB, ln);
-      const float sc1 = rows4_sum(rope_part(k1, ca1, sa1, 0, 2, 0.f));
+      float sc0, sc1;
+      if constexpr (C::Q4) {
+#pragma unroll
+        for (int mt = 0; mt < C::NMT; ++mt) kdot(part, C::NKC - 1, mt);
+        sc0 = rows4_sum(part0);
+        if (HAD) pv_mfma((const uint8_t*)zvb + ((n - 1) % C::NVB) * C::TILEB, ln);
+        sc1 = rows4_sum(part);
+      } else {
+        sc0 = rows4_sum(part);
+        if (HAD) pv_mfma((const uint8_t*)zvb + ((n - 1) % C::NVB) * C::TILEB, ln);
+        sc1 = rows4_sum(rope_part(k1, ca1, sa1, 0, 2, 0.f));
+      }
       if (ln.kq == 0) {
         sp[n & 1][c][hf][ln.s] = sc0;
         sp[n & 1][c][hf][16 + ln.s] = sc1;

@@ -30,7 +30,26 @@ struct DequantParams {
   const int* seq_lens;      // device [batch], clamped to [0, max_len]; NULL: every length is max_len
   int batch, G, max_len, max_nch;   // (max_len * max_nch^2 < 2^32)
   int n_sides;              // 2: keys and values; 1: side[0] only
+  // 0: each 32-element chunk becomes 32 values code * scale rounded once to
+  //    the 16-bit format (64 bytes per chunk);
+  // 1: each chunk becomes 64 values, the 16-bit rounding hi of code * scale
+  //    followed by the remainder lo = code * scale - hi (128 bytes per chunk);
+  //    hi + lo is code * scale exactly (the product has at most 14
+  //    significant bits, hi keeps 11 (fp16) or 8 (bf16) of them and lo the rest)
+  int split;
 };
+// Factor rows for split expansions: B'[64 c + i] = B'[64 c + 32 + i] =
+// B[32 c + i] for 32 c + i < r, zero rows for the rest (r' = 64 ceil(r/32)),
+// so that hi z B' + lo z B' = (hi + lo) B.  One launch covers keys and values
+// of every group.
+struct DupParams {
+  const void* src[2];       // B_k, B_v (concatenated per group, [r_j][w])
+  void* dst[2];             // B'_k, B'_v ([r'_j][w] per group)
+  int64_t soff[2][kDqMaxGroups], doff[2][kDqMaxGroups];   // element offsets of group j
+  int rank[2][kDqMaxGroups];
+  int G, w, max_rows;       // max_rows = max r'_j
+};
+hipError_t launch_dup_factor(const DupParams& p, hipStream_t stream);
 // out_dtype: 1 = fp16, 2 = bf16
 hipError_t launch_dequant(int out_dtype, const DequantParams& p, hipStream_t stream);
 }  // namespace palu

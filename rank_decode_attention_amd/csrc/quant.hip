@@ -87,7 +87,9 @@ static hipError_t launch_q(const void* z, int64_t n_rows, int r, int64_t stride,
 // before any is used.  The decode consumes the int4 latent
 // z_hat = code * scale (PALU page, section "Rollout", route C: quantization
 // on top of the low-rank cache); the product is exact in fp32 and is
-// rounded once, to the activation format that the decode's MFMA takes.
+// rounded once to the 16-bit format, or (split mode, what the decode
+// attends over on shapes that do not read the codes directly) kept exactly
+// as a hi + lo pair of 16-bit values.
 template <class T>
 __global__ void __launch_bounds__(256) palu_dequant_kernel(const DequantParams p) {
   const int b = blockIdx.y / p.G, j = blockIdx.y - b * p.G;
@@ -101,7 +103,7 @@ __global__ void __launch_bounds__(256) palu_dequant_kernel(const DequantParams p
   if (c0 >= n_chunks) return;
   const uint8_t* codes = d.codes + b * d.seq_c + d.goff_c[j] + 4 * (l & 3);
   const uint8_t* scales = d.scales + b * d.seq_s + d.goff_s[j];
-  uint8_t* out = d.out + b * d.seq_o + d.goff_o[j] + 16 * (l & 3);
+  uint8_t* out = d.out + b * d.seq_o + d.goff_o[j];
   unsigned w[4];
   float s[4];
 #pragma unroll
@@ -113,22 +115,59 @@ __global__ void __launch_bounds__(256) palu_dequant_kernel(const DequantParams p
     }
   }
   const int tail = d.rank[j] & 31;   // elements in a row's last chunk (0: a whole chunk)
+  auto mask_tail = [&](uint4& o, unsigned c) {
+    if (tail != 0 && c - __umulhi(c, d.magic[j]) * nch == nch - 1) {
+      // the row's last chunk: zero from the rank on (elements e0 .. e0+7 here)
+      const int nv = tail - 8 * (l & 3);
+      unsigned* h = (unsigned*)&o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        h[q] &= (2 * q < nv ? 0xFFFFu : 0u) | (2 * q + 1 < nv ? 0xFFFF0000u : 0u);
+    }
+  };
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const unsigned c = c0 + 16 * k;
     if (c < n_chunks) {
-      uint4 o = expand8<T>(w[k], s[k]);
-      if (tail != 0 && c - __umulhi(c, d.magic[j]) * nch == nch - 1) {
-        // the row's last chunk: zero from the rank on (elements e0 .. e0+7 here)
-        const int nv = tail - 8 * (l & 3);
-        unsigned* h = (unsigned*)&o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          h[q] &= (2 * q < nv ? 0xFFFFu : 0u) | (2 * q + 1 < nv ? 0xFFFF0000u : 0u);
+      if (p.split) {
+        uint4 hi, lo;
+        split8<T>(w[k], s[k], hi, lo);
+        mask_tail(hi, c);
+        mask_tail(lo, c);
+        // (the out pointer already holds this lane's 16-byte piece offset)
+        *(uint4*)(out + 128 * (int64_t)c + 16 * (l & 3)) = hi;
+        *(uint4*)(out + 128 * (int64_t)c + 64 + 16 * (l & 3)) = lo;
+      } else {
+        uint4 o = expand8<T>(w[k], s[k]);
+        mask_tail(o, c);
+        *(uint4*)(out + 64 * (int64_t)c + 16 * (l & 3)) = o;
       }
-      *(uint4*)(out + 64 * (int64_t)c) = o;
     }
   }
+}
+
+// One thread per 8 columns of one row of B': rows 64 c + i and 64 c + 32 + i
+// both copy row 32 c + i of B (zero past the rank).
+template <class T>
+__global__ void __launch_bounds__(256) palu_dup_factor_kernel(const DupParams p) {
+  const int side = blockIdx.z, j = blockIdx.y;
+  const int r = p.rank[side][j], rr = 64 * cdiv(r, 32);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = p.w / 8;                      // 8-column pieces per row
+  if (idx >= (int64_t)rr * cpr) return;
+  const int row = (int)(idx / cpr), col = (int)(idx - (int64_t)row * cpr) * 8;
+  const int src_row = 32 * (row / 64) + (row & 31);
+  uint4 v = uint4{0u, 0u, 0u, 0u};
+  if (src_row < r) v = *(const uint4*)((const T*)p.src[side] + p.soff[side][j] + (int64_t)src_row * p.w + col);
+  *(uint4*)((T*)p.dst[side] + p.doff[side][j] + (int64_t)row * p.w + col) = v;
+}
+
+hipError_t launch_dup_factor(const DupParams& p, hipStream_t stream) {
+  if (p.G == 0) return hipSuccess;
+  if (p.w % 8 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)cdiv64((int64_t)p.max_rows * (p.w / 8), 256), (unsigned)p.G, 2);
+  hipLaunchKernelGGL(palu_dup_factor_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant(int out_dtype, const DequantParams& p, hipStream_t stream) {

@@ -233,12 +233,19 @@ def half_ulp(ref: np.ndarray, fmt: str) -> np.ndarray:
     return 0.5 * 2.0 ** (np.floor(np.log2(mag)) - _ULP_BITS[fmt])
 
 
+# every comparison of the session: (what, fmt, elements, max_abs, max |err| / allowance, rel, rel / rtol),
+# written out by tests/conftest.py when PALU_PARITY_SUMMARY names a file
+RESULTS: List[Tuple[str, str, int, float, float, float, float]] = []
+
+
 def compare(gpu: np.ndarray, ref: np.ndarray, fmt: str, what: str = "") -> Dict[str, float]:
     atol, rtol = TOL[fmt]
     err = np.abs(gpu - ref)
     allow = atol + (half_ulp(ref, fmt) if fmt != "f32" else 0.0)
     rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
     stats = dict(max_abs=float(err.max()) if err.size else 0.0, rel=rel)
+    used = float((err / allow).max()) if err.size else 0.0
+    RESULTS.append((what, fmt, int(err.size), stats["max_abs"], used, rel, rel / rtol))
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     bad = err > allow
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond tolerance, max_abs={stats['max_abs']:.3e}"

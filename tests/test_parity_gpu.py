@@ -32,13 +32,19 @@ SMALL = [
     ("gqa_norope_small", _small("gqa_norope", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
     ("7b_f16_gqa_shape", PI.scaled("gqa_rope", latent="f16", act="f16", batch=2, max_len=96,
                                    fixed_lengths=(96, 50)), None),
-    # int4 latents: expanded to 16-bit rows (rank rounded up to 32), then the
-    # MHA-group kernel (rank 154 -> 160, 100 -> 128) or the split kernel
+    # int4 latents (the oracle attends over the exact code * scale): the MHA
+    # head-group kernel reads the codes itself (rank 154 -> 5 chunks, 100 ->
+    # 4); other shapes attend over exact hi/lo 16-bit rows of twice the rank
+    # rounded up to 32 (no RoPE: the absorbed-query kernel; GQA: the split
+    # kernel, ranks up to 160)
     ("int4_small", _small("int4", batch=3, max_len=300, fixed_lengths=(300, 1, 77)), None),
     ("int4_bf16_r100", _small("int4", act="bf16", rank=100, batch=2, max_len=200, fixed_lengths=(200, 65)), None),
     ("int4_empty_seq", _small("int4", batch=3, max_len=100, fixed_lengths=(0, 100, 33)), None),
     ("int4_norope", _small("int4", use_rope=False, batch=2, max_len=160, fixed_lengths=(160, 3)), None),
-    ("int4_gqa", _small("gqa_rope", latent="i4", batch=3, max_len=200, fixed_lengths=(200, 33, 129)), None),
+    ("int4_norope_bf16", _small("int4", act="bf16", use_rope=False, batch=2, max_len=130, fixed_lengths=(130, 64)),
+     None),
+    ("int4_gqa", _small("gqa_rope", latent="i4", rank_choices=(64, 128, 160), batch=3, max_len=200,
+                        fixed_lengths=(200, 33, 129)), None),
     # MHA-group kernel with fewer than 8 key chunks, and per-group ranks
     ("7b_r160", _small("llama2_7b", rank=160, batch=2, max_len=300, fixed_lengths=(300, 77)), None),
     ("long_r128_bf16", _small("long_b4", rank=128, batch=2, max_len=400), None),
@@ -65,6 +71,27 @@ def test_small_full_compare(name, wl, _):
     ref = oracle_decode(case)
     stats = compare(gpu, ref, wl.act, name)
     print(name, stats)
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_int4_exact_latents(act, q_scale):
+    """int4 decode against the oracle's exact code * scale, flat and peaked
+    attention, fp16 and bf16 activations (rounding the latent to bf16 first
+    would miss the bar under peaked attention by an order of magnitude)."""
+    wl = _small("int4", act=act, batch=3, max_len=260, fixed_lengths=(260, 97, 32), name=f"int4_{act}")
+    case = build_decode_case(wl, q_scale=q_scale)
+    stats = compare(run_decode(case), oracle_decode(case), wl.act, f"int4 {act} q x{q_scale:g}")
+    print(f"int4 {act} q x{q_scale:g}", stats)
+
+
+def test_int4_unsupported_rank():
+    """Shapes attended over hi/lo rows need twice the rank (rounded up to 32)
+    within a kernel's capacity (GQA: 320): rank 192 is refused."""
+    import rank_decode_attention_amd as R
+    wl = _small("gqa_rope", latent="i4", rank=192, batch=1, max_len=64)
+    with pytest.raises(R.PaluError, match="hi/lo"):
+        build_decode_case(wl)
 
 
 @pytest.mark.parametrize("q_scale", [8.0])
@@ -102,18 +129,22 @@ def test_batch_zero_is_noop():
 
 
 def test_int4_workspace_and_errors():
-    """int4 latents on shapes the MHA kernel covers are expanded inside it (no
-    extra workspace); elsewhere (here: no RoPE) the 16-bit expansion (rank
-    rounded up to 32, keys and values) is added to the workspace.  Missing
-    scales are an argument error."""
+    """int4 latents on shapes the MHA kernel covers are read by it directly (no
+    extra workspace); elsewhere (here: no RoPE) the workspace adds the exact
+    hi/lo expansion (rank 160 -> 320, keys and values) and the factors with
+    duplicated rows.  Missing scales are an argument error."""
     import rank_decode_attention_amd as R
     batch, max_len = 3, 100
     wl = _small("int4", batch=batch, max_len=max_len)
-    dense = batch * max_len * 8 * 2 * 160
-    for rope, extra in ((True, 0), (False, 2 * ((dense + 255) // 256 * 256))):
+    r256 = lambda x: (x + 255) // 256 * 256
+    dense = batch * max_len * 8 * 2 * 320
+    dup = 8 * 320 * 512 * 2
+    for rope, extra in ((True, 0), (False, 2 * r256(dense) + 2 * r256(dup))):
         f = R.AttnDesc(32, 32, 128, 8, [154] * 8, use_rope=rope, latent_dtype="f16", act_dtype="f16")
+        f2 = R.AttnDesc(32, 32, 128, 8, [320] * 8, use_rope=rope, latent_dtype="f16", act_dtype="f16")
         i = R.AttnDesc(32, 32, 128, 8, [154] * 8, use_rope=rope, latent_dtype="i4", act_dtype="f16")
-        assert R.decode_workspace_bytes(i, batch, max_len) == R.decode_workspace_bytes(f, batch, max_len) + extra
+        base = R.decode_workspace_bytes(f if rope else f2, batch, max_len)
+        assert R.decode_workspace_bytes(i, batch, max_len) == base + extra
     case = build_decode_case(wl)
     c = case["cache"]
     no_scales = R.LatentCache(c.zk, c.zv, None, None, c.max_len)
@@ -130,25 +161,31 @@ def test_deterministic():
     assert np.array_equal(a, b)
 
 
-FULL = [
-    ("llama2_7b", [(0, 0), (0, 31), (7, 13), (15, 22)]),
-    ("long_b1", [(0, 0), (0, 17)]),
-    ("long_b4", [(0, 3), (3, 28)]),
-    ("gqa_rope", [(0, 0), (5, 9), (31, 31)]),
-    ("gqa_norope", [(0, 1), (17, 20), (31, 30)]),
-    ("int4", [(0, 0), (3, 17), (7, 31)]),
-]
+def _one_head_per_group(wl):
+    """One query head of every (sequence, head-group): head b mod (H/G) of
+    group g, so that the sampled heads vary inside the groups too."""
+    per = wl.n_q_heads // wl.n_groups
+    return [(b, g * per + (b + g) % per) for b in range(wl.batch) for g in range(wl.n_groups)]
 
 
-@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled(name, heads):
+FULL = [("llama2_7b", 1.0), ("llama2_7b", 8.0), ("long_b1", 1.0), ("long_b4", 1.0), ("gqa_rope", 1.0),
+        ("gqa_rope", 8.0), ("gqa_norope", 1.0), ("int4", 1.0), ("int4", 8.0)]
+
+
+@pytest.mark.parametrize("name,q_scale", FULL, ids=[f"{n}_q{s:g}" for n, s in FULL])
+def test_full_size_sampled(name, q_scale):
+    """The workloads at full size, in the benchmark's launch configuration:
+    one query head of every (sequence, group) against the oracle (which
+    rebuilds that group's keys and values in fp64), flat and peaked (q x 8)
+    attention."""
     wl = PI.workload(name)
-    case = build_decode_case(wl)
+    case = build_decode_case(wl, q_scale=q_scale)
     gpu = run_decode(case)
+    heads = _one_head_per_group(wl)
     ref = oracle_decode(case, heads=heads)
     bs = [b for b, _ in heads]
     hs = [h for _, h in heads]
-    stats = compare(gpu[bs, hs], ref[bs, hs], wl.act, name)
+    stats = compare(gpu[bs, hs], ref[bs, hs], wl.act, f"{name} full q x{q_scale:g}")
     assert np.all(np.isfinite(gpu))
     print(name, stats)
 
