@@ -274,6 +274,33 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
                              const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the device scratch array behind palu_decode_attn_noalloc (one
+ * per GPU the library runs on, held until the process ends). */
+#define PALU_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * palu_decode_attn_noalloc - palu_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, kernels and
+ * results as palu_decode_attn on a contiguous cache, with the workspace
+ * taken from a library-owned static device array of
+ * PALU_NOALLOC_SCRATCH_BYTES instead of an argument.  It calls no hipMalloc,
+ * hipFree or other allocating routine; its first call on a device resolves
+ * that device's copy of the array (hipGetSymbolAddress).
+ *   arguments  as palu_decode_attn, without workspace / workspace_bytes
+ * No part of the scratch needs to start at zero: every call writes what it
+ * reads.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind, so calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ * Errors: as palu_decode_attn, plus UNSUPPORTED when the call needs more
+ * than PALU_NOALLOC_SCRATCH_BYTES of workspace (palu_decode_workspace_bytes
+ * tells; e.g. I4 caches on shapes that are expanded into the workspace).
+ */
+palu_status palu_decode_attn_noalloc(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
+                                     const void* B_k, const void* B_v, const int32_t* seq_lens,
+                                     const int32_t* q_pos, int32_t batch, float sm_scale, void* out,
+                                     hipStream_t stream);
+
 /*
  * palu_decode_attn_paged - palu_decode_attn over a paged latent cache: the
  * same computation and results, with row t of sequence b read from page

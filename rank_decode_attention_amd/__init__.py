@@ -20,7 +20,7 @@ __all__ = [
     "latent_bytes", "latent_offset", "row_pitch", "scale_pitch", "alloc_cache", "fill_cache",
     "fill_paged_cache", "decode_workspace_bytes", "palu_decode_attn", "palu_decode_attn_paged", "palu_project",
     "palu_project_paged", "palu_quant_latent", "palu_dequant_latent", "palu_profile_events",
-    "chunk_workspace_bytes", "palu_decode_attn_chunk",
+    "chunk_workspace_bytes", "palu_decode_attn_chunk", "palu_decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,8 @@ def load():
     lib.palu_decode_workspace_bytes.restype = sz
     lib.palu_decode_attn.argtypes = [D, vp, C, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.palu_decode_attn.restype = ctypes.c_int
+    lib.palu_decode_attn_noalloc.argtypes = [D, vp, C, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp]
+    lib.palu_decode_attn_noalloc.restype = ctypes.c_int
     lib.palu_decode_attn_paged.argtypes = [D, vp, ctypes.POINTER(_PagedCache), vp, vp, vp, vp, i32, ctypes.c_float,
                                            vp, vp, sz, vp]
     lib.palu_decode_attn_paged.restype = ctypes.c_int
@@ -301,6 +303,20 @@ def palu_decode_attn(desc: AttnDesc, q, cache: LatentCache, B_k, B_v, seq_lens, 
                                    seq_lens.data_ptr(), None if q_pos is None else q_pos.data_ptr(),
                                    int(q.shape[0]), float(sm_scale), out.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def palu_decode_attn_noalloc(desc: AttnDesc, q, cache: LatentCache, B_k, B_v, seq_lens, q_pos, sm_scale: float, out,
+                             stream=None):
+    """One decode step without a workspace argument (palu_decode_attn_noalloc):
+    the library's static device scratch of NOALLOC_SCRATCH_BYTES is used."""
+    c = cache.c()
+    _check(load().palu_decode_attn_noalloc(desc.ref(), q.data_ptr(), ctypes.byref(c), B_k.data_ptr(), B_v.data_ptr(),
+                                           seq_lens.data_ptr(), None if q_pos is None else q_pos.data_ptr(),
+                                           int(q.shape[0]), float(sm_scale), out.data_ptr(), _stream(stream)))
+
+
+# bytes of that scratch (PALU_NOALLOC_SCRATCH_BYTES in include/palu.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def palu_decode_attn_paged(desc: AttnDesc, q, cache: PagedCache, B_k, B_v, seq_lens, q_pos, sm_scale: float, out,

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "decode.h"
 #include "project.h"
@@ -508,6 +509,32 @@ palu_status decode_impl(const palu_attn_desc* desc, const void* q, const CacheVi
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
 }
+// Scratch of palu_decode_attn_noalloc: one array per GPU, held by the loaded
+// code object until the process ends.  Host code never uses the array's
+// name as a device address: each device's address is resolved once with
+// hipGetSymbolAddress (with that device current) and kept here.
+static __device__ __align__(256) uint8_t scratch[PALU_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+palu_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PALU_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(PALU_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PALU_OK;
+}
+
 // workspace of a chunk call: virtual lengths, positions and block-table rows,
 // then the decode workspace of the virtual batch
 size_t chunk_front_bytes(int64_t vbatch, int max_pages) {
@@ -657,6 +684,25 @@ palu_status palu_decode_attn(const palu_attn_desc* desc, const void* q, const pa
   if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
   const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
   return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+palu_status palu_decode_attn_noalloc(const palu_attn_desc* desc, const void* q, const palu_latent_cache* cache,
+                                     const void* B_k, const void* B_v, const int32_t* seq_lens, const int32_t* q_pos,
+                                     int32_t batch, float sm_scale, void* out, hipStream_t stream) {
+  if (!cache) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+  DecodePlan pl;
+  palu_status s = plan_decode(desc, batch, cache->max_len, &pl);
+  if (s != PALU_OK) return s;
+  if (pl.total > PALU_NOALLOC_SCRATCH_BYTES)
+    return fail(PALU_ERR_UNSUPPORTED, "this call needs %zu bytes of scratch, above the %zu bytes of the no-alloc entry point",
+                pl.total, (size_t)PALU_NOALLOC_SCRATCH_BYTES);
+  if (batch == 0) return ok();   // nothing is read or written
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != PALU_OK) return s;
+  const CacheView v{cache->zk, cache->zv, cache->sk, cache->sv, cache->max_len, cache->max_len, nullptr, 0, 0};
+  return decode_impl(desc, q, &v, B_k, B_v, seq_lens, q_pos, batch, sm_scale, out, ws, PALU_NOALLOC_SCRATCH_BYTES,
                      stream);
 }
 
