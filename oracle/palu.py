@@ -44,6 +44,15 @@ Readings where the pages are silent:
   nearest even, into fp16 or bf16 (int4_rows16); the decode never reads
   them.
 
+* low-rank-aware int4 (rotated chunks): before quantisation every full
+  32-element chunk of a latent row is rotated by the Sylvester Hadamard
+  matrix H (entries +-1, H H^T = 32 I): z' = z H; a trailing partial chunk
+  is left as is.  The rotation is folded into the factors, A' = A H and
+  B' = H B / 32, so that z' B' = z B and the decode is the plain definition
+  over z' and B'.  The quantiser decides codes on z' formed in binary32 by
+  the fast Walsh-Hadamard butterflies (stages h = 1, 2, 4, 8, 16; pairs
+  (i, i + h) become (a + b, a - b)), the precision the kernel uses.
+
 Pins (tests/test_oracle_pins.py): standard attention through
 torch.nn.functional.scaled_dot_product_attention (float64, CPU) in the
 identity case A = W, B = I; the absorbed-query and fused-value forms for
@@ -63,6 +72,7 @@ __all__ = [
     "upcast", "rope_theta", "rope", "reconstruct", "attend", "attend_partial", "merge_partials",
     "decode_attention", "project", "quant_int4", "pack_int4", "unpack_int4", "dequant_int4",
     "chunks_per_row", "round_to", "int4_latent", "int4_rows16", "chunk_attention",
+    "hadamard", "rotate_chunks", "rotate_chunks_f32", "fold_rotation", "quant_int4_rotated",
 ]
 
 QUANT_GROUP = 32
@@ -298,3 +308,71 @@ def dequant_int4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     r = codes.shape[-1]
     s = np.repeat(np.asarray(scales, dtype=np.float64), QUANT_GROUP, axis=-1)[..., :r]
     return codes.astype(np.float64) * s
+
+
+# ------------------------------------------------------------------ low-rank-aware int4 (rotated chunks)
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1:
+    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]."""
+    assert n >= 1 and n & (n - 1) == 0, "order must be a power of two"
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def _full_chunks(r: int) -> int:
+    return r // QUANT_GROUP
+
+
+def rotate_chunks(z: np.ndarray) -> np.ndarray:
+    """z' = z H on every full 32-element chunk of the last axis (a trailing
+    partial chunk is left as is), in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    out = z.copy()
+    H = hadamard(QUANT_GROUP)
+    for c in range(_full_chunks(z.shape[-1])):
+        sl = slice(c * QUANT_GROUP, (c + 1) * QUANT_GROUP)
+        out[..., sl] = z[..., sl] @ H
+    return out
+
+
+def rotate_chunks_f32(z: np.ndarray) -> np.ndarray:
+    """The same rotation formed in binary32 by the fast Walsh-Hadamard
+    butterflies: for h = 1, 2, 4, 8, 16, within blocks of 2h elements the pair
+    (i, i + h) becomes (a + b, a - b), every sum rounded to binary32."""
+    x = np.array(z, dtype=np.float32)
+    for c in range(_full_chunks(x.shape[-1])):
+        base = c * QUANT_GROUP
+        h = 1
+        while h < QUANT_GROUP:
+            for start in range(base, base + QUANT_GROUP, 2 * h):
+                a = x[..., start:start + h].copy()
+                b = x[..., start + h:start + 2 * h].copy()
+                x[..., start:start + h] = a + b
+                x[..., start + h:start + 2 * h] = a - b
+            h *= 2
+    return x
+
+
+def fold_rotation(A: np.ndarray, B: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Factors for rotated latents: A' = A Hbd, B' = Hbd B / 32 (Hbd: H on
+    each full 32-row block, identity on a trailing partial block), so that
+    (x A') B' = x A B; fp64."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    r = A.shape[1]
+    assert B.shape[0] == r
+    H = hadamard(QUANT_GROUP)
+    A2, B2 = A.copy(), B.copy()
+    for c in range(_full_chunks(r)):
+        sl = slice(c * QUANT_GROUP, (c + 1) * QUANT_GROUP)
+        A2[:, sl] = A[:, sl] @ H
+        B2[sl] = H @ B[sl] / QUANT_GROUP
+    return A2, B2
+
+
+def quant_int4_rotated(z: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Low-rank-aware int4: rotate the full chunks in binary32, then the
+    plain symmetric int4 quantisation of the rotated row."""
+    return quant_int4(rotate_chunks_f32(z))

@@ -419,6 +419,54 @@ def pin_int4_decode_golden():
     np.testing.assert_allclose(out[0, 0], want, rtol=0, atol=1e-14)
 
 
+def pin_hadamard_rotation():
+    """Rotated-chunk int4 (low-rank-aware reading): the Hadamard matrix against
+    the library routine (scipy.linalg.hadamard), H H^T = 32 I; the binary32
+    butterflies equal the matrix product exactly on integer rows (sums of
+    small integers are exact in binary32) and within the binary32 bound on
+    real rows; a trailing partial chunk is not rotated; the folded factors
+    leave z B unchanged (fp64)."""
+    import scipy.linalg
+    for n in (1, 2, 4, 8, 16, 32, 64):
+        assert np.array_equal(O.hadamard(n), scipy.linalg.hadamard(n).astype(np.float64))
+    H = O.hadamard(32)
+    assert np.array_equal(H @ H.T, 32 * np.eye(32))
+    rng = np.random.default_rng(31)
+    zi = rng.integers(-50, 50, size=(40, 70)).astype(np.float32)          # 2 full chunks + 6
+    want = zi.astype(np.float64).copy()
+    want[:, :32] = zi[:, :32] @ scipy.linalg.hadamard(32)
+    want[:, 32:64] = zi[:, 32:64] @ scipy.linalg.hadamard(32)
+    assert np.array_equal(O.rotate_chunks(zi), want)
+    assert np.array_equal(O.rotate_chunks_f32(zi).astype(np.float64), want)
+    zr = rng.standard_normal((40, 70)).astype(np.float32)
+    ref = O.rotate_chunks(zr)
+    bound = 5 * 2.0 ** -24 * np.repeat(np.abs(zr[:, :64]).reshape(40, 2, 32).sum(-1), 32, axis=1)
+    assert np.all(np.abs(O.rotate_chunks_f32(zr)[:, :64] - ref[:, :64]) <= bound)
+    assert np.array_equal(O.rotate_chunks_f32(zr)[:, 64:], zr[:, 64:])
+    # fold: (x A') B' = x A B for ranks with and without a partial chunk
+    for r in (64, 70, 154):
+        x = rng.standard_normal((5, 48))
+        A = rng.standard_normal((48, r))
+        B = rng.standard_normal((r, 24))
+        A2, B2 = O.fold_rotation(A, B)
+        assert np.allclose((x @ A2) @ B2, (x @ A) @ B, rtol=0, atol=1e-11)
+        assert np.allclose(x @ A2, O.rotate_chunks(x @ A), rtol=0, atol=1e-11)
+
+
+def pin_hadamard_hand_worked():
+    """Order 4 by hand: H_4 = [[1,1,1,1],[1,-1,1,-1],[1,1,-1,-1],[1,-1,-1,1]];
+    the row [1, 2, 3, 4] rotates to [10, -2, -4, 0].  A 32-chunk holding a
+    single 8 at position 5 rotates to 8 times row 5 of H_32 (entries +-8)."""
+    assert np.array_equal(O.hadamard(4), np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]]))
+    assert (np.array([1.0, 2, 3, 4]) @ O.hadamard(4)).tolist() == [10, -2, -4, 0]
+    z = np.zeros((1, 32), np.float32)
+    z[0, 5] = 8.0
+    got = O.rotate_chunks_f32(z)[0]
+    # row 5 of the Sylvester matrix: entry (5, j) = (-1)^popcount(5 & j)
+    want = [8.0 * (-1) ** bin(5 & j).count("1") for j in range(32)]
+    assert got.tolist() == want
+
+
 def pin_chunk_attention():
     """Chunk attention: q_len = 1 is the decode step; later latents do not
     reach earlier queries; in the identity case A = W, B = I it equals
@@ -455,7 +503,7 @@ def pin_chunk_attention():
 PINS = [pin_absorbed_and_fused_value, pin_mpmath_bruteforce, pin_softmax_closed_forms, pin_rope, pin_gqa,
         pin_split_merge, pin_golden_decode, pin_rope_closed_form_d2, pin_project, pin_int4_golden,
         pin_int4_properties, pin_upcast, pin_round_to, pin_int4_latent, pin_int4_rows16, pin_int4_decode_golden,
-        pin_chunk_attention]
+        pin_chunk_attention, pin_hadamard_rotation, pin_hadamard_hand_worked]
 
 
 @pytest.mark.parametrize("use_rope", [False, True])
@@ -525,6 +573,18 @@ def _int4_latent_rounded_f16(packed, scales, r):
     return O.round_to(O.dequant_int4(O.unpack_int4(packed, r), scales), "f16")
 
 
+def _butterfly_sign_swapped(z):
+    x = O.__dict__["_orig_rot32"](z)
+    # (b - a) instead of (a - b) in the last stage: the upper half changes sign
+    x[..., 16:32] = -x[..., 16:32]
+    return x
+
+
+def _fold_without_scale(A, B):
+    A2, B2 = O.__dict__["_orig_fold"](A, B)
+    return A2, B2 * 32
+
+
 def _unpack_nibbles_swapped(packed, r):
     p = np.asarray(packed, dtype=np.uint8)
     return O.__dict__["_orig_unpack"](((p << 4) | (p >> 4)).astype(np.uint8), r)
@@ -542,6 +602,8 @@ MUTANTS = [
     ("round_to", _round_f16_as_bf16),
     ("unpack_int4", _unpack_nibbles_swapped),
     ("int4_latent", _int4_latent_rounded_f16),
+    ("rotate_chunks_f32", _butterfly_sign_swapped),
+    ("fold_rotation", _fold_without_scale),
 ]
 
 
@@ -553,6 +615,8 @@ def test_planted_mistakes(name, mutant, monkeypatch):
     monkeypatch.setitem(O.__dict__, "_orig_quant", O.quant_int4)
     monkeypatch.setitem(O.__dict__, "_orig_round", O.round_to)
     monkeypatch.setitem(O.__dict__, "_orig_unpack", O.unpack_int4)
+    monkeypatch.setitem(O.__dict__, "_orig_rot32", O.rotate_chunks_f32)
+    monkeypatch.setitem(O.__dict__, "_orig_fold", O.fold_rotation)
     monkeypatch.setattr(O, name, mutant)
     caught = False
     for pin in [lambda: pin_identity_vs_sdpa(True), lambda: pin_identity_vs_sdpa(False)] + PINS:
