@@ -164,6 +164,31 @@ palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows,
                               int64_t z_row_stride, void* codes, void* scales, hipStream_t stream);
 
 /*
+ * palu_quant_latent_rotated - low-rank-aware int4 quantisation (arXiv
+ * 2407.21118v2 abstract: a low-rank-aware quantization enhancement; PALU
+ * page, section "Rollout", route C: quantization on top of the low-rank
+ * cache).  The pages do not define the enhancement; this library's reading:
+ * latents of an SVD-style factorisation carry very unequal energy per
+ * channel, and a chunk's amax/7 step is set by its largest channel, so
+ * every full 32-element chunk is first rotated by the Sylvester Hadamard
+ * matrix H of order 32 (entries +-1, H H^T = 32 I), which spreads a chunk's
+ * energy over all its elements: the row z becomes z' = z H chunk by chunk
+ * (a trailing partial chunk is left as is), and z' is quantised exactly as
+ * by palu_quant_latent.  The rotation is undone in the factors, not in the
+ * decode: with A' = A H and B' = H B / 32 per full 32-row block (identity
+ * on a partial block), z' B' = z B, so palu_decode_attn over the rotated
+ * int4 cache with B_k', B_v' attends as over the unrotated latents; a prefill
+ * through palu_project with A' writes z' directly (then use
+ * palu_quant_latent, or an I4 cache, on it).  z H is formed in binary32 by
+ * the fast Walsh-Hadamard butterflies (stages h = 1, 2, 4, 8, 16; the pair
+ * (i, i + h) becomes (a + b, a - b)); codes and scales are then decided as in
+ * palu_quant_latent.
+ * Arguments, layouts and errors: as palu_quant_latent.
+ */
+palu_status palu_quant_latent_rotated(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r,
+                                      int64_t z_row_stride, void* codes, void* scales, hipStream_t stream);
+
+/*
  * palu_dequant_latent - int4 latent rows to 16-bit rows (quantization on top
  * of the low-rank cache: PALU page, section "Rollout", route C), for callers
  * that want a 16-bit copy of an int4 cache.  The values are rounded to the

@@ -21,6 +21,7 @@ __all__ = [
     "fill_paged_cache", "decode_workspace_bytes", "palu_decode_attn", "palu_decode_attn_paged", "palu_project",
     "palu_project_paged", "palu_quant_latent", "palu_dequant_latent", "palu_profile_events",
     "chunk_workspace_bytes", "palu_decode_attn_chunk", "palu_decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "palu_quant_latent_rotated",
 ]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +86,8 @@ def load():
     lib.palu_latent_offset.restype = i64
     lib.palu_quant_latent.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp]
     lib.palu_quant_latent.restype = ctypes.c_int
+    lib.palu_quant_latent_rotated.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp]
+    lib.palu_quant_latent_rotated.restype = ctypes.c_int
     lib.palu_dequant_latent.argtypes = [vp, vp, i64, i32, ctypes.c_int, vp, vp]
     lib.palu_dequant_latent.restype = ctypes.c_int
     lib.palu_project.argtypes = [D, vp, i32, i64, vp, C, i32, i32, vp]
@@ -370,6 +373,15 @@ def palu_dequant_latent(codes, scales, n_rows: int, r: int, out, stream=None):
     dt = {torch.float16: 1, torch.bfloat16: 2}[out.dtype]
     _check(load().palu_dequant_latent(codes.data_ptr(), scales.data_ptr(), int(n_rows), int(r), dt, out.data_ptr(),
                                       _stream(stream)))
+
+
+def palu_quant_latent_rotated(z, r: int, row_stride: int, codes, scales, stream=None):
+    """Low-rank-aware int4 quantisation (palu_quant_latent_rotated): every full
+    32-element chunk is rotated by the order-32 Hadamard matrix first."""
+    import torch
+    dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[z.dtype]
+    _check(load().palu_quant_latent_rotated(z.data_ptr(), dt, int(z.shape[0]), int(r), int(row_stride),
+                                            codes.data_ptr(), scales.data_ptr(), _stream(stream)))
 
 
 def palu_quant_latent(z, r: int, row_stride: int, codes, scales, stream=None):

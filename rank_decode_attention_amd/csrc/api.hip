@@ -624,6 +624,19 @@ palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows,
   return ok();
 }
 
+palu_status palu_quant_latent_rotated(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r,
+                                      int64_t z_row_stride, void* codes, void* scales, hipStream_t stream) {
+  if (n_rows < 0 || r <= 0 || z_row_stride < r) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r / z_row_stride");
+  if (z_dtype == PALU_I4) return fail(PALU_ERR_UNSUPPORTED, "input must be F32, F16 or BF16");
+  if (!valid_dtype(z_dtype)) return fail(PALU_ERR_INVALID_ARG, "invalid dtype");
+  if (n_rows == 0) return ok();
+  if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream, true);
+  if (e != hipSuccess) return hip_fail(e, "quantiser launch");
+  return ok();
+}
+
 palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n_rows, int32_t r,
                                 palu_dtype out_dtype, void* out, hipStream_t stream) {
   if (n_rows < 0 || r <= 0) return fail(PALU_ERR_INVALID_ARG, "bad n_rows / r");

@@ -4,9 +4,10 @@
 #include <hip/hip_runtime.h>
 
 namespace palu {
-// dtype: 0 = fp32, 1 = fp16, 2 = bf16 input rows
+// dtype: 0 = fp32, 1 = fp16, 2 = bf16 input rows; rotate: quantise z H on
+// every full 32-element chunk (H the Sylvester Hadamard matrix of order 32)
 hipError_t launch_quant(int dtype, const void* z, int64_t n_rows, int r, int64_t stride, void* codes,
-                        void* scales, hipStream_t stream);
+                        void* scales, hipStream_t stream, bool rotate = false);
 
 // Expansion of one layer's int4 latent cache (keys and values) into 16-bit
 // rows for the decode kernels: row t of (sequence b, group j) becomes

@@ -15,65 +15,150 @@
 
 namespace palu {
 
-// One thread per (row, 32-element chunk).  Stores 16 bytes of codes and one
-// binary16 scale.  The chunk's 32 loads are issued before any is used (the
-// index is clamped inside the row, values past the rank are dropped after).
+// Four lanes per (row, 32-element chunk), lane i of the quad owning
+// elements 8i .. 8i + 7, so that a wave's loads cover sixteen chunks of
+// contiguous row memory (one 16-byte load per lane where the piece is
+// aligned, 4-byte or element loads otherwise).  The chunk's amax is reduced
+// over the quad with DPP; every lane forms the same scale, quantises its 8
+// elements and stores their 4 bytes of codes (a chunk's 16 bytes are the
+// quad's 4 stores); lane 0 stores the scale.
 // code = rint(fl(z / s)) needs the correctly rounded binary32 quotient only
 // where it decides the rounding: t = z * fl(1 / s) lies within 1.5e-6 of
 // fl(z / s) for |t| < 8 (two roundings of relative size 2^-24 each), so
 // rint(t) is the code unless t is within 4e-6 of a half-integer, where the
 // exact quotient is formed; beyond |t| >= 8 both clamp to +-7.
 template <class T>
+__device__ __forceinline__ void load8(const T* p, int n, float (&v)[8]) {
+  const uintptr_t a = (uintptr_t)p;
+  if (n == 8 && (a & 15) == 0) {
+    const uint4 u = *(const uint4*)p;
+    const T* e = (const T*)&u;
+    if constexpr (sizeof(T) == 4) {
+      // (16 bytes hold 4 binary32 values: the second half is the next 16 bytes)
+      const uint4 u2 = *(const uint4*)(p + 4);
+      const T* e2 = (const T*)&u2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[i] = to_f32(e[i]); v[4 + i] = to_f32(e2[i]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = to_f32(e[i]);
+    }
+    return;
+  }
+  if (n == 8 && (a & 3) == 0) {
+    constexpr int PER = 4 / sizeof(T);          // elements per 32-bit word
+#pragma unroll
+    for (int k = 0; k < 8 / PER; ++k) {
+      const unsigned u = *(const unsigned*)(p + PER * k);
+      const T* e = (const T*)&u;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[PER * k + i] = to_f32(e[i]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = i < n ? to_f32(p[i]) : 0.f;
+}
+
+__device__ __forceinline__ int quant_code(float v, float sf, float inv) {
+  const float t = v * inv;
+  float qf = rintf(t);
+  if (fabsf(t) < 8.f && fabsf(fabsf(t - qf) - 0.5f) < 4e-6f) qf = rintf(__fdiv_rn(v, sf));
+  qf = fminf(fmaxf(qf, -7.f), 7.f);
+  return (int)qf;
+}
+
+// Rotated chunks (the low-rank-aware variant): before the amax, every full
+// 32-element chunk is replaced by z H (H the Sylvester Hadamard matrix of
+// order 32, entries +-1), formed by the fast Walsh-Hadamard butterflies in
+// binary32 - stages h = 1, 2, 4 inside a lane's 8 elements, h = 8 and 16
+// between the quad's lanes (DPP) - the pair (i, i + h) becoming
+// (a + b, a - b).  A trailing partial chunk is quantised as it is.
+__device__ __forceinline__ void fwht32(float (&v)[8], int qi) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  // h = 8: lanes qi and qi ^ 1; h = 16: lanes qi and qi ^ 2 (the lower lane
+  // holds a, the upper lane b)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = dpp<0xB1>(v[i]);
+    v[i] = (qi & 1) ? p - v[i] : v[i] + p;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = dpp<0x4E>(v[i]);
+    v[i] = (qi & 2) ? p - v[i] : v[i] + p;
+  }
+}
+
+template <class T, bool ROT>
 __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z, int64_t n_rows, int r,
                                                          int64_t stride, uint8_t* __restrict__ codes,
                                                          _Float16* __restrict__ scales) {
   const int nc = cdiv(r, 32);
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_rows * nc) return;
-  const int64_t row = idx / nc;
-  const int c = (int)(idx - row * nc);
-  const T* zr = z + row * stride + c * 32;
-  const int n = min(32, r - c * 32);
-  T raw[32];
+  const int qi = threadIdx.x & 3;
+  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2;   // chunk of this quad
+  const bool live = idx < n_rows * nc;
+  const int64_t row = live ? idx / nc : 0;
+  const int c = live ? (int)(idx - row * nc) : 0;
+  const int e0 = 32 * c + 8 * qi;               // this lane's first element in the row
+  int n = live ? r - e0 : 0;
+  n = n < 0 ? 0 : (n > 8 ? 8 : n);
+  float v[8];
+  load8<T>(z + row * stride + e0, n, v);
+  if constexpr (ROT) {
+    // (every lane of the wave runs the butterflies; chunks that are not full
+    // keep their values)
+    float w[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) raw[i] = zr[min(i, n - 1)];
-  float v[32];
+    for (int i = 0; i < 8; ++i) w[i] = v[i];
+    fwht32(w, qi);
+    if (32 * c + 32 <= r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = w[i];
+    }
+  }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = i < n ? to_f32(raw[i]) : 0.f;
-    amax = fmaxf(amax, fabsf(v[i]));
-  }
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // amax over the quad (the whole wave takes part; quads past the end carry zeros)
+  amax = fmaxf(amax, dpp<0xB1>(amax));
+  amax = fmaxf(amax, dpp<0x4E>(amax));
   const float s32 = __fdiv_rn(amax, 7.0f);
   const _Float16 s16 = (_Float16)s32;
   const float sf = (float)s16;
-  unsigned int words[4] = {0u, 0u, 0u, 0u};
+  unsigned word = 0u;   // element 8 qi + i in nibble i
   if (sf != 0.f) {
     const float inv = __fdiv_rn(1.0f, sf);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float t = v[i] * inv;
-      float qf = rintf(t);
-      if (fabsf(t) < 8.f && fabsf(fabsf(t - qf) - 0.5f) < 4e-6f) qf = rintf(__fdiv_rn(v[i], sf));
-      qf = fminf(fmaxf(qf, -7.f), 7.f);
-      const int q = i < n ? (int)qf : 0;
-      words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
+    for (int i = 0; i < 8; ++i) {
+      const int q = i < n ? quant_code(v[i], sf, inv) : 0;
+      word |= (unsigned)(q & 0xF) << (4 * i);
     }
   }
-  uint4 packed = make_uint4(words[0], words[1], words[2], words[3]);
-  *(uint4*)(codes + row * (int64_t)(16 * nc) + 16 * c) = packed;
-  scales[row * nc + c] = s16;
+  if (live) {
+    *(unsigned*)(codes + row * (int64_t)(16 * nc) + 16 * c + 4 * qi) = word;
+    if (qi == 0) scales[row * nc + c] = s16;
+  }
 }
 
-template <class T>
+template <class T, bool ROT>
 static hipError_t launch_q(const void* z, int64_t n_rows, int r, int64_t stride, void* codes, void* scales,
                            hipStream_t stream) {
   const int nc = cdiv(r, 32);
-  const int64_t work = n_rows * nc;
+  const int64_t work = n_rows * nc;     // chunks, 4 lanes each
   if (work == 0) return hipSuccess;
-  const int64_t blocks = cdiv64(work, 256);
-  hipLaunchKernelGGL(palu_quant_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, stream, (const T*)z, n_rows, r,
-                     stride, (uint8_t*)codes, (_Float16*)scales);
+  const int64_t blocks = cdiv64(work * 4, 256);
+  hipLaunchKernelGGL((palu_quant_kernel<T, ROT>), dim3((unsigned)blocks), dim3(256), 0, stream, (const T*)z, n_rows,
+                     r, stride, (uint8_t*)codes, (_Float16*)scales);
   return hipGetLastError();
 }
 
@@ -186,14 +271,21 @@ hipError_t launch_dequant(int out_dtype, const DequantParams& p, hipStream_t str
   return hipGetLastError();
 }
 
-hipError_t launch_quant(int dtype, const void* z, int64_t n_rows, int r, int64_t stride, void* codes,
-                        void* scales, hipStream_t stream) {
+template <bool ROT>
+static hipError_t launch_quant_r(int dtype, const void* z, int64_t n_rows, int r, int64_t stride, void* codes,
+                                 void* scales, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_q<float>(z, n_rows, r, stride, codes, scales, stream);
-    case 1: return launch_q<_Float16>(z, n_rows, r, stride, codes, scales, stream);
-    case 2: return launch_q<__bf16>(z, n_rows, r, stride, codes, scales, stream);
+    case 0: return launch_q<float, ROT>(z, n_rows, r, stride, codes, scales, stream);
+    case 1: return launch_q<_Float16, ROT>(z, n_rows, r, stride, codes, scales, stream);
+    case 2: return launch_q<__bf16, ROT>(z, n_rows, r, stride, codes, scales, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant(int dtype, const void* z, int64_t n_rows, int r, int64_t stride, void* codes,
+                        void* scales, hipStream_t stream, bool rotate) {
+  return rotate ? launch_quant_r<true>(dtype, z, n_rows, r, stride, codes, scales, stream)
+                : launch_quant_r<false>(dtype, z, n_rows, r, stride, codes, scales, stream);
 }
 
 }  // namespace palu

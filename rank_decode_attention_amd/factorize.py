@@ -26,7 +26,7 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["factorize_group", "allocate_ranks", "factorize_layer"]
+__all__ = ["factorize_group", "allocate_ranks", "factorize_layer", "fold_rotation"]
 
 
 def factorize_group(W: np.ndarray, rank: int) -> Tuple[np.ndarray, np.ndarray, float]:
@@ -82,3 +82,30 @@ def factorize_layer(W_groups: Sequence[np.ndarray], ranks: Sequence[int]):
     ([A_j], [B_j], [relative error_j])."""
     out = [factorize_group(W, int(r)) for W, r in zip(W_groups, ranks)]
     return [o[0] for o in out], [o[1] for o in out], [o[2] for o in out]
+
+
+def _sylvester(n: int) -> np.ndarray:
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.vstack([np.hstack([H, H]), np.hstack([H, -H])])
+    return H
+
+
+def fold_rotation(A: np.ndarray, B: np.ndarray, chunk: int = 32) -> Tuple[np.ndarray, np.ndarray]:
+    """Factors for latents quantised with palu_quant_latent_rotated: A' = A H
+    and B' = H B / chunk on every full `chunk`-row block of the rank (H the
+    Sylvester Hadamard matrix, entries +-1, H H^T = chunk I; a trailing
+    partial block is left as is), so that (x A') B' = x A B and x A' is the
+    chunk-rotated latent.  float64."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    r = A.shape[1]
+    if B.shape[0] != r:
+        raise ValueError("A and B ranks differ")
+    H = _sylvester(chunk)
+    A2, B2 = A.copy(), B.copy()
+    for c in range(r // chunk):
+        sl = slice(c * chunk, (c + 1) * chunk)
+        A2[:, sl] = A[:, sl] @ H
+        B2[sl] = (H @ B[sl]) / chunk
+    return A2, B2
