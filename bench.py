@@ -242,6 +242,16 @@ def record_traffic(prof_dir: str, workload: str, copy_bytes: int, out_path: str 
            "fetch_scale": round(scale_r, 5), "write_scale": round(scale_w, 5),
            "how": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches), "
                   "each times the bytes-per-counted-byte of a plain copy of known size"}
+    # (optional third pass: read requests that leave the L2 for the memory
+    # side, in 32-byte units, scaled the same way; Infinity-Cache hits are
+    # among them)
+    if glob.glob(os.path.join(prof_dir, "DRAM_32B", "*counter_collection.csv")):
+        scale_d = copy_bytes / (32 * med([v for v in values("copy_DRAM_32B", "copyBuffer") if v > 1024]))
+        dr = med(values("DRAM_32B", "palu_decode")) * 32 * scale_d
+        rec["l2_to_memory_read_bytes_per_launch"] = int(round(dr))
+        rec["l2_to_memory_scale"] = round(scale_d, 5)
+        rec["how_l2_to_memory"] = ("rocprofv3 --pmc TCC_EA0_RDREQ_DRAM_32B_sum (32-byte read requests from the L2 "
+                                   "towards memory, median over dispatches), times the same calibration")
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -262,6 +272,7 @@ def cpu_baseline(wl, n_seq: int, reps: int = 3):
     import oracle
     import palu_inputs as PI
     cores = _blas_threads()
+    n_seq = min(n_seq, wl.batch)
     lens = PI.lengths(wl)[:n_seq]
 
     def lat(which, b, j):
