@@ -261,10 +261,18 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       for (int mt = 0; mt < C::NMT; ++mt) {
         const int j = mt >> 1, half = mt & 1;
         const int i0 = c * C::DH + half * (C::DH / 2) + 32 * hf + 16 * j;
-        // (the rank is a multiple of 32: every staged row is a real row of B_k)
+        // (16-bit latents: the rank is a multiple of 32, every staged row is a
+        // real row of B_k; int4: element i is rank 32 kc + 8 kq + i, set to
+        // zero past the rank, so that the codes the cache holds there, which
+        // the tiles carry unmasked, meet zero rows)
         const i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * W + i0 + 4 * (s & 3));
         const i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * W + i0 + 4 * (s & 3));
-        const s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (C::Q4) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (32 * kc + 8 * kq + i >= rk) both[i] = 0;
+        }
         // move the operand into the AGPR file once; it stays there
         op_t v = __builtin_bit_cast(op_t, both), av;
         if constexpr (C::BREG_V) av = v; else asm volatile("" : "=a"(av) : "0"(v));
@@ -465,12 +473,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // Its 16 bytes of codes and its scale are loaded into registers one step
   // ahead (rows past the history repeat its last row); the expansion writes
   // the chunk's codes, as exact 16-bit integers, in four 16-byte pieces into
-  // the tile ring in the swizzled layout the DMA would have produced (zero
-  // past the rank and on rows past the history), and its scale, as fp32,
-  // into the ring's scale array (zero on rows past the history).  The scale
-  // is applied after the matrix products: to each 32-deep partial of the key
-  // rebuild, and to P before P z_v, so the latent code * scale enters the
-  // attention exactly.
+  // the tile ring in the swizzled layout the DMA would have produced, and its
+  // scale, as fp32, into the ring's scale array (zero on rows past the
+  // history).  The scale is applied after the matrix products: to each
+  // 32-deep partial of the key rebuild, and to P before P z_v, so the latent
+  // code * scale enters the attention exactly.  No code is masked: past the
+  // rank the keys' codes meet zero rows of B_k and the values' land in
+  // accumulator ranks the merge never reads; on rows past the history the
+  // key scale is zero and P is zero.
   const int nchk = pk >> 4, nchv = pv >> 4;
   const int magk = (65536 + nchk - 1) / nchk, magv = (65536 + nchv - 1) / nchv;
   struct Q4It { int row, ch; bool isv, ok; };
@@ -504,14 +514,9 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       q4s = *(gs16)sb;
     }
   };
-  auto q4_mask = [](int q, int n) __attribute__((always_inline)) {
-    return (2 * q < n ? 0xFFFFu : 0u) | (2 * q + 1 < n ? 0xFFFF0000u : 0u);
-  };
   auto q4_expand = [&](int m, int nvalid, const Lane& ln) __attribute__((always_inline)) {
     const Q4It it = q4_item(ln);
     if (!it.ok) return;
-    // elements of this chunk below the rank (none on rows past the history)
-    const int tail = it.row < nvalid ? (it.isv ? p.rv[g] : rk) - 32 * it.ch : 0;
     uint8_t* rowp = it.isv ? (uint8_t*)zvb + (m % C::NVB) * C::TILEB + it.row * C::ROWB
                            : (uint8_t*)zkb + (m % C::NKB) * C::TILEB + it.row * C::ROWB;
     const int swz = it.isv ? 2 * vswz(it.row) : (it.row & 15);
@@ -522,15 +527,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     const unsigned cw[4] = {q4c[0], q4c[1], q4c[2], q4c[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 o = codes8<LT>(cw[i]);
-      const int nv8 = tail - 8 * i;
-      if (nv8 < 8) {
-        o.x &= q4_mask(0, nv8);
-        o.y &= q4_mask(1, nv8);
-        o.z &= q4_mask(2, nv8);
-        o.w &= q4_mask(3, nv8);
-      }
-      *(uint4*)(rowp + 16 * ((4 * it.ch + i) ^ swz)) = o;
+      *(uint4*)(rowp + 16 * ((4 * it.ch + i) ^ swz)) = codes8<LT>(cw[i]);
     }
   };
 
