@@ -205,3 +205,37 @@ def test_maximum_batch_and_groups():
                    fixed_lengths=(100, 37), rank_choices=(64, 128))
     case = build_decode_case(wl)
     compare(run_decode(case), oracle_decode(case), wl.act, "16 groups")
+
+
+@pytest.mark.parametrize("rope", [True, False], ids=["mha_fused", "expanded"])
+def test_int4_padding_and_rows_past_history_are_ignored(rope):
+    """int4 codes past the rank (the padding nibbles of a row's last 32-rank
+    chunk) and rows past each history (codes and scales) may hold anything:
+    the decode output is bit-identical to that of the clean cache (the fused
+    kernel carries the codes unmasked into the MFMAs, where the keys' meet
+    zero rows of B_k and the values' land in ranks the merge never reads), and
+    it still matches the oracle."""
+    import rank_decode_attention_amd as R
+    wl = _small("int4", use_rope=rope, batch=3, max_len=200, fixed_lengths=(200, 77, 33), name=f"int4_dirty_{rope}")
+    case = build_decode_case(wl)
+    clean = run_decode(case)
+    ranks = PI.ranks(wl)
+    rng = np.random.default_rng(123)
+
+    def rows(which, b, j):
+        L = int(case["lens"][b])
+        codes, scales = PI.latent_int4(wl, "k" if which == 0 else "v", b, j, n=max(L, 1))
+        r, nc = int(ranks[j]), scales.shape[1]
+        codes = np.concatenate([codes, rng.integers(0, 256, size=(wl.max_len - codes.shape[0], codes.shape[1]),
+                                                    dtype=np.uint8)])
+        scales = np.concatenate([scales, rng.uniform(-1e4, 1e4, size=(wl.max_len - scales.shape[0], nc))
+                                 .astype(np.float16)])
+        nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
+        nib[:, r:] = rng.integers(1, 16, size=(codes.shape[0], nib.shape[1] - r), dtype=np.uint8)
+        return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8), scales
+
+    dirty = dict(case)
+    dirty["cache"] = R.fill_cache(case["desc"], wl.batch, wl.max_len, rows)
+    gpu = run_decode(dirty)
+    assert np.array_equal(gpu, clean)
+    compare(gpu, oracle_decode(case), wl.act, f"int4 dirty padding rope={rope}")
