@@ -155,6 +155,55 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   const int kq = l >> 4, s = l & 15;
   const int g = blockIdx.x % p.G, pb = blockIdx.x / p.G;
   const int batch = p.batch;
+  // 16-bit latents: the first B_k chunks and the first tile's keys are
+  // requested before the tile prefix sums and the rest of the B_k staging,
+  // so that their latency overlaps that work (int4 tiles arrive through
+  // registers and keep the plain order)
+  constexpr bool EARLY = !C::Q4;
+  const int rk = p.rk[g];
+
+  // ---------------------------------------------------------------- B_k^T staging (LDS DMA) and gather into AGPRs
+  // M-tile mt = 2j + half: dims half*64 + 32*hf + 16j + (0..15), i.e. rotation
+  // frequencies 32*hf + 16j + (0..15) in both RoPE halves
+  op_t breg[C::NKC][C::NMT];
+  const LT* Bg = (const LT*)p.Bk + p.boff_k[g];   // [rk][4 * DH]
+  constexpr int W = C::NH * C::DH;
+  constexpr int NSI = C::STGB / (16 * C::NT);     // DMA instructions per wave per staged chunk (4)
+  uint8_t* const slots[3] = {(uint8_t*)zkb, (uint8_t*)zvb, (uint8_t*)zvb + C::STGB};
+  auto stage = [&](int slot, int kc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NSI; ++m) {
+      const int q = (m * C::NW + w) * 64 + l;     // 16-byte slot of the staged chunk
+      const int row = q >> 6, col = (q & 63) * 8;
+      const int kr = min(kc * 32 + row, rk - 1);
+      dma16(Bg + (int64_t)kr * W + col, lds_addr(slots[slot]) + 16u * ((m * C::NW + w) * 64));
+    }
+  };
+  auto gather = [&](int slot, int kc) __attribute__((always_inline)) {
+    const LT* sb = (const LT*)slots[slot];
+#pragma unroll
+    for (int mt = 0; mt < C::NMT; ++mt) {
+      const int j = mt >> 1, half = mt & 1;
+      const int i0 = c * C::DH + half * (C::DH / 2) + 32 * hf + 16 * j;
+      // (16-bit latents: the rank is a multiple of 32, every staged row is a
+      // real row of B_k; int4: element i is rank 32 kc + 8 kq + i, set to
+      // zero past the rank, so that the codes the cache holds there, which
+      // the tiles carry unmasked, meet zero rows)
+      const i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * W + i0 + 4 * (s & 3));
+      const i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * W + i0 + 4 * (s & 3));
+      s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (C::Q4) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (32 * kc + 8 * kq + i >= rk) both[i] = 0;
+      }
+      // move the operand into the AGPR file once; it stays there
+      op_t v = __builtin_bit_cast(op_t, both), av;
+      if constexpr (C::BREG_V) av = v; else asm volatile("" : "=a"(av) : "0"(v));
+      breg[kc][mt] = av;
+    }
+  };
+  const int nkc = cdiv(rk, 32);
 
   // ---------------------------------------------------------------- tile prefix sums
   // (no table is kept: block (0, 0) writes the tile starts of every sequence
@@ -177,6 +226,21 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       loc[i] = v;
       sacc += v;
     }
+    if constexpr (EARLY) {
+      stage(0, 0);
+      if (1 < nkc) stage(1, 1);
+    }
+    // (barriers that leave the B_k DMA in flight: LDS writes only)
+    auto sync_lds = [&]() __attribute__((always_inline)) {
+      if constexpr (EARLY) {
+        asm volatile("" ::: "memory");
+        wait_lgkm0();
+        barrier();
+        asm volatile("" ::: "memory");
+      } else {
+        __syncthreads();
+      }
+    };
     int incl = sacc;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -193,7 +257,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       ((float*)stpc)[tid] = cv;
       ((float*)stps)[tid] = sv;
     }
-    __syncthreads();
+    sync_lds();
     int all = 0, before = 0;
     for (int i = 0; i < C::NW; ++i) {
       all += wsum[i];
@@ -218,14 +282,16 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       run += loc[i];
     }
     if (hdr && tid == C::NT - 1) p.hdr[batch] = total;
-    __syncthreads();
+    sync_lds();
   }
   const int tpb = cdiv(total, p.P);
   const int n_begin = pb * tpb;
   const int n_end = min(total, n_begin + tpb);
-  if (n_begin >= n_end) return;
+  if (n_begin >= n_end) {
+    if constexpr (EARLY) wait_vmcnt<0>();   // (no LDS DMA outlives the block)
+    return;
+  }
 
-  const int rk = p.rk[g];
   const int pk = p.pk[g], pv = p.pv[g];
   const int cprk = pk >> 4, cprv = pv >> 4;
   const uint8_t* zk_seq = p.zk + p.goff_k[g];
@@ -237,98 +303,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   const int64_t sbk = p.seq_bytes_k, sbv = p.seq_bytes_v;
   const int h = g * C::NH + c;                    // query head of this wave (one per kv head)
 
-  // ---------------------------------------------------------------- B_k^T rows of this wave into AGPRs
-  // M-tile mt = 2j + half: dims half*64 + 32*hf + 16j + (0..15), i.e. rotation
-  // frequencies 32*hf + 16j + (0..15) in both RoPE halves
-  op_t breg[C::NKC][C::NMT];
-  {
-    const LT* Bg = (const LT*)p.Bk + p.boff_k[g];   // [rk][4 * DH]
-    constexpr int W = C::NH * C::DH;
-    constexpr int NSI = C::STGB / (16 * C::NT);     // DMA instructions per wave per staged chunk (4)
-    uint8_t* const slots[3] = {(uint8_t*)zkb, (uint8_t*)zvb, (uint8_t*)zvb + C::STGB};
-    auto stage = [&](int slot, int kc) __attribute__((always_inline)) {
-#pragma unroll
-      for (int m = 0; m < NSI; ++m) {
-        const int q = (m * C::NW + w) * 64 + l;     // 16-byte slot of the staged chunk
-        const int row = q >> 6, col = (q & 63) * 8;
-        const int kr = min(kc * 32 + row, rk - 1);
-        dma16(Bg + (int64_t)kr * W + col, lds_addr(slots[slot]) + 16u * ((m * C::NW + w) * 64));
-      }
-    };
-    auto gather = [&](int slot, int kc) __attribute__((always_inline)) {
-      const LT* sb = (const LT*)slots[slot];
-#pragma unroll
-      for (int mt = 0; mt < C::NMT; ++mt) {
-        const int j = mt >> 1, half = mt & 1;
-        const int i0 = c * C::DH + half * (C::DH / 2) + 32 * hf + 16 * j;
-        // (16-bit latents: the rank is a multiple of 32, every staged row is a
-        // real row of B_k; int4: element i is rank 32 kc + 8 kq + i, set to
-        // zero past the rank, so that the codes the cache holds there, which
-        // the tiles carry unmasked, meet zero rows)
-        const i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * W + i0 + 4 * (s & 3));
-        const i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * W + i0 + 4 * (s & 3));
-        s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if constexpr (C::Q4) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (32 * kc + 8 * kq + i >= rk) both[i] = 0;
-        }
-        // move the operand into the AGPR file once; it stays there
-        op_t v = __builtin_bit_cast(op_t, both), av;
-        if constexpr (C::BREG_V) av = v; else asm volatile("" : "=a"(av) : "0"(v));
-        breg[kc][mt] = av;
-      }
-    };
-    const int nkc = cdiv(rk, 32);
-    stage(0, 0);
-    if (1 < nkc) stage(1, 1);
-#pragma unroll
-    for (int kc = 0; kc < C::NKC; ++kc) {
-      if (kc < nkc) {
-        if (kc + 1 < nkc) wait_vmcnt<NSI>(); else wait_vmcnt<0>();
-        barrier();
-        if constexpr (C::NSTG == 3) {
-          if (kc + 2 < nkc) stage((kc + 2) % 3, kc + 2);
-          gather(kc % 3, kc);
-        } else {
-          // two slots: chunk kc + 2 goes into kc's slot once every wave has read it
-          gather(kc % 2, kc);
-          if (kc + 2 < nkc) {
-            wait_lgkm0();
-            barrier();
-            stage(kc % 2, kc + 2);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < C::NMT; ++mt) {
-          op_t z = op_t{}, az;
-          if constexpr (C::BREG_V) az = z; else asm volatile("" : "=a"(az) : "0"(z));
-          breg[kc][mt] = az;
-        }
-      }
-    }
-    wait_lgkm0();
-    barrier();   // staging buffers are free before the tile DMA overwrites them
-    if constexpr (C::Q4) {
-      // ring rows past a group's ranks are read by the MFMAs but never
-      // written by the expansion: they must hold finite values (zeros)
-      constexpr int NZ = (C::NKB + C::NVB) * C::TILEB / 16;
-      for (int i = tid; i < NZ; i += C::NT) {
-        uint4* dst = i < C::NKB * C::TILEB / 16 ? zkb + i : zvb + (i - C::NKB * C::TILEB / 16);
-        *dst = uint4{0u, 0u, 0u, 0u};
-      }
-      // (and the scales of chunks past a group's ranks: zero codes times a
-      // zero scale)
-      constexpr int NZS = (C::NSK + C::NSV) * C::TT * C::SCP / 4;
-      for (int i = tid; i < NZS; i += C::NT) {
-        f32x4* dst = i < C::NSK * C::TT * C::SCP / 4 ? sck + i : scv + (i - C::NSK * C::TT * C::SCP / 4);
-        *dst = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      wait_lgkm0();
-      barrier();
-    }
-  }
+  // key ring slot of tile m (16-bit latents: the block's first tile takes
+  // slot 2, the one slot the B_k staging leaves free)
+  const int koff = EARLY ? (2 - n_begin % C::NKB + C::NKB) % C::NKB : 0;
+  auto kslot = [&](int m) __attribute__((always_inline)) { return (m + koff) % C::NKB; };
 
   // ---------------------------------------------------------------- per-lane constants
   // DMA slots: instruction m of wave w fills 16-byte slots (m*NW + w)*64 + l of
@@ -446,7 +424,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     DmaPlan q;
     q.kb = d.kb;
     q.vb = d.vb;
-    q.kdst = lds_addr(zkb) + (unsigned)((m % C::NKB) * C::TILEB) + 16u * (w * 64);
+    q.kdst = lds_addr(zkb) + (unsigned)(kslot(m) * C::TILEB) + 16u * (w * 64);
     q.vdst = lds_addr(zvb) + (unsigned)((m % C::NVB) * C::TILEB) + 16u * (w * 64);
     const int lim = d.L - 1 - d.t0;
     int row, ck, cv;
@@ -575,6 +553,76 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     angc[(m & 1) * (C::TT * C::AP) + e] = oc;
     angs[(m & 1) * (C::TT * C::AP) + e] = os;
   };
+
+  // ---------------------------------------------------------------- the first tile's keys, B_k^T into AGPRs
+  if constexpr (EARLY) {
+    const Lane ln = lane();
+    dma_query(cd, n_begin, ln);   // (the block's first tile starts a segment)
+    const DmaPlan q = dma_plan(cd, n_begin, ln);
+#pragma unroll
+    for (int i = 0; i < C::NDT; ++i) dma_piece(q, i);
+  }
+  {
+    if constexpr (!EARLY) {
+      stage(0, 0);
+      if (1 < nkc) stage(1, 1);
+    }
+    // requests issued between chunk 1 and chunk 2: the first tile's query and keys
+    constexpr int NK = EARLY ? 1 + C::NDT : 0;
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc) {
+      if (kc < nkc) {
+        // chunk kc is in once at most the requests issued after it are outstanding
+        if (kc == 0) {
+          if (1 < nkc) wait_vmcnt<NSI + NK>(); else wait_vmcnt<NK>();
+        } else if (kc == 1) {
+          if (2 < nkc) wait_vmcnt<NK + NSI>(); else wait_vmcnt<NK>();
+        } else {
+          if (kc + 1 < nkc) wait_vmcnt<NSI>(); else wait_vmcnt<0>();
+        }
+        barrier();
+        if constexpr (C::NSTG == 3) {
+          if (kc + 2 < nkc) stage((kc + 2) % 3, kc + 2);
+          gather(kc % 3, kc);
+        } else {
+          // two slots: chunk kc + 2 goes into kc's slot once every wave has read it
+          gather(kc % 2, kc);
+          if (kc + 2 < nkc) {
+            wait_lgkm0();
+            barrier();
+            stage(kc % 2, kc + 2);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < C::NMT; ++mt) {
+          op_t z = op_t{}, az;
+          if constexpr (C::BREG_V) az = z; else asm volatile("" : "=a"(az) : "0"(z));
+          breg[kc][mt] = az;
+        }
+      }
+    }
+    wait_lgkm0();
+    barrier();   // staging buffers are free before the tile DMA overwrites them
+    if constexpr (C::Q4) {
+      // ring rows past a group's ranks are read by the MFMAs but never
+      // written by the expansion: they must hold finite values (zeros)
+      constexpr int NZ = (C::NKB + C::NVB) * C::TILEB / 16;
+      for (int i = tid; i < NZ; i += C::NT) {
+        uint4* dst = i < C::NKB * C::TILEB / 16 ? zkb + i : zvb + (i - C::NKB * C::TILEB / 16);
+        *dst = uint4{0u, 0u, 0u, 0u};
+      }
+      // (and the scales of chunks past a group's ranks: zero codes times a
+      // zero scale)
+      constexpr int NZS = (C::NSK + C::NSV) * C::TT * C::SCP / 4;
+      for (int i = tid; i < NZS; i += C::NT) {
+        f32x4* dst = i < C::NSK * C::TT * C::SCP / 4 ? sck + i : scv + (i - C::NSK * C::TT * C::SCP / 4);
+        *dst = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      wait_lgkm0();
+      barrier();
+    }
+  }
 
   // ---------------------------------------------------------------- running state
   // Softmax state and the P z_v accumulators cover all four heads in every
@@ -736,7 +784,17 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // MFMA beside RoPE + dot of tokens 16-31.
   // tiles n_begin and n_begin + 1 (info words of the current and next tile)
   int i_c = info_of(cd), i_a = 0, i_p = 0, t0_a = 0;
-  issue(cd, n_begin, i_c);
+  if constexpr (EARLY) {
+    // its query and keys are in (waited for with the last B_k chunk, or
+    // here); its values go out now
+    wait_vmcnt<0>();
+    const Lane ln = lane();
+    const DmaPlan q = dma_plan(cd, n_begin, ln);
+#pragma unroll
+    for (int i = C::NDT; i < 2 * C::NDT; ++i) dma_piece(q, i);
+  } else {
+    issue(cd, n_begin, i_c);
+  }
   if constexpr (C::Q4) q4_expand(n_begin, (i_c >> 16) & 63, lane());   // (waits for its loads)
   ang_seed(n_begin, cd.t0);
   if (n_begin + 1 < n_end) {
@@ -757,7 +815,11 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       wait_vmcnt<0>();   // the query of tile n; this lane's chunk of tile n + 1
       wait_lgkm0();      // the expansion of tile n (last step) is in LDS
     } else if (HAVE) {
-      if (n + 1 < n_end) wait_vmcnt<C::NDMA>(); else wait_vmcnt<0>();
+      // (16-bit latents, the first of several steps: its tile's query and keys
+      // were waited for before its values were requested, and the values are
+      // used one step later)
+      if (n + 1 >= n_end) wait_vmcnt<0>();
+      else if (HAD || !EARLY) wait_vmcnt<C::NDMA>();
     }
     barrier();   // tile n, angle table n and the partial scores of tile n - 1 are visible
     // tile n + 1 (if any) gets an exact angle table at a segment start and
@@ -836,7 +898,7 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       else
         asm volatile("" : "+a"(breg[kc][mt]) : "v"(dc), "v"(part));
     };
-    const uint8_t* zk = (const uint8_t*)zkb + (n % C::NKB) * C::TILEB;
+    const uint8_t* zk = (const uint8_t*)zkb + kslot(n) * C::TILEB;
     const int kbase = kbase_of(ln);
     // key operand of chunk kc of token half u (read two chunks ahead)
     auto bload = [&](int u, int kc) __attribute__((always_inline)) {
