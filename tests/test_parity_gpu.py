@@ -52,6 +52,12 @@ SMALL = [
                               fixed_lengths=(200, 45)), None),
     ("int4_mixed_ranks", _small("int4", rank=None, rank_choices=(70, 154, 200), batch=2, max_len=260,
                                 fixed_lengths=(260, 31)), None),
+    # ranks of one and two 32-rank chunks (the MHA kernel's B_k staging waits
+    # differ there), one-tile blocks and blocks of several tiles
+    ("7b_low_ranks", _small("llama2_7b", rank=None, rank_choices=(32, 64), batch=3, max_len=300,
+                            fixed_lengths=(300, 1, 77)), None),
+    ("7b_low_ranks_long", _small("llama2_7b", rank=None, rank_choices=(32, 64), batch=2, max_len=2048,
+                                 fixed_lengths=(2048, 1100)), None),
     # absorbed-query kernel (no RoPE, 16-bit): histories of at most 16 tokens
     # leave the second token half of every tile masked (its stream never sees
     # a token), an empty sequence, tile boundaries, odd ranks (chunk counts
