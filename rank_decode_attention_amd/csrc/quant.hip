@@ -16,9 +16,8 @@
 namespace palu {
 
 // Four lanes per (row, 32-element chunk), lane i of the quad owning
-// elements 8i .. 8i + 7, so that a wave's loads cover sixteen chunks of
-// contiguous row memory (one 16-byte load per lane where the piece is
-// aligned, 4-byte or element loads otherwise).  The chunk's amax is reduced
+// elements 8i .. 8i + 7, so that each of a wave's load rounds covers sixteen
+// chunks of contiguous row memory.  The chunk's amax is reduced
 // over the quad with DPP; every lane forms the same scale, quantises its 8
 // elements and stores their 4 bytes of codes (a chunk's 16 bytes are the
 // quad's 4 stores); lane 0 stores the scale.
@@ -26,47 +25,64 @@ namespace palu {
 // where it decides the rounding: t = z * fl(1 / s) lies within 1.5e-6 of
 // fl(z / s) for |t| < 8 (two roundings of relative size 2^-24 each), so
 // rint(t) is the code unless t is within 4e-6 of a half-integer, where the
-// exact quotient is formed; beyond |t| >= 8 both clamp to +-7.
+// exact quotient is formed (also beyond |t| >= 8, where both clamp to +-7).
+// A lane's 8 elements are read as the whole 16-byte blocks that hold them
+// (two for 16-bit elements, three for binary32; a block is loaded only if
+// it holds bytes of the piece, so no load leaves the pages of the row) and
+// realigned in registers; loads and realignment are separate steps so that
+// a wave issues several pieces' loads before it uses any.
 template <class T>
-__device__ __forceinline__ void load8(const T* p, int n, float (&v)[8]) {
+struct Piece {
+  static constexpr int NS = 8 * (int)sizeof(T) / 16 + 1;   // 16-byte blocks a piece can touch
+  uint4 seg[NS];
+  unsigned sh;                                           // the piece's byte offset in its first block
+};
+
+template <class T>
+__device__ __forceinline__ void piece_load(Piece<T>& pc, const T* p, int n) {
   const uintptr_t a = (uintptr_t)p;
-  if (n == 8 && (a & 15) == 0) {
-    const uint4 u = *(const uint4*)p;
-    const T* e = (const T*)&u;
-    if constexpr (sizeof(T) == 4) {
-      // (16 bytes hold 4 binary32 values: the second half is the next 16 bytes)
-      const uint4 u2 = *(const uint4*)(p + 4);
-      const T* e2 = (const T*)&u2;
+  const uintptr_t base = a & ~(uintptr_t)15;
+  const uintptr_t end = a + (uintptr_t)n * sizeof(T);     // one past the piece's last element
+  pc.sh = (unsigned)(a & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { v[i] = to_f32(e[i]); v[4 + i] = to_f32(e2[i]); }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = to_f32(e[i]);
-    }
-    return;
+  for (int i = 0; i < Piece<T>::NS; ++i) {
+    pc.seg[i] = uint4{0u, 0u, 0u, 0u};
+    if (n > 0 && base + 16 * i < end) pc.seg[i] = *(const uint4*)(base + 16 * i);
   }
-  if (n == 8 && (a & 3) == 0) {
-    constexpr int PER = 4 / sizeof(T);          // elements per 32-bit word
-#pragma unroll
-    for (int k = 0; k < 8 / PER; ++k) {
-      const unsigned u = *(const unsigned*)(p + PER * k);
-      const T* e = (const T*)&u;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) v[PER * k + i] = to_f32(e[i]);
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = i < n ? to_f32(p[i]) : 0.f;
 }
 
-__device__ __forceinline__ int quant_code(float v, float sf, float inv) {
-  const float t = v * inv;
-  float qf = rintf(t);
-  if (fabsf(t) < 8.f && fabsf(fabsf(t - qf) - 0.5f) < 4e-6f) qf = rintf(__fdiv_rn(v, sf));
-  qf = fminf(fmaxf(qf, -7.f), 7.f);
-  return (int)qf;
+template <class T>
+__device__ __forceinline__ void piece_values(const Piece<T>& pc, int n, float (&v)[8]) {
+  constexpr int ND = 2 * (int)sizeof(T);                 // dwords of 8 elements
+  unsigned d[4 * Piece<T>::NS];
+#pragma unroll
+  for (int i = 0; i < Piece<T>::NS; ++i) {
+    d[4 * i] = pc.seg[i].x;
+    d[4 * i + 1] = pc.seg[i].y;
+    d[4 * i + 2] = pc.seg[i].z;
+    d[4 * i + 3] = pc.seg[i].w;
+  }
+  const unsigned b = pc.sh & 3;
+  // dword offset sh / 4 in two bitwise selects (by 2, then by 1; written
+  // as masks so that the compiler keeps the words in registers instead of
+  // indexing an array)
+  const unsigned m2 = 0u - ((pc.sh >> 3) & 1u), m1 = 0u - ((pc.sh >> 2) & 1u);
+  unsigned f2[ND + 2], e[ND + 1];
+#pragma unroll
+  for (int j = 0; j < ND + 2; ++j) f2[j] = (d[j + 2] & m2) | (d[j] & ~m2);
+#pragma unroll
+  for (int j = 0; j <= ND; ++j) e[j] = (f2[j + 1] & m1) | (f2[j] & ~m1);
+  unsigned o[ND];
+#pragma unroll
+  for (int k = 0; k < ND; ++k) o[k] = __builtin_amdgcn_alignbyte(e[k + 1], e[k], b);
+  const T* el = (const T*)o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = i < n ? to_f32(el[i]) : 0.f;
 }
+
+// t within 4e-6 of a half-integer (|t - rint(t)| <= 1/2 always; beyond
+// |t| >= 8 the exact quotient clamps to the same code as t)
+__device__ __forceinline__ bool near_half(float t, float rt) { return fabsf(t - rt) > 0.5f - 4e-6f; }
 
 // Rotated chunks (the low-rank-aware variant): before the amax, every full
 // 32-element chunk is replaced by z H (H the Sylvester Hadamard matrix of
@@ -99,23 +115,15 @@ __device__ __forceinline__ void fwht32(float (&v)[8], int qi) {
   }
 }
 
-template <class T, bool ROT>
-__global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z, int64_t n_rows, int r,
-                                                         int64_t stride, uint8_t* __restrict__ codes,
-                                                         _Float16* __restrict__ scales) {
-  const int nc = cdiv(r, 32);
-  const int qi = threadIdx.x & 3;
-  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2;   // chunk of this quad
-  const bool live = idx < n_rows * nc;
-  const int64_t row = live ? idx / nc : 0;
-  const int c = live ? (int)(idx - row * nc) : 0;
-  const int e0 = 32 * c + 8 * qi;               // this lane's first element in the row
-  int n = live ? r - e0 : 0;
-  n = n < 0 ? 0 : (n > 8 ? 8 : n);
-  float v[8];
-  load8<T>(z + row * stride + e0, n, v);
+// One quad's chunk: its 8 elements v (zero past the row's rank),
+// rotated first for ROT where the chunk is full; the quad's amax, the
+// chunk's scale, this lane's 4 bytes of codes and (lane 0) the scale.  All
+// four lanes of the quad run it together (the amax crosses the quad by DPP).
+template <bool ROT>
+__device__ __forceinline__ void quant_quad(float (&v)[8], int qi, int c, int r, bool live, uint8_t* crow,
+                                           _Float16* srow) {
   if constexpr (ROT) {
-    // (every lane of the wave runs the butterflies; chunks that are not full
+    // (every lane of the quad runs the butterflies; chunks that are not full
     // keep their values)
     float w[8];
 #pragma unroll
@@ -129,7 +137,6 @@ __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // amax over the quad (the whole wave takes part; quads past the end carry zeros)
   amax = fmaxf(amax, dpp<0xB1>(amax));
   amax = fmaxf(amax, dpp<0x4E>(amax));
   const float s32 = __fdiv_rn(amax, 7.0f);
@@ -138,15 +145,78 @@ __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z
   unsigned word = 0u;   // element 8 qi + i in nibble i
   if (sf != 0.f) {
     const float inv = __fdiv_rn(1.0f, sf);
+    float qf[8];
+    bool near = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int q = i < n ? quant_code(v[i], sf, inv) : 0;
+      const float t = v[i] * inv;
+      qf[i] = rintf(t);
+      near |= near_half(t, qf[i]);
+    }
+    if (near) {   // (rare) the exact quotient where it decides the rounding
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = v[i] * inv;
+        if (near_half(t, rintf(t))) qf[i] = rintf(__fdiv_rn(v[i], sf));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // (elements past the row are zero: code 0)
+      const int q = (int)__builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
       word |= (unsigned)(q & 0xF) << (4 * i);
     }
   }
   if (live) {
-    *(unsigned*)(codes + row * (int64_t)(16 * nc) + 16 * c + 4 * qi) = word;
-    if (qi == 0) scales[row * nc + c] = s16;
+    *(unsigned*)(crow + 16 * c + 4 * qi) = word;
+    if (qi == 0) srow[c] = s16;
+  }
+}
+
+// A wave quantises 64 consecutive chunks (of the flattened (row, chunk)
+// list) in kQRounds rounds of 16: in round k, lane l takes quarter l % 4 of
+// chunk 16 k + l / 4.  Every round's loads are issued before any chunk is
+// quantised, so that a wave keeps 4 KB of rows in flight.
+constexpr int kQRounds = 4;
+
+template <class T, bool ROT>
+__global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z, int64_t n_rows, int r,
+                                                         int64_t stride, uint8_t* __restrict__ codes,
+                                                         _Float16* __restrict__ scales, unsigned nc_magic) {
+  const int nc = cdiv(r, 32);
+  const int qi = threadIdx.x & 3;
+  const int64_t work = n_rows * nc;
+  // the wave's first chunk and its (row, chunk) (wave-uniform); a lane's
+  // chunk in round k lies rel = c0 + 16 k + l / 4 chunks past the start of
+  // row row0, i.e. in row row0 + rel / nc (rel / nc by a multiply with
+  // ceil(2^32 / nc), exact for rel < 2^32 / nc; nc = 1 needs none)
+  const int64_t w0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * (16 * kQRounds);
+  const int64_t row0 = w0 / nc;
+  const int c0 = (int)(w0 - row0 * nc);
+  const T* zrow0 = z + row0 * stride;
+  uint8_t* crow0 = codes + row0 * (int64_t)(16 * nc);
+  _Float16* srow0 = scales + row0 * nc;
+  Piece<T> pc[kQRounds];
+  unsigned rrel[kQRounds];
+  int c[kQRounds], n[kQRounds];
+  bool live[kQRounds];
+#pragma unroll
+  for (int k = 0; k < kQRounds; ++k) {
+    const unsigned rel = (unsigned)c0 + 16u * k + ((threadIdx.x & 63) >> 2);
+    rrel[k] = nc == 1 ? rel : __umulhi(rel, nc_magic);
+    c[k] = (int)(rel - rrel[k] * (unsigned)nc);
+    live[k] = w0 + (int64_t)(16 * k) + ((threadIdx.x & 63) >> 2) < work;
+    const int e0 = 32 * c[k] + 8 * qi;            // this lane's first element in the row
+    int m = live[k] ? r - e0 : 0;
+    n[k] = m < 0 ? 0 : (m > 8 ? 8 : m);
+    piece_load<T>(pc[k], zrow0 + (int64_t)rrel[k] * stride + e0, n[k]);
+  }
+  // (the whole wave takes part; quads past the end carry zeros)
+#pragma unroll
+  for (int k = 0; k < kQRounds; ++k) {
+    float v[8];
+    piece_values<T>(pc[k], n[k], v);
+    quant_quad<ROT>(v, qi, c[k], r, live[k], crow0 + rrel[k] * (16u * nc), srow0 + rrel[k] * (unsigned)nc);
   }
 }
 
@@ -154,11 +224,12 @@ template <class T, bool ROT>
 static hipError_t launch_q(const void* z, int64_t n_rows, int r, int64_t stride, void* codes, void* scales,
                            hipStream_t stream) {
   const int nc = cdiv(r, 32);
-  const int64_t work = n_rows * nc;     // chunks, 4 lanes each
+  const int64_t work = n_rows * nc;     // chunks, 4 lanes each, 64 per wave
   if (work == 0) return hipSuccess;
-  const int64_t blocks = cdiv64(work * 4, 256);
+  const unsigned magic = (unsigned)((0xFFFFFFFFull / (unsigned)nc) + 1);   // ceil(2^32 / nc) for nc > 1
+  const int64_t blocks = cdiv64(work, 4 * 16 * kQRounds);
   hipLaunchKernelGGL((palu_quant_kernel<T, ROT>), dim3((unsigned)blocks), dim3(256), 0, stream, (const T*)z, n_rows,
-                     r, stride, (uint8_t*)codes, (_Float16*)scales);
+                     r, stride, (uint8_t*)codes, (_Float16*)scales, nc == 1 ? 0u : magic);
   return hipGetLastError();
 }
 

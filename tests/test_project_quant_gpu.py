@@ -77,6 +77,33 @@ def test_quant_bit_exact(fmt, r, stride):
         assert oracle.unpack_int4(got_codes[2:3], r)[0, :8].tolist() == [7, 0, 2, 2, 0, -2, -2, 4]
 
 
+@pytest.mark.parametrize("fmt,r,stride,off", [("f16", 154, 154, 1), ("bf16", 154, 157, 3), ("f32", 154, 155, 1),
+                                               ("bf16", 40, 41, 5), ("f16", 2100, 2100, 1), ("f32", 1100, 1103, 2)])
+def test_quant_unaligned_and_long_rows(fmt, r, stride, off):
+    """Rows starting at every alignment (the first row `off` elements past a
+    256-byte boundary, odd strides), and rows of more than 4 KB (quantised
+    straight from global memory instead of through the LDS-staged windows)."""
+    import torch
+    import rank_decode_attention_amd as R
+    n_rows = 1500 if r * stride < 200000 else 300
+    stored = _quant_rows(fmt, n_rows, r, seed=r * 3 + stride + off)
+    flat = np.zeros(n_rows * stride + off, dtype=stored.dtype)
+    for i in range(n_rows):
+        flat[off + i * stride: off + i * stride + r] = stored[i]
+    dev = to_device(flat, fmt)
+    z = dev[off:off + n_rows * stride].view(n_rows, stride)
+    nc = oracle.chunks_per_row(r)
+    codes = torch.full((n_rows, 16 * nc), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n_rows, nc), -1, dtype=torch.int16, device="cuda")
+    R.palu_quant_latent(z, r, stride, codes, scales)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = oracle.quant_int4(oracle.upcast(stored, fmt).astype(np.float32))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_scales.view(np.uint16)), "scales differ"
+    got = codes.cpu().numpy()
+    ref = oracle.pack_int4(ref_codes)
+    assert np.array_equal(got, ref), f"codes differ in {int((got != ref).sum())} bytes"
+
+
 def test_quant_empty_is_noop():
     import torch
     import rank_decode_attention_amd as R

@@ -34,26 +34,31 @@ def _rows(fmt, n_rows, r, seed):
     return PI.to_format(z, fmt)
 
 
-def _quant_gpu(stored, fmt, r, stride, rotated=True):
+def _quant_gpu(stored, fmt, r, stride, rotated=True, off=0):
     import torch
     import rank_decode_attention_amd as R
     n = stored.shape[0]
-    buf = np.zeros((n, stride), dtype=stored.dtype)
-    buf[:, :r] = stored
+    flat = np.zeros(n * stride + off, dtype=stored.dtype)
+    for i in range(n):
+        flat[off + i * stride: off + i * stride + r] = stored[i]
+    z = to_device(flat, fmt)[off:off + n * stride].view(n, stride)
     nc = oracle.chunks_per_row(r)
     codes = torch.full((n, 16 * nc), 0xAB, dtype=torch.uint8, device="cuda")
     scales = torch.full((n, nc), -1, dtype=torch.int16, device="cuda")
     fn = R.palu_quant_latent_rotated if rotated else R.palu_quant_latent
-    fn(to_device(buf, fmt), r, stride, codes, scales)
+    fn(z, r, stride, codes, scales)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("fmt,r,stride", [("f32", 154, 160), ("f16", 154, 154), ("bf16", 64, 64),
-                                           ("f16", 320, 328), ("bf16", 7, 8), ("f32", 96, 97)])
-def test_rotated_quant_bit_exact(fmt, r, stride):
-    stored = _rows(fmt, 1200, r, seed=r + stride)
-    codes, scales = _quant_gpu(stored, fmt, r, stride)
+@pytest.mark.parametrize("fmt,r,stride,off", [("f32", 154, 160, 0), ("f16", 154, 154, 0), ("bf16", 64, 64, 0),
+                                               ("f16", 320, 328, 0), ("bf16", 7, 8, 0), ("f32", 96, 97, 0),
+                                               ("bf16", 154, 157, 3), ("f32", 1100, 1100, 1)])
+def test_rotated_quant_bit_exact(fmt, r, stride, off):
+    """(off: the first row starts that many elements past a 256-byte boundary;
+    rows over 4 KB are quantised straight from global memory)"""
+    stored = _rows(fmt, 1200 if r < 1000 else 300, r, seed=r + stride)
+    codes, scales = _quant_gpu(stored, fmt, r, stride, off=off)
     ref_codes, ref_scales = oracle.quant_int4_rotated(oracle.upcast(stored, fmt).astype(np.float32))
     assert np.array_equal(scales, ref_scales.view(np.uint16)), "scales differ"
     ref_packed = oracle.pack_int4(ref_codes)
