@@ -81,8 +81,9 @@ def test_quant_bit_exact(fmt, r, stride):
                                                ("bf16", 40, 41, 5), ("f16", 2100, 2100, 1), ("f32", 1100, 1103, 2)])
 def test_quant_unaligned_and_long_rows(fmt, r, stride, off):
     """Rows starting at every alignment (the first row `off` elements past a
-    256-byte boundary, odd strides), and rows of more than 4 KB (quantised
-    straight from global memory instead of through the LDS-staged windows)."""
+    256-byte boundary, odd strides: a lane's 8 elements straddle two aligned
+    16-byte blocks, or three for binary32), and rows of more than 4 KB (a
+    wave's 64 chunks within one or two rows)."""
     import torch
     import rank_decode_attention_amd as R
     n_rows = 1500 if r * stride < 200000 else 300

@@ -55,8 +55,9 @@ def _quant_gpu(stored, fmt, r, stride, rotated=True, off=0):
                                                ("f16", 320, 328, 0), ("bf16", 7, 8, 0), ("f32", 96, 97, 0),
                                                ("bf16", 154, 157, 3), ("f32", 1100, 1100, 1)])
 def test_rotated_quant_bit_exact(fmt, r, stride, off):
-    """(off: the first row starts that many elements past a 256-byte boundary;
-    rows over 4 KB are quantised straight from global memory)"""
+    """(off: the first row starts that many elements past a 256-byte boundary,
+    so lanes' pieces straddle aligned 16-byte blocks; rows over 4 KB put a
+    wave's 64 chunks within one or two rows)"""
     stored = _rows(fmt, 1200 if r < 1000 else 300, r, seed=r + stride)
     codes, scales = _quant_gpu(stored, fmt, r, stride, off=off)
     ref_codes, ref_scales = oracle.quant_int4_rotated(oracle.upcast(stored, fmt).astype(np.float32))
