@@ -9,9 +9,11 @@
 // Layout: x [n_tok][D] row-major; A is passed as its transpose A^T
 // [n_lat][D] (the weight layout of a Linear(D -> n_lat)), so both MFMA
 // operands are 16-byte contiguous runs of D.  Block = 256 tokens x up to 160
-// latent channels of one latent row (group j of keys or values); 8 waves of
-// 32 tokens x 160 channels (two per SIMD); K-steps of 128 bytes staged by LDS
-// DMA, double-buffered.
+// latent channels of one latent row (group j of keys or values); 8 waves in a
+// 4 x 2 grid of 64 tokens x 80 channels (two per SIMD); K-steps of 64 bytes
+// per row staged by LDS DMA in a ring of 5 stages (4 requested ahead), the
+// operands of the next stage read into registers while the MFMAs of the
+// current one run.
 #include "common.h"
 #include "project.h"
 
@@ -24,16 +26,20 @@ struct PrjCfg {
   typedef T_ T;
   static constexpr bool F32 = std::is_same<T, float>::value;
   static constexpr int ESZ = sizeof(T);
-  static constexpr int BM = 256, BN = 160, BK = F32 ? 32 : 64, NW = 8, NT = 512;
-  static constexpr int MT = BM / (16 * NW), NTL = 10;    // m-tiles / n-tiles per wave
-  static constexpr int CPR = BK * ESZ / 16;              // 16-byte chunks per staged row
-  static constexpr int PIT = CPR + 1;                    // padded LDS row pitch (slots)
-  static constexpr int SX = cdiv(BM * PIT, 64 * NW) * 64 * NW;   // x slots (whole instructions)
-  static constexpr int SA = cdiv(BN * PIT, 64 * NW) * 64 * NW;
-  static constexpr int NIX = SX / (64 * NW), NIA = SA / (64 * NW);
-  static constexpr int NDMA = NIX + NIA;
-  static constexpr int BUF = (SX + SA);                  // slots per stage
-  static constexpr int KCH = 2;                          // operand chunks (4 x 16 bytes) per K-step per row
+  static constexpr int BM = 256, BN = 160, NW = 8, NT = 512;
+  static constexpr int WM = 4, WN = 2;                   // wave grid: 64 tokens x 80 channels per wave
+  static constexpr int MT = BM / (16 * WM);              // m-tiles per wave (4)
+  static constexpr int NTL = BN / (16 * WN);             // n-tiles per wave (5)
+  static constexpr int ROWB = 64;                        // bytes of a row per K-step: four 16-byte chunks
+  static constexpr int BK = ROWB / ESZ;                  // K per step (32 for 16-bit, 16 for fp32)
+  static constexpr int SXS = BM * 4, SAS = BN * 4;       // 16-byte slots of the x and A^T tiles of a stage
+  static constexpr int NIX = SXS / (64 * NW);            // DMA instructions per wave (x)
+  static constexpr int NIA = cdiv(SAS, 64 * NW);         // (A^T; the last one only for waves inside the tile)
+  static constexpr int STG = SXS + SAS;                  // slots per stage (26 KB)
+  static constexpr int NS = 5;                           // stages: NS - 1 in flight ahead of the one computed
+  static constexpr int TP = 68;                          // int4 epilogue: floats per staged column (64 tokens + pad)
+  static_assert(SXS % (64 * NW) == 0 && SAS % 64 == 0, "DMA slots");
+  static_assert(BN * TP <= NS * STG * 4, "epilogue staging");
 };
 
 template <class C, class OT>
@@ -43,10 +49,10 @@ template <class C>
 __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectParams p) {
   typedef typename C::T T;
   typedef typename std::conditional<C::F32, f32x4, typename Vec8<typename std::conditional<C::F32, _Float16, T>::type>::type>::type op_t;
-  __shared__ uint4 st0[C::BUF];
-  __shared__ uint4 st1[C::BUF];
+  __shared__ uint4 stg[C::NS * C::STG];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wm = w & (C::WM - 1), wn = w / C::WM;
   const int64_t m0 = (int64_t)blockIdx.x * C::BM;
   const int j = blockIdx.y;                       // latent row: keys of groups 0..G-1, then values
   const int r = p.rank[j];
@@ -58,36 +64,49 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   const T* A = (const T*)p.A;
   const int64_t D = p.d_model;
 
-  // per-lane DMA geometry (slot -> row, chunk)
-  int gx[C::NIX], ga[C::NIA];
+  // Stage layout: row-major tiles of 64-byte rows (x: BM token rows, then
+  // A^T: BN channel rows), the four 16-byte chunks of row R stored at chunk
+  // position c ^ ((R >> 2) & 3), so that the 16 rows of an MFMA operand read
+  // (same logical chunk) fall on 16 distinct 16-byte bank groups.  DMA
+  // instruction m of wave w fills slots (m * NW + w) * 64 + l of a region:
+  // row slot / 4, physical chunk slot % 4.  Rows past the tokens or the
+  // valid channels load the last valid row (never stored).
+  const T* xsrc[C::NIX];
+  const T* asrc[C::NIA];
 #pragma unroll
   for (int m = 0; m < C::NIX; ++m) {
     const int slot = (m * C::NW + w) * 64 + l;
-    int row = slot / C::PIT, pos = slot - row * C::PIT;
-    row = row < C::BM ? row : C::BM - 1;
-    pos = pos < C::CPR ? pos : 0;
-    int64_t tok = m0 + row;
-    tok = tok < p.n_tok ? tok : p.n_tok - 1;
-    gx[m] = (int)((tok - m0) << 8) | pos;
+    const int row = slot >> 2, lc = (slot & 3) ^ ((row >> 2) & 3);
+    const int64_t tok = min(m0 + row, p.n_tok - 1);
+    xsrc[m] = X + tok * D + lc * (16 / C::ESZ);
   }
 #pragma unroll
   for (int m = 0; m < C::NIA; ++m) {
     const int slot = (m * C::NW + w) * 64 + l;
-    int row = slot / C::PIT, pos = slot - row * C::PIT;
-    row = row < nvalid ? row : nvalid - 1;
-    pos = pos < C::CPR ? pos : 0;
-    ga[m] = (row << 8) | pos;
+    const int row = min(slot >> 2, nvalid - 1), lc = (slot & 3) ^ (((slot >> 2) >> 2) & 3);
+    asrc[m] = A + (col0 + row) * D + lc * (16 / C::ESZ);
   }
-  auto issue = [&](uint4* buf, int64_t k0) __attribute__((always_inline)) {
+  // (waves whose slots of an A^T instruction lie past the tile skip it: they
+  // issue one DMA instruction fewer per stage)
+  const bool afull = (C::NIA - 1) * C::NW * 64 + w * 64 < C::SAS;
+  auto issue = [&](int buf, int64_t k0) __attribute__((always_inline)) {
+    const unsigned base = lds_addr(stg) + 16u * (unsigned)(buf * C::STG);
 #pragma unroll
-    for (int m = 0; m < C::NIX; ++m) {
-      const T* src = X + (m0 + (gx[m] >> 8)) * D + k0 + (gx[m] & 0xFF) * (16 / C::ESZ);
-      dma16(src, lds_addr(buf) + 16u * ((m * C::NW + w) * 64));
-    }
+    for (int m = 0; m < C::NIX; ++m) dma16(xsrc[m] + k0, base + 16u * ((m * C::NW + w) * 64));
 #pragma unroll
-    for (int m = 0; m < C::NIA; ++m) {
-      const T* src = A + (col0 + (ga[m] >> 8)) * D + k0 + (ga[m] & 0xFF) * (16 / C::ESZ);
-      dma16(src, lds_addr(buf) + 16u * (C::SX + (m * C::NW + w) * 64));
+    for (int m = 0; m < C::NIA; ++m)
+      if (m < C::NIA - 1 || afull) dma16(asrc[m] + k0, base + 16u * (C::SXS + (m * C::NW + w) * 64));
+  };
+  // wait until at most `after` stages issued after the next one are in flight
+  auto wait_stages = [&](int after) __attribute__((always_inline)) {
+    constexpr int N4 = C::NIX + C::NIA, N3 = N4 - 1;
+    static_assert(C::NS == 5, "wait counts below");
+    if (afull) {
+      if (after >= 3) wait_vmcnt<3 * N4>(); else if (after == 2) wait_vmcnt<2 * N4>();
+      else if (after == 1) wait_vmcnt<N4>(); else wait_vmcnt<0>();
+    } else {
+      if (after >= 3) wait_vmcnt<3 * N3>(); else if (after == 2) wait_vmcnt<2 * N3>();
+      else if (after == 1) wait_vmcnt<N3>(); else wait_vmcnt<0>();
     }
   };
 
@@ -96,73 +115,79 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   for (int a = 0; a < C::MT; ++a)
 #pragma unroll
     for (int b = 0; b < C::NTL; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ntl = cdiv(nvalid, 16);
+  const int kq = l >> 4, rr = l & 15;
+  // operand read offset of this lane inside a 16-row tile: row rr, logical
+  // chunk kq (16-bit: k = 8 kq .. +7 of the step; fp32: k = 4 kq .. +3)
+  const int lo = rr * C::ROWB + 16 * (kq ^ ((rr >> 2) & 3));
 
-  auto compute = [&](const uint4* buf) __attribute__((always_inline)) {
-    const int kq = l >> 4, rr = l & 15;
+  // Every n-tile runs (branch-free, so the operand reads go out ahead of the
+  // MFMAs): rows of A^T past the valid channels are copies of the last valid
+  // row in LDS, and their columns are not stored.
+  struct Ops { op_t xa[C::MT], bv[C::NTL]; };
+  auto load = [&](int buf, Ops& o) __attribute__((always_inline)) {
+    const uint8_t* sb = (const uint8_t*)stg + buf * C::STG * 16;
 #pragma unroll
-    for (int kc = 0; kc < C::KCH; ++kc) {
-      op_t xa[C::MT];
+    for (int a = 0; a < C::MT; ++a) o.xa[a] = *(const op_t*)(sb + (64 * wm + 16 * a) * C::ROWB + lo);
+#pragma unroll
+    for (int b = 0; b < C::NTL; ++b) o.bv[b] = *(const op_t*)(sb + 16 * C::SXS + (80 * wn + 16 * b) * C::ROWB + lo);
+  };
+  auto mma = [&](const Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < C::NTL; ++b)
 #pragma unroll
       for (int a = 0; a < C::MT; ++a) {
-        const int row = C::MT * 16 * w + 16 * a + rr;
-        // 16-bit: chunk 4*kc + kq holds k = 32 kc + 8 kq .. +7; fp32: 4 floats
-        xa[a] = *(const op_t*)(buf + row * C::PIT + 4 * kc + kq);
-      }
-      // Every n-tile runs (branch-free, so the operand reads go out ahead of
-      // the MFMAs; a runtime bound here puts each read and its MFMAs in a
-      // basic block of its own): rows of A^T past the valid channels are
-      // copies of the last valid row in LDS, and their columns are not stored.
-#pragma unroll
-      for (int b = 0; b < C::NTL; ++b) {
-        const op_t bv = *(const op_t*)(buf + C::SX + (16 * b + rr) * C::PIT + 4 * kc + kq);
-#pragma unroll
-        for (int a = 0; a < C::MT; ++a) {
-          if constexpr (C::F32) {
-            f32x4 c = acc[a][b];
-            c = mfma16x16x4(xa[a][0], bv[0], c);
-            c = mfma16x16x4(xa[a][1], bv[1], c);
-            c = mfma16x16x4(xa[a][2], bv[2], c);
-            c = mfma16x16x4(xa[a][3], bv[3], c);
-            acc[a][b] = c;
-          } else {
-            acc[a][b] = mfma16x16x32(xa[a], bv, acc[a][b]);
-          }
+        if constexpr (C::F32) {
+          f32x4 c = acc[a][b];
+          c = mfma16x16x4(o.xa[a][0], o.bv[b][0], c);
+          c = mfma16x16x4(o.xa[a][1], o.bv[b][1], c);
+          c = mfma16x16x4(o.xa[a][2], o.bv[b][2], c);
+          c = mfma16x16x4(o.xa[a][3], o.bv[b][3], c);
+          acc[a][b] = c;
+        } else {
+          acc[a][b] = mfma16x16x32(o.xa[a], o.bv[b], acc[a][b]);
         }
       }
-    }
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    barrier();
+    asm volatile("" ::: "memory");
   };
 
+  // K loop: stage ks lives in buffer ks % NS, and NS - 1 stages are
+  // requested ahead.  Step ks waits for stage ks + 1, refills the buffer of
+  // stage ks - 1 (its operands were read in step ks - 2 and used in step
+  // ks - 1 by every wave past the barrier), reads stage ks + 1's operands
+  // into registers and runs the MFMAs of stage ks on the operands read in
+  // the step before: the LDS reads of one stage overlap the MFMAs of the
+  // previous one.  One barrier per step.
   const int nk = (int)(D / C::BK);
-  issue(st0, 0);
-  for (int ks = 0; ks < nk; ks += 2) {
-    // stage ks in st0, ks + 1 in st1
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s)
+    if (s < nk) issue(s, (int64_t)s * C::BK);
+  auto step = [&](int ks, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
     if (ks + 1 < nk) {
-      issue(st1, (int64_t)(ks + 1) * C::BK);
-      wait_vmcnt<C::NDMA>();
-    } else {
-      wait_vmcnt<0>();
+      wait_stages(min(nk - 1, ks + C::NS - 2) - (ks + 1));
+      sync();
+      if (ks + C::NS - 1 < nk) issue((ks + C::NS - 1) % C::NS, (int64_t)(ks + C::NS - 1) * C::BK);
+      load((ks + 1) % C::NS, nxt);
     }
-    barrier();
-    compute(st0);
-    wait_lgkm0();
-    barrier();
-    if (ks + 1 < nk) {
-      if (ks + 2 < nk) {
-        issue(st0, (int64_t)(ks + 2) * C::BK);
-        wait_vmcnt<C::NDMA>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      barrier();
-      compute(st1);
-      wait_lgkm0();
-      barrier();
+    mma(cur);
+  };
+  {
+    Ops o0, o1;
+    wait_stages(min(nk - 1, C::NS - 2));
+    sync();
+    load(0, o0);
+    int ks = 0;
+    for (; ks + 1 < nk; ks += 2) {
+      step(ks, o0, o1);
+      step(ks + 1, o1, o0);
     }
+    if (ks < nk) step(ks, o0, o1);
   }
 
   // ---- epilogue
-  const int kq = l >> 4, rr = l & 15;
   const int gj = j % p.G, is_v = j >= p.G;
   const int pitch = is_v ? p.pv[gj] : p.pk[gj];
   // block of latent row t of the written sequence (paged: the page holding
@@ -186,16 +211,16 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     for (int a = 0; a < C::MT; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t tok = m0 + C::MT * 16 * w + 16 * a + 4 * kq + e;
+        const int64_t tok = m0 + 64 * wm + 16 * a + 4 * kq + e;
         if (tok < p.n_tok) {
           uint8_t* rowp = zrow(p.pos0 + tok);
 #pragma unroll
           for (int b = 0; b < C::NTL; ++b) {
-            const int n = n0 + 16 * b + rr;
-            if (b < ntl && n < r) store_elem<C, T>(rowp + n * C::ESZ, from_f32<T>(acc[a][b][e]));
+            const int n = 80 * wn + 16 * b + rr;
+            if (n < nvalid) store_elem<C, T>(rowp + (n0 + n) * C::ESZ, from_f32<T>(acc[a][b][e]));
           }
           // zero the row padding (pitch beyond the rank) once, from the last block
-          if (n0 + C::BN >= r) {
+          if (wn == 0 && n0 + C::BN >= r) {
             const int padn = pitch / C::ESZ;
             for (int n = r + rr; n < padn; n += 16) store_elem<C, T>(rowp + n * C::ESZ, from_f32<T>(0.f));
           }
@@ -203,14 +228,10 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
       }
   } else {
     // Quantise per (token, 32-element chunk) exactly as palu_quant_latent.
-    // Each wave stages one 16-token m-tile at a time in its own LDS region,
-    // transposed ([column][token], 16-byte vector writes of the lane's four
-    // consecutive tokens), then its lanes take one (token, chunk) each.
-    // The region reuses a stage buffer: every wave has passed the main
-    // loop's final barrier, so no stage data is read any more.
-    constexpr int TP = 20;                                  // floats per staged column (16 tokens + pad)
-    static_assert((C::NW / 2) * C::BN * TP * 4 <= C::BUF * 16, "staging");
-    float* zs = (float*)(w < C::NW / 2 ? st0 : st1) + (w % (C::NW / 2)) * (C::BN * TP);
+    // The block stages 64 tokens at a time (m-tile a of every wave row) in
+    // LDS, transposed ([channel][token], 16-byte writes of a lane's four
+    // consecutive tokens), then a thread takes one (token, chunk) each.
+    float* zs = (float*)stg;
     const int nc_row = cdiv(r, 32);
     auto srow = [&](int64_t t) __attribute__((always_inline)) {
       int64_t tin;
@@ -221,18 +242,21 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     const int nchunk = cdiv(nvalid, 32);
 #pragma unroll
     for (int a = 0; a < C::MT; ++a) {
-#pragma unroll
-      for (int b = 0; b < C::NTL; ++b) *(f32x4*)(zs + (16 * b + rr) * TP + 4 * kq) = acc[a][b];
       wait_lgkm0();
-      for (int it = l; it < 16 * nchunk; it += 64) {
-        const int trow = it & 15, c = it >> 4;
-        const int64_t tok = m0 + C::MT * 16 * w + 16 * a + trow;
+      __syncthreads();   // the stages (first round) or the previous round's staged tile are read
+#pragma unroll
+      for (int b = 0; b < C::NTL; ++b)
+        *(f32x4*)(zs + (80 * wn + 16 * b + rr) * C::TP + 16 * wm + 4 * kq) = acc[a][b];
+      __syncthreads();
+      if (tid < 64 * nchunk) {
+        const int trow = tid & 63, c = tid >> 6;
+        const int64_t tok = m0 + 64 * (trow >> 4) + 16 * a + (trow & 15);
         const int cg = n0 / 32 + c;                // chunk index within the latent row
         const int n = min(32, r - cg * 32);
         if (tok < p.n_tok) {
-          const float* v = zs + (32 * c) * TP + trow;
+          const float* v = zs + (32 * c) * C::TP + trow;
           float amax = 0.f;
-          for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i * TP]));
+          for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i * C::TP]));
           const float s32 = __fdiv_rn(amax, 7.0f);
           const _Float16 s16 = (_Float16)s32;
           const float sf = (float)s16;
@@ -240,7 +264,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
           for (int i = 0; i < n; ++i) {
             int q = 0;
             if (sf != 0.f) {
-              float qf = rintf(__fdiv_rn(v[i * TP], sf));
+              float qf = rintf(__fdiv_rn(v[i * C::TP], sf));
               qf = fminf(fmaxf(qf, -7.f), 7.f);
               q = (int)qf;
             }
@@ -250,7 +274,6 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
           ((_Float16*)srow(p.pos0 + tok))[cg] = s16;
         }
       }
-      wait_lgkm0();   // this m-tile's reads are done before the next one is staged
     }
   }
 }
