@@ -776,11 +776,12 @@ __global__ void __launch_bounds__(256) palu_qabs_kernel(const DecodeParams p, in
 // 16 rows of (sequence, query head of kv head c)).  For every row the split
 // records of its sequence are combined,
 //   m* = max m_i, l* = sum l_i 2^(m_i - m*), a = sum acc_i 2^(m_i - m*) / l*,
-// with the per-record weights 2^(m_i - m*) / l* formed once per row, then
+// (online over the records, in record order), then
 // out[b][h][cols] = a . B_v^g[:, c*DH + cols] (16-bit: MFMA with a split into
 // hi + lo parts, one wave per 16 columns; fp32: VALU).  The kernel is
-// latency-bound: every phase issues all of a thread's global loads before
-// using any of them.
+// latency-bound: it makes two dependent rounds of global loads (the tile
+// starts, then every record of a thread's items at once), with the B_v
+// slice loaded beside the first.
 constexpr int kMergeRows = 16;
 constexpr int kMergeCols = 32;
 constexpr int kMergeThreads = 256;
@@ -798,125 +799,119 @@ __global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeP
   const int rv = p.rv[g];
   const int rvk = (rv + 31) / 32 * 32;               // rank padded to whole k-steps
   const int w_grp = ng * DH;
-  const int wpitch = p.P + 1;
-  // (uint4-typed so that the dynamic region starts 16-byte aligned after the
-  // static arrays below: the a rows and the B_v slice take 16-byte accesses)
+  // (uint4-typed so that the region is 16-byte aligned: the a rows and the
+  // B_v slice take 16-byte accesses)
   extern __shared__ uint4 smem_u4[];
   float* smem = (float*)smem_u4;
-  float* wts = smem;                                 // [16][P + 1] record weights
-  float* a = wts + kMergeRows * wpitch;              // [16][rvk + 4]
+  float* a = smem;                                   // [16][rvk + 4]
   const int apitch = rvk + 4;
   constexpr int BP = kMergeCols + (F32 ? 4 : 16);    // B_v slice row pitch (elements)
   LT* bs = (LT*)(a + kMergeRows * apitch);           // [rvk][BP]
-  __shared__ int rinfo[kMergeRows][2];               // first record index, record count (0: empty row)
-  __shared__ int maxrec;
 
-  // stage B_v^g[:, c*DH + cb*32 .. +32], zero rows past the rank
-  {
-    const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH + cb * kMergeCols;
-    constexpr int EPC = 16 / sizeof(LT);             // elements per 16-byte chunk
-    constexpr int CPRW = kMergeCols / EPC;           // chunks per staged row
-    constexpr int SPT = cdiv(kMergeMaxRank * CPRW, NT);
-    uint4 v[SPT];
+  // B_v^g[:, c*DH + cb*32 .. +32] into registers (stored to LDS, with zero
+  // rows past the rank, once the records are merged)
+  const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH + cb * kMergeCols;
+  constexpr int EPC = 16 / sizeof(LT);               // elements per 16-byte chunk
+  constexpr int CPRW = kMergeCols / EPC;             // chunks per staged row
+  constexpr int SPT = cdiv(kMergeMaxRank * CPRW, NT);
+  uint4 bvr[SPT];
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-      const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
-      v[k] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < rv) v[k] = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
-    }
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-      const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
-      if (r < rvk) *(uint4*)(bs + r * BP + cc * EPC) = v[k];
-    }
+  for (int k = 0; k < SPT; ++k) {
+    const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
+    bvr[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rv) bvr[k] = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
   }
 
-  // per-row record weights: 16 lanes per row
-  const int total = p.hdr[p.batch];
-  const int tpb = cdiv(total, p.Pg[g]);
-  if (tid == 0) maxrec = 0;
-  __syncthreads();
-  {
-    const int row = tid >> 4, sub = tid & 15;
-    const int b = b0 + row / qpk, qq = row % qpk;
-    const int hq = c * qpk + qq;
-    int nrec = 0, k0 = 0;
-    if (b < p.batch) {
-      int L = p.seq_lens[b];
-      L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
-      const int ts = p.hdr[b], te = p.hdr[b + 1];
-      if (L > 0 && te > ts) {
-        const int p0 = ts / tpb, p1 = (te - 1) / tpb;
-        nrec = p1 - p0 + 1;
-        k0 = p0 + b;
-      }
-    }
-    const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + k0) * p.rec_stride;
-    float m = -INFINITY;
-    for (int i = sub; i < nrec; i += 16) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * hq]);
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-    float ls = 0.f;
-    for (int i = sub; i < nrec; i += 16) {
-      const float* rr = recs + (int64_t)i * p.rec_stride;
-      const float e = exp2f(rr[2 * hq] - m);
-      wts[row * wpitch + i] = e;
-      ls = fmaf(rr[2 * hq + 1], e, ls);
-    }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) ls += __shfl_xor(ls, d, 64);
-    const float inv = nrec > 0 ? 1.f / ls : 0.f;
-    for (int i = sub; i < nrec; i += 16) wts[row * wpitch + i] *= inv;
-    if (sub == 0) {
-      rinfo[row][0] = k0;
-      rinfo[row][1] = nrec;
-      atomicMax(&maxrec, nrec);
-    }
-  }
-  __syncthreads();
-
-  // a[row][r] = sum_i w_i acc_i[r]: 4 consecutive ranks per item, consecutive
-  // threads on consecutive items; per record all of a thread's loads go out
-  // before any is used
+  // a[row][r] for 4 consecutive ranks per item, consecutive threads on
+  // consecutive items.  Each thread finds its items' record ranges from the
+  // tile starts, then loads every record's (m, l) of its head and its 4
+  // accumulator values (two records per round, all items' loads issued
+  // before any is used) and merges them online.
   {
     constexpr int IPT = cdiv(kMergeRows * kMergeMaxRank / 4, NT);
     const int rq = rvk / 4;                          // items per row
     const int ni = kMergeRows * rq;
-    const int nmax = maxrec;
-    f32x4 acc4[IPT];
+    const int total = p.hdr[p.batch];
+    const int tpb = cdiv(total, p.Pg[g]);
     const float* base[IPT];
     int nr[IPT];
-    int rowi[IPT];
+    int nmax = 0;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int q = tid + NT * k;
       const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
-      const int qq = row % qpk, hq = c * qpk + qq;
-      rowi[k] = row;
-      nr[k] = (q < ni && 4 * r4 < rv) ? rinfo[row][1] : 0;
-      base[k] = p.rec + ((int64_t)g * (p.P + p.batch) + rinfo[row][0]) * p.rec_stride + 2 * nq + hq * p.rvp + 4 * r4;
-      acc4[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int b = b0 + row / qpk;
+      int nrec = 0, k0 = 0;
+      if (q < ni && 4 * r4 < rv && b < p.batch) {
+        int L = p.seq_lens[b];
+        L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
+        const int ts = p.hdr[b], te = p.hdr[b + 1];
+        if (L > 0 && te > ts) {
+          const int p0 = ts / tpb, p1 = (te - 1) / tpb;
+          nrec = p1 - p0 + 1;
+          k0 = p0 + b;
+        }
+      }
+      nr[k] = nrec;
+      nmax = nrec > nmax ? nrec : nmax;
+      // (m, l) of head hq at base[2 hq], accumulator ranks at base[2 nq + hq rvp + 4 r4]
+      base[k] = p.rec + ((int64_t)g * (p.P + p.batch) + k0) * p.rec_stride;
     }
-    for (int i = 0; i < nmax; ++i) {
-      f32x4 v[IPT];
+    float mk[IPT], lk[IPT];
+    f32x4 ak[IPT];
 #pragma unroll
-      for (int k = 0; k < IPT; ++k)
-        v[k] = i < nr[k] ? *(const f32x4*)(base[k] + (int64_t)i * p.rec_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < IPT; ++k) {
+      mk[k] = -INFINITY;
+      lk[k] = 0.f;
+      ak[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int i = 0; i < nmax; i += 2) {
+      float2 ml[IPT][2];
+      f32x4 v[IPT][2];
 #pragma unroll
       for (int k = 0; k < IPT; ++k) {
-        const float wi = i < nr[k] ? wts[rowi[k] * wpitch + i] : 0.f;
+        const int q = tid + NT * k;
+        const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
+        const int hq = c * qpk + row % qpk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc4[k][e] = fmaf(v[k][e], wi, acc4[k][e]);
+        for (int u = 0; u < 2; ++u) {
+          const float* rr = base[k] + (int64_t)(i + u) * p.rec_stride;
+          const bool ok = i + u < nr[k];
+          ml[k][u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
+          v[k][u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
+#pragma unroll
+      for (int k = 0; k < IPT; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (i + u < nr[k]) {
+            const float mi = ml[k][u].x, mn = fmaxf(mk[k], mi);
+            const float al = exp2f(mk[k] - mn), be = exp2f(mi - mn);
+            lk[k] = fmaf(lk[k], al, ml[k][u].y * be);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ak[k][e] = fmaf(ak[k][e], al, v[k][u][e] * be);
+            mk[k] = mn;
+          }
+        }
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int q = tid + NT * k;
       if (q < ni) {
         const int row = q / rq, r4 = q - row * rq;
-        *(f32x4*)(a + row * apitch + 4 * r4) = acc4[k];
+        const float inv = nr[k] > 0 ? 1.f / lk[k] : 0.f;
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = ak[k][e] * inv;
+        *(f32x4*)(a + row * apitch + 4 * r4) = o;
       }
     }
+  }
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
+    if (r < rvk) *(uint4*)(bs + r * BP + cc * EPC) = bvr[k];
   }
   __syncthreads();
 
@@ -1080,8 +1075,7 @@ static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipS
   if (nq % 2 != 0 || k.rv_max > kMergeMaxRank) return hipErrorInvalidValue;
   const int bpc = kMergeRows / k.q_per_kv;
   const int rvk = (k.rv_max + 31) / 32 * 32;
-  const size_t smem = (size_t)kMergeRows * (p.P + 1) * sizeof(float) +
-                      (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
+  const size_t smem = (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
                       (size_t)rvk * (kMergeCols + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   dim3 grid(p.G * k.kv_per_group * (k.head_dim / kMergeCols), (p.batch + bpc - 1) / bpc);
