@@ -822,26 +822,29 @@ __global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeP
     if (r < rv) bvr[k] = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
   }
 
-  // a[row][r] for 4 consecutive ranks per item, consecutive threads on
-  // consecutive items.  Each thread finds its items' record ranges from the
-  // tile starts, then loads every record's (m, l) of its head and its 4
-  // accumulator values (two records per round, all items' loads issued
-  // before any is used) and merges them online.
+  // a[row][r] for 4 consecutive ranks per item (row, r4).  Each thread
+  // finds its items' record ranges from the tile starts, then loads every
+  // record's (m, l) of its head and its 4 accumulator values (several
+  // records per round, all loads of a round issued before any is used) and
+  // merges them online.  With at most one valid item per thread (small
+  // batches, whose sequences are split over many records) nsub threads
+  // share an item, each taking every nsub-th record four per round, and
+  // their partial merges are combined through LDS.
   {
-    constexpr int IPT = cdiv(kMergeRows * kMergeMaxRank / 4, NT);
     const int rq = rvk / 4;                          // items per row
     const int ni = kMergeRows * rq;
     const int total = p.hdr[p.batch];
     const int tpb = cdiv(total, p.Pg[g]);
-    const float* base[IPT];
-    int nr[IPT];
-    int nmax = 0;
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const int q = tid + NT * k;
+    const int rows_valid = min(kMergeRows, (p.batch - b0) * qpk);
+    const int niv = rows_valid * rq;
+    int nsub = 1;
+    while (nsub < 16 && 2 * nsub * niv <= NT) nsub *= 2;
+    // record range of the sequence of item q (nrec = 0: no record, a = 0)
+    auto range = [&](int q, int& nrec, const float*& base) __attribute__((always_inline)) {
       const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
       const int b = b0 + row / qpk;
-      int nrec = 0, k0 = 0;
+      int k0 = 0;
+      nrec = 0;
       if (q < ni && 4 * r4 < rv && b < p.batch) {
         int L = p.seq_lens[b];
         L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
@@ -852,60 +855,120 @@ __global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeP
           k0 = p0 + b;
         }
       }
-      nr[k] = nrec;
-      nmax = nrec > nmax ? nrec : nmax;
       // (m, l) of head hq at base[2 hq], accumulator ranks at base[2 nq + hq rvp + 4 r4]
-      base[k] = p.rec + ((int64_t)g * (p.P + p.batch) + k0) * p.rec_stride;
-    }
-    float mk[IPT], lk[IPT];
-    f32x4 ak[IPT];
+      base = p.rec + ((int64_t)g * (p.P + p.batch) + k0) * p.rec_stride;
+    };
+    // online merge of one record into (m, l, acc)
+    auto fold = [&](float& m, float& ls, f32x4& acc, float2 ml, const f32x4& v) __attribute__((always_inline)) {
+      const float mn = fmaxf(m, ml.x);
+      const float al = exp2f(m - mn), be = exp2f(ml.x - mn);
+      ls = fmaf(ls, al, ml.y * be);
 #pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      mk[k] = -INFINITY;
-      lk[k] = 0.f;
-      ak[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int i = 0; i < nmax; i += 2) {
-      float2 ml[IPT][2];
-      f32x4 v[IPT][2];
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(acc[e], al, v[e] * be);
+      m = mn;
+    };
+    auto store_a = [&](int q, float m, float ls, const f32x4& acc, int nrec) __attribute__((always_inline)) {
+      const int row = q / rq, r4 = q - row * rq;
+      const float inv = nrec > 0 ? 1.f / ls : 0.f;
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[e] * inv;
+      *(f32x4*)(a + row * apitch + 4 * r4) = o;
+      (void)m;
+    };
+    if (niv > NT) {
+      constexpr int IPT = cdiv(kMergeRows * kMergeMaxRank / 4, NT);
+      const float* base[IPT];
+      int nr[IPT];
+      int nmax = 0;
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        range(tid + NT * k, nr[k], base[k]);
+        nmax = nr[k] > nmax ? nr[k] : nmax;
+      }
+      float mk[IPT], lk[IPT];
+      f32x4 ak[IPT];
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        mk[k] = -INFINITY;
+        lk[k] = 0.f;
+        ak[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int i = 0; i < nmax; i += 2) {
+        float2 ml[IPT][2];
+        f32x4 v[IPT][2];
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+          const int q = tid + NT * k;
+          const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
+          const int hq = c * qpk + row % qpk;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float* rr = base[k] + (int64_t)(i + u) * p.rec_stride;
+            const bool ok = i + u < nr[k];
+            ml[k][u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
+            v[k][u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < IPT; ++k)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (i + u < nr[k]) fold(mk[k], lk[k], ak[k], ml[k][u], v[k][u]);
+      }
 #pragma unroll
       for (int k = 0; k < IPT; ++k) {
         const int q = tid + NT * k;
-        const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
-        const int hq = c * qpk + row % qpk;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float* rr = base[k] + (int64_t)(i + u) * p.rec_stride;
-          const bool ok = i + u < nr[k];
-          ml[k][u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
-          v[k][u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        if (q < ni) store_a(q, mk[k], lk[k], ak[k], nr[k]);
       }
+    } else {
+      // thread tid: item tid % niv, records sub, sub + nsub, ... (four per
+      // round; nsub = 1 when the valid items fill the block)
+      float* part = a + kMergeRows * apitch + rvk * (BP * (int)sizeof(LT) / 4);   // [nsub * niv][8]
+      const int q = tid % niv, sub = tid / niv;
+      const bool act = sub < nsub;
+      int nrec = 0;
+      const float* base;
+      range(q, nrec, base);
+      const int row = q / rq, r4 = q - row * rq;
+      const int hq = c * qpk + row % qpk;
+      float m = -INFINITY, ls = 0.f;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (act) {
+        for (int i = sub; i < nrec; i += 4 * nsub) {
+          float2 ml[4];
+          f32x4 v[4];
 #pragma unroll
-      for (int k = 0; k < IPT; ++k)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (i + u < nr[k]) {
-            const float mi = ml[k][u].x, mn = fmaxf(mk[k], mi);
-            const float al = exp2f(mk[k] - mn), be = exp2f(mi - mn);
-            lk[k] = fmaf(lk[k], al, ml[k][u].y * be);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ak[k][e] = fmaf(ak[k][e], al, v[k][u][e] * be);
-            mk[k] = mn;
+          for (int u = 0; u < 4; ++u) {
+            const int ii = i + u * nsub;
+            const float* rr = base + (int64_t)ii * p.rec_stride;
+            const bool ok = ii < nrec;
+            ml[u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
+            v[u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (i + u * nsub < nrec) fold(m, ls, acc, ml[u], v[u]);
         }
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const int q = tid + NT * k;
-      if (q < ni) {
-        const int row = q / rq, r4 = q - row * rq;
-        const float inv = nr[k] > 0 ? 1.f / lk[k] : 0.f;
-        f32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = ak[k][e] * inv;
-        *(f32x4*)(a + row * apitch + 4 * r4) = o;
+        float* pp = part + 8 * (sub * niv + q);
+        pp[0] = m;
+        pp[1] = ls;
+        *(f32x4*)(pp + 4) = acc;
       }
+      __syncthreads();
+      if (tid < niv) {
+        // combine the nsub partials in subset order (a subset without a
+        // record has m = -inf and contributes nothing)
+        float mc = -INFINITY, lc = 0.f;
+        f32x4 ac = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < nsub && u < nrec; ++u) {
+          const float* pp = part + 8 * (u * niv + tid);
+          fold(mc, lc, ac, float2{pp[0], pp[1]}, *(const f32x4*)(pp + 4));
+        }
+        store_a(tid, mc, lc, ac, nrec);
+      }
+      // rows past the valid ones are zero
+      for (int qq = niv + tid; qq < ni; qq += NT) store_a(qq, 0.f, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}, 0);
     }
   }
 #pragma unroll
@@ -1076,7 +1139,8 @@ static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipS
   const int bpc = kMergeRows / k.q_per_kv;
   const int rvk = (k.rv_max + 31) / 32 * 32;
   const size_t smem = (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
-                      (size_t)rvk * (kMergeCols + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT);
+                      (size_t)rvk * (kMergeCols + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT) +
+                      (size_t)kMergeThreads * 8 * sizeof(float);   // partial merges of shared items
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   dim3 grid(p.G * k.kv_per_group * (k.head_dim / kMergeCols), (p.batch + bpc - 1) / bpc);
   auto kern = k.head_dim == 64 ? palu_merge_kernel<LT, 64> : palu_merge_kernel<LT, 128>;
