@@ -254,21 +254,43 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
         const int cg = n0 / 32 + c;                // chunk index within the latent row
         const int n = min(32, r - cg * 32);
         if (tok < p.n_tok) {
-          const float* v = zs + (32 * c) * C::TP + trow;
+          const float* vs = zs + (32 * c) * C::TP + trow;
+          float v[32];
+#pragma unroll
+          for (int i = 0; i < 32; ++i) v[i] = i < n ? vs[i * C::TP] : 0.f;
           float amax = 0.f;
-          for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i * C::TP]));
+#pragma unroll
+          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
           const float s32 = __fdiv_rn(amax, 7.0f);
           const _Float16 s16 = (_Float16)s32;
           const float sf = (float)s16;
           unsigned int words[4] = {0u, 0u, 0u, 0u};
-          for (int i = 0; i < n; ++i) {
-            int q = 0;
-            if (sf != 0.f) {
-              float qf = rintf(__fdiv_rn(v[i * C::TP], sf));
-              qf = fminf(fmaxf(qf, -7.f), 7.f);
-              q = (int)qf;
+          if (sf != 0.f) {
+            // code = rint(fl(z / s)): t = z * fl(1 / s) is within 1.5e-6 of
+            // fl(z / s) for |t| < 8, so rint(t) is the code unless t lies
+            // within 4e-6 of a half-integer, where the correctly rounded
+            // quotient is formed (for |t| >= 8 both clamp to +-7)
+            const float inv = __fdiv_rn(1.0f, sf);
+            float qf[32];
+            bool near = false;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              const float t = v[i] * inv;
+              qf[i] = rintf(t);
+              near |= fabsf(t - qf[i]) > 0.5f - 4e-6f;
             }
-            words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
+            if (near) {   // (rare)
+#pragma unroll
+              for (int i = 0; i < 32; ++i) {
+                const float t = v[i] * inv;
+                if (fabsf(t - rintf(t)) > 0.5f - 4e-6f) qf[i] = rintf(__fdiv_rn(v[i], sf));
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              const int q = (int)__builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
+              words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
+            }
           }
           *(uint4*)(zrow(p.pos0 + tok) + 16 * cg) = make_uint4(words[0], words[1], words[2], words[3]);
           ((_Float16*)srow(p.pos0 + tok))[cg] = s16;
