@@ -67,6 +67,11 @@ SMALL = [
                                     max_len=150, fixed_lengths=(150, 9, 64)), None),
     ("7b_norope_short", _small("llama2_7b", use_rope=False, rank=None, rank_choices=(64, 96, 256), batch=4,
                                max_len=100, fixed_lengths=(16, 100, 1, 48)), None),
+    # one or two sequences split over every block of their group: the merge
+    # shares an output item between several threads (each merging every
+    # nsub-th record, several rounds here) and combines their partials
+    ("7b_batch1_all_blocks", _small("llama2_7b", batch=1, max_len=2085, fixed_lengths=(2085,)), None),
+    ("7b_batch2_all_blocks", _small("llama2_7b", batch=2, max_len=1500, fixed_lengths=(1500, 701)), None),
 ]
 
 
