@@ -747,27 +747,56 @@ __global__ void __launch_bounds__(C::NT, 1) palu_decode_kernel(const DecodeParam
 
 // ------------------------------------------------------------------ absorbed query
 // qabs[b][h][k] = qscale * sum_d B_k^g[k][c*DH + d] q[b][h][d]   (k < r_k, else 0)
+// A small product per (group g, kv head c): rows of B_k^g (ranks, d
+// contiguous) times the queries of kv head c of every sequence (columns
+// (b, qq), d contiguous), on MFMA with both operands read as 16-byte runs
+// straight from global memory.  One wave per (g, c, 16 ranks, 128 columns):
+// its B_k rows are loaded once, then every column tile's operands are
+// requested before the first product.
+constexpr int kQabsColTiles = 8;   // 16-column tiles per wave
+
 template <class LT, int DH>
-__global__ void __launch_bounds__(256) palu_qabs_kernel(const DecodeParams p, int nq, int qpk, int ng) {
-  const int b = blockIdx.y, h = blockIdx.x;
-  const int g = h / nq;
-  const int c = (h % nq) / qpk;
+__global__ void __launch_bounds__(64) palu_qabs_kernel(const DecodeParams p, int qpk, int ng, int nmt) {
+  typedef typename Op<LT>::type op_t;
+  constexpr int KC = std::is_same<LT, float>::value ? 16 : 32;   // k per MFMA call
+  constexpr int NKS = DH / KC;
+  constexpr int EPC = 16 / (int)sizeof(LT);                     // elements per 16-byte run
+  const int mt = blockIdx.x % nmt, gc = blockIdx.x / nmt;
+  const int g = gc / ng, c = gc % ng;
+  const int l = threadIdx.x, s = l & 15, kq = l >> 4;
   const int rk = p.rk[g];
-  __shared__ float qs[DH];
-  const LT* qb = (const LT*)p.q + ((int64_t)b * p.H + h) * DH;
-  for (int d = threadIdx.x; d < DH; d += blockDim.x) qs[d] = to_f32(qb[d]);
-  __syncthreads();
-  const LT* Bg = (const LT*)p.Bk + p.boff_k[g];
+  const int k0 = 16 * mt;
   const int w = ng * DH;
-  float* out = (float*)p.qabs + ((int64_t)b * p.H + h) * p.qabs_stride;
-  for (int k = threadIdx.x; k < p.qabs_stride; k += blockDim.x) {
-    float s = 0.f;
-    if (k < rk) {
-      const LT* row = Bg + (int64_t)k * w + c * DH;
-#pragma unroll 8
-      for (int d = 0; d < DH; ++d) s = fmaf(to_f32(row[d]), qs[d], s);
+  // A: rank k0 + s, d = KC ks + EPC kq .. (zero rows past the rank)
+  const LT* Bg = (const LT*)p.Bk + p.boff_k[g] + c * DH;
+  op_t a[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    a[ks] = k0 + s < rk ? *(const op_t*)(Bg + (int64_t)(k0 + s) * w + KC * ks + EPC * kq) : op_t{};
+  // B: column n = b * qpk + qq (query head h = (g ng + c) qpk + qq)
+  const int ncol = p.batch * qpk;
+  const int n0 = blockIdx.y * (16 * kQabsColTiles);
+  op_t bq[kQabsColTiles][NKS];
+#pragma unroll
+  for (int t = 0; t < kQabsColTiles; ++t) {
+    const int n = n0 + 16 * t + s;
+    const int b = n / qpk, h = (g * ng + c) * qpk + n % qpk;
+    const LT* qb = (const LT*)p.q + ((int64_t)b * p.H + h) * DH;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) bq[t][ks] = n < ncol ? *(const op_t*)(qb + KC * ks + EPC * kq) : op_t{};
+  }
+#pragma unroll
+  for (int t = 0; t < kQabsColTiles; ++t) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mma<LT>(a[ks], bq[t][ks], acc);
+    // D lane (s, kq): ranks k0 + 4 kq .. +3 of column n0 + 16 t + s
+    const int n = n0 + 16 * t + s;
+    if (n < ncol && k0 + 4 * kq < p.qabs_stride) {
+      const int b = n / qpk, h = (g * ng + c) * qpk + n % qpk;
+      float* out = (float*)p.qabs + ((int64_t)b * p.H + h) * p.qabs_stride + k0 + 4 * kq;
+      *(f32x4*)out = acc * p.qscale;
     }
-    out[k] = s * p.qscale;
   }
 }
 
@@ -776,12 +805,10 @@ __global__ void __launch_bounds__(256) palu_qabs_kernel(const DecodeParams p, in
 // 16 rows of (sequence, query head of kv head c)).  For every row the split
 // records of its sequence are combined,
 //   m* = max m_i, l* = sum l_i 2^(m_i - m*), a = sum acc_i 2^(m_i - m*) / l*,
-// (online over the records, in record order), then
-// out[b][h][cols] = a . B_v^g[:, c*DH + cols] (16-bit: MFMA with a split into
-// hi + lo parts, one wave per 16 columns; fp32: VALU).  The kernel is
-// latency-bound: it makes two dependent rounds of global loads (the tile
-// starts, then every record of a thread's items at once), with the B_v
-// slice loaded beside the first.
+// then out[b][h][cols] = a . B_v^g[:, c*DH + cols] (16-bit: MFMA with a split
+// into hi + lo parts, one wave per 16 columns; fp32: VALU).  The kernel is
+// latency-bound: every phase issues all of a thread's global loads before
+// using any of them.
 constexpr int kMergeRows = 16;
 constexpr int kMergeCols = 32;
 constexpr int kMergeThreads = 256;
@@ -799,44 +826,142 @@ __global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeP
   const int rv = p.rv[g];
   const int rvk = (rv + 31) / 32 * 32;               // rank padded to whole k-steps
   const int w_grp = ng * DH;
-  // (uint4-typed so that the region is 16-byte aligned: the a rows and the
-  // B_v slice take 16-byte accesses)
+  const int wpitch = p.P + 1;
+  // (uint4-typed so that the dynamic region starts 16-byte aligned after the
+  // static arrays below: the a rows and the B_v slice take 16-byte accesses)
   extern __shared__ uint4 smem_u4[];
   float* smem = (float*)smem_u4;
-  float* a = smem;                                   // [16][rvk + 4]
+  float* wts = smem;                                 // [16][P + 1] record weights
+  float* a = wts + kMergeRows * wpitch;              // [16][rvk + 4]
   const int apitch = rvk + 4;
   constexpr int BP = kMergeCols + (F32 ? 4 : 16);    // B_v slice row pitch (elements)
   LT* bs = (LT*)(a + kMergeRows * apitch);           // [rvk][BP]
+  float* part = (float*)(bs + rvk * BP);             // [NT][8] partial merges of shared items
+  __shared__ int rinfo[kMergeRows][2];               // first record index, record count (0: empty row)
+  __shared__ int maxrec;
 
-  // B_v^g[:, c*DH + cb*32 .. +32] into registers (stored to LDS, with zero
-  // rows past the rank, once the records are merged)
-  const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH + cb * kMergeCols;
-  constexpr int EPC = 16 / sizeof(LT);               // elements per 16-byte chunk
-  constexpr int CPRW = kMergeCols / EPC;             // chunks per staged row
-  constexpr int SPT = cdiv(kMergeMaxRank * CPRW, NT);
-  uint4 bvr[SPT];
+  // stage B_v^g[:, c*DH + cb*32 .. +32], zero rows past the rank
+  {
+    const LT* Bv = (const LT*)p.Bv + p.boff_v[g] + c * DH + cb * kMergeCols;
+    constexpr int EPC = 16 / sizeof(LT);             // elements per 16-byte chunk
+    constexpr int CPRW = kMergeCols / EPC;           // chunks per staged row
+    constexpr int SPT = cdiv(kMergeMaxRank * CPRW, NT);
+    uint4 v[SPT];
 #pragma unroll
-  for (int k = 0; k < SPT; ++k) {
-    const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
-    bvr[k] = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rv) bvr[k] = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
+      v[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rv) v[k] = *(const uint4*)(Bv + (int64_t)r * w_grp + cc * EPC);
+    }
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
+      if (r < rvk) *(uint4*)(bs + r * BP + cc * EPC) = v[k];
+    }
   }
 
-  // a[row][r] for 4 consecutive ranks per item (row, r4).  Each thread
-  // finds its items' record ranges from the tile starts, then loads every
-  // record's (m, l) of its head and its 4 accumulator values (several
-  // records per round, all loads of a round issued before any is used) and
-  // merges them online.  With at most one valid item per thread (small
-  // batches, whose sequences are split over many records) nsub threads
-  // share an item, each taking every nsub-th record four per round, and
-  // their partial merges are combined through LDS.
-  {
+  // Record phase.  Many valid rows: per-row record weights
+  // 2^(m_i - m*) / l* (16 lanes per row) in LDS, then a[row][r] =
+  // sum_i w_i acc_i over 4 consecutive ranks per item, the loads of every
+  // item of a record issued together.  At most one valid item per thread
+  // (small batches, whose sequences are split over many records): nsub
+  // threads share an item, each merging every nsub-th record online (four
+  // per round), and their partials are combined through LDS.
+  const int rows_valid = min(kMergeRows, (p.batch - b0) * qpk);
+  const int niv = rows_valid * (rvk / 4);
+  if (niv > NT) {
+    // per-row record weights: 16 lanes per row
+    const int total = p.hdr[p.batch];
+    const int tpb = cdiv(total, p.Pg[g]);
+    if (tid == 0) maxrec = 0;
+    __syncthreads();
+    {
+      const int row = tid >> 4, sub = tid & 15;
+      const int b = b0 + row / qpk, qq = row % qpk;
+      const int hq = c * qpk + qq;
+      int nrec = 0, k0 = 0;
+      if (b < p.batch) {
+        int L = p.seq_lens[b];
+        L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
+        const int ts = p.hdr[b], te = p.hdr[b + 1];
+        if (L > 0 && te > ts) {
+          const int p0 = ts / tpb, p1 = (te - 1) / tpb;
+          nrec = p1 - p0 + 1;
+          k0 = p0 + b;
+        }
+      }
+      const float* recs = p.rec + ((int64_t)g * (p.P + p.batch) + k0) * p.rec_stride;
+      float m = -INFINITY;
+      for (int i = sub; i < nrec; i += 16) m = fmaxf(m, recs[(int64_t)i * p.rec_stride + 2 * hq]);
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+      float ls = 0.f;
+      for (int i = sub; i < nrec; i += 16) {
+        const float* rr = recs + (int64_t)i * p.rec_stride;
+        const float e = exp2f(rr[2 * hq] - m);
+        wts[row * wpitch + i] = e;
+        ls = fmaf(rr[2 * hq + 1], e, ls);
+      }
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) ls += __shfl_xor(ls, d, 64);
+      const float inv = nrec > 0 ? 1.f / ls : 0.f;
+      for (int i = sub; i < nrec; i += 16) wts[row * wpitch + i] *= inv;
+      if (sub == 0) {
+        rinfo[row][0] = k0;
+        rinfo[row][1] = nrec;
+        atomicMax(&maxrec, nrec);
+      }
+    }
+    __syncthreads();
+
+    // a[row][r] = sum_i w_i acc_i[r]: 4 consecutive ranks per item, consecutive
+    // threads on consecutive items; per record all of a thread's loads go out
+    // before any is used
+    {
+      constexpr int IPT = cdiv(kMergeRows * kMergeMaxRank / 4, NT);
+      const int rq = rvk / 4;                          // items per row
+      const int ni = kMergeRows * rq;
+      const int nmax = maxrec;
+      f32x4 acc4[IPT];
+      const float* base[IPT];
+      int nr[IPT];
+      int rowi[IPT];
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const int q = tid + NT * k;
+        const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
+        const int qq = row % qpk, hq = c * qpk + qq;
+        rowi[k] = row;
+        nr[k] = (q < ni && 4 * r4 < rv) ? rinfo[row][1] : 0;
+        base[k] = p.rec + ((int64_t)g * (p.P + p.batch) + rinfo[row][0]) * p.rec_stride + 2 * nq + hq * p.rvp + 4 * r4;
+        acc4[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int i = 0; i < nmax; ++i) {
+        f32x4 v[IPT];
+#pragma unroll
+        for (int k = 0; k < IPT; ++k)
+          v[k] = i < nr[k] ? *(const f32x4*)(base[k] + (int64_t)i * p.rec_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+          const float wi = i < nr[k] ? wts[rowi[k] * wpitch + i] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc4[k][e] = fmaf(v[k][e], wi, acc4[k][e]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const int q = tid + NT * k;
+        if (q < ni) {
+          const int row = q / rq, r4 = q - row * rq;
+          *(f32x4*)(a + row * apitch + 4 * r4) = acc4[k];
+        }
+      }
+    }
+  } else {
     const int rq = rvk / 4;                          // items per row
     const int ni = kMergeRows * rq;
     const int total = p.hdr[p.batch];
     const int tpb = cdiv(total, p.Pg[g]);
-    const int rows_valid = min(kMergeRows, (p.batch - b0) * qpk);
-    const int niv = rows_valid * rq;
     int nsub = 1;
     while (nsub < 16 && 2 * nsub * niv <= NT) nsub *= 2;
     // record range of the sequence of item q (nrec = 0: no record, a = 0)
@@ -867,114 +992,60 @@ __global__ void __launch_bounds__(kMergeThreads) palu_merge_kernel(const DecodeP
       for (int e = 0; e < 4; ++e) acc[e] = fmaf(acc[e], al, v[e] * be);
       m = mn;
     };
-    auto store_a = [&](int q, float m, float ls, const f32x4& acc, int nrec) __attribute__((always_inline)) {
+    auto store_a = [&](int q, float ls, const f32x4& acc, int nrec) __attribute__((always_inline)) {
       const int row = q / rq, r4 = q - row * rq;
       const float inv = nrec > 0 ? 1.f / ls : 0.f;
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = acc[e] * inv;
       *(f32x4*)(a + row * apitch + 4 * r4) = o;
-      (void)m;
     };
-    if (niv > NT) {
-      constexpr int IPT = cdiv(kMergeRows * kMergeMaxRank / 4, NT);
-      const float* base[IPT];
-      int nr[IPT];
-      int nmax = 0;
+    // thread tid: item tid % niv, records sub, sub + nsub, ... (four per
+    // round; nsub = 1 when the valid items fill the block)
+    const int q = tid % niv, sub = tid / niv;
+    const bool act = sub < nsub;
+    int nrec = 0;
+    const float* base;
+    range(q, nrec, base);
+    const int row = q / rq, r4 = q - row * rq;
+    const int hq = c * qpk + row % qpk;
+    float m = -INFINITY, ls = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (act) {
+      for (int i = sub; i < nrec; i += 4 * nsub) {
+        float2 ml[4];
+        f32x4 v[4];
 #pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        range(tid + NT * k, nr[k], base[k]);
-        nmax = nr[k] > nmax ? nr[k] : nmax;
-      }
-      float mk[IPT], lk[IPT];
-      f32x4 ak[IPT];
-#pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        mk[k] = -INFINITY;
-        lk[k] = 0.f;
-        ak[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      for (int i = 0; i < nmax; i += 2) {
-        float2 ml[IPT][2];
-        f32x4 v[IPT][2];
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-          const int q = tid + NT * k;
-          const int row = q < ni ? q / rq : 0, r4 = q - row * rq;
-          const int hq = c * qpk + row % qpk;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float* rr = base[k] + (int64_t)(i + u) * p.rec_stride;
-            const bool ok = i + u < nr[k];
-            ml[k][u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
-            v[k][u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int ii = i + u * nsub;
+          const float* rr = base + (int64_t)ii * p.rec_stride;
+          const bool ok = ii < nrec;
+          ml[u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
+          v[u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int k = 0; k < IPT; ++k)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            if (i + u < nr[k]) fold(mk[k], lk[k], ak[k], ml[k][u], v[k][u]);
+        for (int u = 0; u < 4; ++u)
+          if (i + u * nsub < nrec) fold(m, ls, acc, ml[u], v[u]);
       }
-#pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        const int q = tid + NT * k;
-        if (q < ni) store_a(q, mk[k], lk[k], ak[k], nr[k]);
-      }
-    } else {
-      // thread tid: item tid % niv, records sub, sub + nsub, ... (four per
-      // round; nsub = 1 when the valid items fill the block)
-      float* part = a + kMergeRows * apitch + rvk * (BP * (int)sizeof(LT) / 4);   // [nsub * niv][8]
-      const int q = tid % niv, sub = tid / niv;
-      const bool act = sub < nsub;
-      int nrec = 0;
-      const float* base;
-      range(q, nrec, base);
-      const int row = q / rq, r4 = q - row * rq;
-      const int hq = c * qpk + row % qpk;
-      float m = -INFINITY, ls = 0.f;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (act) {
-        for (int i = sub; i < nrec; i += 4 * nsub) {
-          float2 ml[4];
-          f32x4 v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ii = i + u * nsub;
-            const float* rr = base + (int64_t)ii * p.rec_stride;
-            const bool ok = ii < nrec;
-            ml[u] = ok ? *(const float2*)(rr + 2 * hq) : float2{-INFINITY, 0.f};
-            v[u] = ok ? *(const f32x4*)(rr + 2 * nq + hq * p.rvp + 4 * r4) : f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (i + u * nsub < nrec) fold(m, ls, acc, ml[u], v[u]);
-        }
-        float* pp = part + 8 * (sub * niv + q);
-        pp[0] = m;
-        pp[1] = ls;
-        *(f32x4*)(pp + 4) = acc;
-      }
-      __syncthreads();
-      if (tid < niv) {
-        // combine the nsub partials in subset order (a subset without a
-        // record has m = -inf and contributes nothing)
-        float mc = -INFINITY, lc = 0.f;
-        f32x4 ac = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int u = 0; u < nsub && u < nrec; ++u) {
-          const float* pp = part + 8 * (u * niv + tid);
-          fold(mc, lc, ac, float2{pp[0], pp[1]}, *(const f32x4*)(pp + 4));
-        }
-        store_a(tid, mc, lc, ac, nrec);
-      }
-      // rows past the valid ones are zero
-      for (int qq = niv + tid; qq < ni; qq += NT) store_a(qq, 0.f, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}, 0);
+      float* pp = part + 8 * (sub * niv + q);
+      pp[0] = m;
+      pp[1] = ls;
+      *(f32x4*)(pp + 4) = acc;
     }
-  }
-#pragma unroll
-  for (int k = 0; k < SPT; ++k) {
-    const int i = tid + NT * k, r = i / CPRW, cc = i - r * CPRW;
-    if (r < rvk) *(uint4*)(bs + r * BP + cc * EPC) = bvr[k];
+    __syncthreads();
+    if (tid < niv) {
+      // combine the nsub partials in subset order (a subset without a
+      // record has m = -inf and contributes nothing)
+      float mc = -INFINITY, lc = 0.f;
+      f32x4 ac = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < nsub && u < nrec; ++u) {
+        const float* pp = part + 8 * (u * niv + tid);
+        fold(mc, lc, ac, float2{pp[0], pp[1]}, *(const f32x4*)(pp + 4));
+      }
+      store_a(tid, lc, ac, nrec);
+    }
+    // rows past the valid ones are zero
+    for (int qq = niv + tid; qq < ni; qq += NT) store_a(qq, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}, 0);
   }
   __syncthreads();
 
@@ -1109,11 +1180,15 @@ hipError_t launch_decode(const DecodeKey& k, const DecodeParams& p, hipStream_t 
 
 template <class LT>
 static hipError_t launch_qabs_t(const DecodeKey& k, const DecodeParams& p, hipStream_t stream) {
-  const int nq = k.kv_per_group * k.q_per_kv;
+  // (16-byte f32x4 stores of 4 ranks: the row stride is a multiple of 4)
+  if (p.qabs_stride % 4 != 0) return hipErrorInvalidValue;
+  const int nmt = (p.qabs_stride + 15) / 16;
+  const int ncol = p.batch * k.q_per_kv;
+  const dim3 grid(p.G * k.kv_per_group * nmt, (ncol + 16 * kQabsColTiles - 1) / (16 * kQabsColTiles));
   if (k.head_dim == 64)
-    hipLaunchKernelGGL((palu_qabs_kernel<LT, 64>), dim3(p.H, p.batch), dim3(256), 0, stream, p, nq, k.q_per_kv, k.kv_per_group);
+    hipLaunchKernelGGL((palu_qabs_kernel<LT, 64>), grid, dim3(64), 0, stream, p, k.q_per_kv, k.kv_per_group, nmt);
   else if (k.head_dim == 128)
-    hipLaunchKernelGGL((palu_qabs_kernel<LT, 128>), dim3(p.H, p.batch), dim3(256), 0, stream, p, nq, k.q_per_kv, k.kv_per_group);
+    hipLaunchKernelGGL((palu_qabs_kernel<LT, 128>), grid, dim3(64), 0, stream, p, k.q_per_kv, k.kv_per_group, nmt);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1138,7 +1213,8 @@ static hipError_t launch_merge_t(const DecodeKey& k, const DecodeParams& p, hipS
   if (nq % 2 != 0 || k.rv_max > kMergeMaxRank) return hipErrorInvalidValue;
   const int bpc = kMergeRows / k.q_per_kv;
   const int rvk = (k.rv_max + 31) / 32 * 32;
-  const size_t smem = (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
+  const size_t smem = (size_t)kMergeRows * (p.P + 1) * sizeof(float) +
+                      (size_t)kMergeRows * (rvk + 4) * sizeof(float) +
                       (size_t)rvk * (kMergeCols + (sizeof(LT) == 4 ? 4 : 16)) * sizeof(LT) +
                       (size_t)kMergeThreads * 8 * sizeof(float);   // partial merges of shared items
   if (smem > 160 * 1024) return hipErrorInvalidValue;
