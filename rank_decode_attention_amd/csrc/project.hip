@@ -66,8 +66,10 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
 
   // Stage layout: row-major tiles of 64-byte rows (x: BM token rows, then
   // A^T: BN channel rows), the four 16-byte chunks of row R stored at chunk
-  // position c ^ ((R >> 2) & 3), so that the 16 rows of an MFMA operand read
-  // (same logical chunk) fall on 16 distinct 16-byte bank groups.  DMA
+  // position c ^ ((R >> 1) & 3): the LDS serves a 16-byte-per-lane read 8
+  // lanes (128 bytes) at a time, and the 8 rows of such a group (same
+  // logical chunk) then cover 8 distinct 16-byte slots of a 128-byte line
+  // (measured: no bank conflicts, where c ^ ((R >> 2) & 3) had two-way ones).  DMA
   // instruction m of wave w fills slots (m * NW + w) * 64 + l of a region:
   // row slot / 4, physical chunk slot % 4.  Rows past the tokens or the
   // valid channels load the last valid row (never stored).
@@ -76,14 +78,14 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
 #pragma unroll
   for (int m = 0; m < C::NIX; ++m) {
     const int slot = (m * C::NW + w) * 64 + l;
-    const int row = slot >> 2, lc = (slot & 3) ^ ((row >> 2) & 3);
+    const int row = slot >> 2, lc = (slot & 3) ^ ((row >> 1) & 3);
     const int64_t tok = min(m0 + row, p.n_tok - 1);
     xsrc[m] = X + tok * D + lc * (16 / C::ESZ);
   }
 #pragma unroll
   for (int m = 0; m < C::NIA; ++m) {
     const int slot = (m * C::NW + w) * 64 + l;
-    const int row = min(slot >> 2, nvalid - 1), lc = (slot & 3) ^ (((slot >> 2) >> 2) & 3);
+    const int row = min(slot >> 2, nvalid - 1), lc = (slot & 3) ^ (((slot >> 2) >> 1) & 3);
     asrc[m] = A + (col0 + row) * D + lc * (16 / C::ESZ);
   }
   // (waves whose slots of an A^T instruction lie past the tile skip it: they
@@ -118,7 +120,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   const int kq = l >> 4, rr = l & 15;
   // operand read offset of this lane inside a 16-row tile: row rr, logical
   // chunk kq (16-bit: k = 8 kq .. +7 of the step; fp32: k = 4 kq .. +3)
-  const int lo = rr * C::ROWB + 16 * (kq ^ ((rr >> 2) & 3));
+  const int lo = rr * C::ROWB + 16 * (kq ^ ((rr >> 1) & 3));
 
   // Every n-tile runs (branch-free, so the operand reads go out ahead of the
   // MFMAs): rows of A^T past the valid channels are copies of the last valid
