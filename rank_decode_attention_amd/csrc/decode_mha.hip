@@ -447,7 +447,9 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
     if (ln.l < 16) dma16s(qb, 16u * ln.l, lds_addr(&qst[m % 3][w][0]));
   };
   // ---- int4 tiles: lane tid expands one 32-rank chunk of a tile row, keys
-  // for tid < 32 nchk (row tid / nchk), values for the next 32 nchv lanes.
+  // for tid < 32 nchk (row tid % 32, chunk tid / 32), values for the next
+  // 32 nchv lanes (chunk-major, so that the 8 lanes of an LDS write phase
+  // hold 8 rows of one chunk, whose swizzled positions differ).
   // Its 16 bytes of codes and its scale are loaded into registers one step
   // ahead (rows past the history repeat its last row); the expansion writes
   // the chunk's codes, as exact 16-bit integers, in four 16-byte pieces into
@@ -460,16 +462,14 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
   // accumulator ranks the merge never reads; on rows past the history the
   // key scale is zero and P is zero.
   const int nchk = pk >> 4, nchv = pv >> 4;
-  const int magk = (65536 + nchk - 1) / nchk, magv = (65536 + nchv - 1) / nchv;
   struct Q4It { int row, ch; bool isv, ok; };
   auto q4_item = [&](const Lane& ln) __attribute__((always_inline)) {
     Q4It it;
     int u = ln.t;
     it.isv = u >= 32 * nchk;
     if (it.isv) u -= 32 * nchk;
-    const int n = it.isv ? nchv : nchk;
-    it.row = (u * (it.isv ? magv : magk)) >> 16;   // u / n (u < 256, n <= 8)
-    it.ch = u - it.row * n;
+    it.row = u & 31;
+    it.ch = u >> 5;
     it.ok = !it.isv || u < 32 * nchv;
     return it;
   };
