@@ -94,22 +94,6 @@ __device__ __forceinline__ void sincos_turns(double t, double theta_turns, float
   *s = __builtin_amdgcn_sinf(r);
 }
 
-// 16-byte global -> LDS copy from a wave-uniform base plus a per-lane 32-bit
-// byte offset; lane l lands at LDS byte `lds_wave_base` + 16*l.
-__device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned lds_wave_base) {
-  const uint64_t a = (uint64_t)base;
-  // (readfirstlane returns int: each half goes through unsigned, so that the
-  // low half is zero-extended)
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  const unsigned lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"(sb)
-               : "memory", "m0");
-}
-
 // Reductions over a 16-lane row (DPP only); every lane of the row receives
 // the result.
 __device__ __forceinline__ float max16(float x) {

@@ -51,7 +51,8 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   typedef typename std::conditional<C::F32, f32x4, typename Vec8<typename std::conditional<C::F32, _Float16, T>::type>::type>::type op_t;
   __shared__ uint4 stg[C::NS * C::STG];
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // (wave-uniform: scalar registers)
   const int wm = w & (C::WM - 1), wn = w / C::WM;
   const int64_t m0 = (int64_t)blockIdx.x * C::BM;
   const int j = blockIdx.y;                       // latent row: keys of groups 0..G-1, then values
@@ -73,31 +74,39 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   // instruction m of wave w fills slots (m * NW + w) * 64 + l of a region:
   // row slot / 4, physical chunk slot % 4.  Rows past the tokens or the
   // valid channels load the last valid row (never stored).
-  const T* xsrc[C::NIX];
-  const T* asrc[C::NIA];
+  // Per-lane 32-bit byte offsets of the DMA sources inside the block's x
+  // and A^T tiles; the wave-uniform bases advance by one K-step per stage.
+  constexpr int EPC = 16 / C::ESZ;                 // elements per 16-byte chunk
+  unsigned xoff[C::NIX], aoff[C::NIA];
 #pragma unroll
   for (int m = 0; m < C::NIX; ++m) {
     const int slot = (m * C::NW + w) * 64 + l;
     const int row = slot >> 2, lc = (slot & 3) ^ ((row >> 1) & 3);
     const int64_t tok = min(m0 + row, p.n_tok - 1);
-    xsrc[m] = X + tok * D + lc * (16 / C::ESZ);
+    xoff[m] = (unsigned)(((tok - m0) * D + lc * EPC) * C::ESZ);
   }
 #pragma unroll
   for (int m = 0; m < C::NIA; ++m) {
     const int slot = (m * C::NW + w) * 64 + l;
     const int row = min(slot >> 2, nvalid - 1), lc = (slot & 3) ^ (((slot >> 2) >> 1) & 3);
-    asrc[m] = A + (col0 + row) * D + lc * (16 / C::ESZ);
+    aoff[m] = (unsigned)(((int64_t)row * D + lc * EPC) * C::ESZ);
   }
+  const T* xblk = X + m0 * D;
+  const T* ablk = A + col0 * D;
   // (waves whose slots of an A^T instruction lie past the tile skip it: they
   // issue one DMA instruction fewer per stage)
   const bool afull = (C::NIA - 1) * C::NW * 64 + w * 64 < C::SAS;
-  auto issue = [&](int buf, int64_t k0) __attribute__((always_inline)) {
-    const unsigned base = lds_addr(stg) + 16u * (unsigned)(buf * C::STG);
+  // stage ks into buffer BUF (a compile-time constant)
+  auto issue = [&](auto bufc, int ks) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    const unsigned base = lds_addr(stg) + 16u * (unsigned)(BUF * C::STG);
+    const T* xb = xblk + (int64_t)ks * C::BK;
+    const T* ab = ablk + (int64_t)ks * C::BK;
 #pragma unroll
-    for (int m = 0; m < C::NIX; ++m) dma16(xsrc[m] + k0, base + 16u * ((m * C::NW + w) * 64));
+    for (int m = 0; m < C::NIX; ++m) dma16s(xb, xoff[m], base + 16u * ((m * C::NW + w) * 64));
 #pragma unroll
     for (int m = 0; m < C::NIA; ++m)
-      if (m < C::NIA - 1 || afull) dma16(asrc[m] + k0, base + 16u * (C::SXS + (m * C::NW + w) * 64));
+      if (m < C::NIA - 1 || afull) dma16s(ab, aoff[m], base + 16u * (C::SXS + (m * C::NW + w) * 64));
   };
   // wait until at most `after` stages issued after the next one are in flight
   auto wait_stages = [&](int after) __attribute__((always_inline)) {
@@ -126,8 +135,8 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   // MFMAs): rows of A^T past the valid channels are copies of the last valid
   // row in LDS, and their columns are not stored.
   struct Ops { op_t xa[C::MT], bv[C::NTL]; };
-  auto load = [&](int buf, Ops& o) __attribute__((always_inline)) {
-    const uint8_t* sb = (const uint8_t*)stg + buf * C::STG * 16;
+  auto load = [&](auto bufc, Ops& o) __attribute__((always_inline)) {
+    const uint8_t* sb = (const uint8_t*)stg + decltype(bufc)::value * C::STG * 16;
 #pragma unroll
     for (int a = 0; a < C::MT; ++a) o.xa[a] = *(const op_t*)(sb + (64 * wm + 16 * a) * C::ROWB + lo);
 #pragma unroll
@@ -162,17 +171,26 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   // ks - 1 by every wave past the barrier), reads stage ks + 1's operands
   // into registers and runs the MFMAs of stage ks on the operands read in
   // the step before: the LDS reads of one stage overlap the MFMAs of the
-  // previous one.  One barrier per step.
+  // previous one.  One barrier per step.  The loop is unrolled over 2 NS
+  // steps, so that every buffer index and LDS address offset is a constant.
   const int nk = (int)(D / C::BK);
-#pragma unroll
-  for (int s = 0; s < C::NS - 1; ++s)
-    if (s < nk) issue(s, (int64_t)s * C::BK);
-  auto step = [&](int ks, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  static_assert(C::NS == 5, "buffer constants below");
+  if (0 < nk) issue(I0{}, 0);
+  if (1 < nk) issue(I1{}, 1);
+  if (2 < nk) issue(I2{}, 2);
+  if (3 < nk) issue(I3{}, 3);
+  auto step = [&](auto bufc, int ks, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
     if (ks + 1 < nk) {
       wait_stages(min(nk - 1, ks + C::NS - 2) - (ks + 1));
       sync();
-      if (ks + C::NS - 1 < nk) issue((ks + C::NS - 1) % C::NS, (int64_t)(ks + C::NS - 1) * C::BK);
-      load((ks + 1) % C::NS, nxt);
+      if (ks + C::NS - 1 < nk) issue(std::integral_constant<int, (BUF + C::NS - 1) % C::NS>{}, ks + C::NS - 1);
+      load(std::integral_constant<int, (BUF + 1) % C::NS>{}, nxt);
     }
     mma(cur);
   };
@@ -180,13 +198,19 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     Ops o0, o1;
     wait_stages(min(nk - 1, C::NS - 2));
     sync();
-    load(0, o0);
-    int ks = 0;
-    for (; ks + 1 < nk; ks += 2) {
-      step(ks, o0, o1);
-      step(ks + 1, o1, o0);
+    load(I0{}, o0);
+    for (int ks = 0; ks < nk; ks += 2 * C::NS) {
+      step(I0{}, ks, o0, o1);
+      if (ks + 1 < nk) step(I1{}, ks + 1, o1, o0);
+      if (ks + 2 < nk) step(I2{}, ks + 2, o0, o1);
+      if (ks + 3 < nk) step(I3{}, ks + 3, o1, o0);
+      if (ks + 4 < nk) step(I4{}, ks + 4, o0, o1);
+      if (ks + 5 < nk) step(I0{}, ks + 5, o1, o0);
+      if (ks + 6 < nk) step(I1{}, ks + 6, o0, o1);
+      if (ks + 7 < nk) step(I2{}, ks + 7, o1, o0);
+      if (ks + 8 < nk) step(I3{}, ks + 8, o0, o1);
+      if (ks + 9 < nk) step(I4{}, ks + 9, o1, o0);
     }
-    if (ks < nk) step(ks, o0, o1);
   }
 
   // ---- epilogue
