@@ -36,7 +36,7 @@ struct PrjCfg {
   static constexpr int NIX = SXS / (64 * NW);            // DMA instructions per wave (x)
   static constexpr int NIA = cdiv(SAS, 64 * NW);         // (A^T; the last one only for waves inside the tile)
   static constexpr int STG = SXS + SAS;                  // slots per stage (26 KB)
-  static constexpr int NS = 5;                           // stages: NS - 1 in flight ahead of the one computed
+  static constexpr int NS = 6;                           // stages (26 KB each): a ring of 6, refilled two at a time
   static constexpr int TP = 68;                          // int4 epilogue: floats per staged column (64 tokens + pad)
   static_assert(SXS % (64 * NW) == 0 && SAS % 64 == 0, "DMA slots");
   static_assert(BN * TP <= NS * STG * 4, "epilogue staging");
@@ -111,13 +111,10 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   // wait until at most `after` stages issued after the next one are in flight
   auto wait_stages = [&](int after) __attribute__((always_inline)) {
     constexpr int N4 = C::NIX + C::NIA, N3 = N4 - 1;
-    static_assert(C::NS == 5, "wait counts below");
     if (afull) {
-      if (after >= 3) wait_vmcnt<3 * N4>(); else if (after == 2) wait_vmcnt<2 * N4>();
-      else if (after == 1) wait_vmcnt<N4>(); else wait_vmcnt<0>();
+      if (after >= 2) wait_vmcnt<2 * N4>(); else if (after == 1) wait_vmcnt<N4>(); else wait_vmcnt<0>();
     } else {
-      if (after >= 3) wait_vmcnt<3 * N3>(); else if (after == 2) wait_vmcnt<2 * N3>();
-      else if (after == 1) wait_vmcnt<N3>(); else wait_vmcnt<0>();
+      if (after >= 2) wait_vmcnt<2 * N3>(); else if (after == 1) wait_vmcnt<N3>(); else wait_vmcnt<0>();
     }
   };
 
@@ -165,51 +162,44 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     asm volatile("" ::: "memory");
   };
 
-  // K loop: stage ks lives in buffer ks % NS, and NS - 1 stages are
-  // requested ahead.  Step ks waits for stage ks + 1, refills the buffer of
-  // stage ks - 1 (its operands were read in step ks - 2 and used in step
-  // ks - 1 by every wave past the barrier), reads stage ks + 1's operands
-  // into registers and runs the MFMAs of stage ks on the operands read in
-  // the step before: the LDS reads of one stage overlap the MFMAs of the
-  // previous one.  One barrier per step.  The loop is unrolled over 2 NS
-  // steps, so that every buffer index and LDS address offset is a constant.
-  const int nk = (int)(D / C::BK);
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  static_assert(C::NS == 5, "buffer constants below");
-  if (0 < nk) issue(I0{}, 0);
-  if (1 < nk) issue(I1{}, 1);
-  if (2 < nk) issue(I2{}, 2);
-  if (3 < nk) issue(I3{}, 3);
-  auto step = [&](auto bufc, int ks, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;
-    if (ks + 1 < nk) {
-      wait_stages(min(nk - 1, ks + C::NS - 2) - (ks + 1));
+  // K loop: stage ks lives in buffer ks % 6, and steps go in pairs (ks even,
+  // ks + 1) with one barrier between them: behind it stages ks + 2 and
+  // ks + 3 have landed (two more stay in flight), and stages ks + 5 and
+  // ks + 6 go into the buffers of stages ks - 1 and ks, whose operands every
+  // wave past the barrier has already used in its MFMAs.  Within a step the
+  // next stage's operands are read while the MFMAs of the current one run.
+  // The loop is unrolled over the ring, so that every buffer index and LDS
+  // address offset is a constant.
+  const int nk = (int)(D / C::BK);                  // even (d_model is a multiple of 64)
+  static_assert(C::NS == 6, "buffer constants below");
+  if (0 < nk) issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
+  if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
+  if (3 < nk) issue(std::integral_constant<int, 3>{}, 3);
+  if (4 < nk) issue(std::integral_constant<int, 4>{}, 4);
+  // steps ks (buffer B, even) and ks + 1: o0 holds stage ks's operands
+  auto pair = [&](auto bufc, int ks, Ops& o0, Ops& o1) __attribute__((always_inline)) {
+    constexpr int B = decltype(bufc)::value;
+    load(std::integral_constant<int, (B + 1) % C::NS>{}, o1);
+    mma(o0);
+    if (ks + 2 < nk) {
+      wait_stages(min(nk - 1, ks + 4) - (ks + 3));   // stages ks + 2 and ks + 3 have landed
       sync();
-      if (ks + C::NS - 1 < nk) issue(std::integral_constant<int, (BUF + C::NS - 1) % C::NS>{}, ks + C::NS - 1);
-      load(std::integral_constant<int, (BUF + 1) % C::NS>{}, nxt);
+      if (ks + 5 < nk) issue(std::integral_constant<int, (B + 5) % C::NS>{}, ks + 5);
+      if (ks + 6 < nk) issue(std::integral_constant<int, (B + 6) % C::NS>{}, ks + 6);
+      load(std::integral_constant<int, (B + 2) % C::NS>{}, o0);
     }
-    mma(cur);
+    mma(o1);
   };
   {
     Ops o0, o1;
-    wait_stages(min(nk - 1, C::NS - 2));
+    wait_stages(min(nk - 1, 4) - 1);   // stages 0 and 1 (and at most two more) have landed
     sync();
-    load(I0{}, o0);
-    for (int ks = 0; ks < nk; ks += 2 * C::NS) {
-      step(I0{}, ks, o0, o1);
-      if (ks + 1 < nk) step(I1{}, ks + 1, o1, o0);
-      if (ks + 2 < nk) step(I2{}, ks + 2, o0, o1);
-      if (ks + 3 < nk) step(I3{}, ks + 3, o1, o0);
-      if (ks + 4 < nk) step(I4{}, ks + 4, o0, o1);
-      if (ks + 5 < nk) step(I0{}, ks + 5, o1, o0);
-      if (ks + 6 < nk) step(I1{}, ks + 6, o0, o1);
-      if (ks + 7 < nk) step(I2{}, ks + 7, o1, o0);
-      if (ks + 8 < nk) step(I3{}, ks + 8, o0, o1);
-      if (ks + 9 < nk) step(I4{}, ks + 9, o1, o0);
+    load(std::integral_constant<int, 0>{}, o0);
+    for (int ks = 0; ks < nk; ks += C::NS) {
+      pair(std::integral_constant<int, 0>{}, ks, o0, o1);
+      if (ks + 2 < nk) pair(std::integral_constant<int, 2>{}, ks + 2, o0, o1);
+      if (ks + 4 < nk) pair(std::integral_constant<int, 4>{}, ks + 4, o0, o1);
     }
   }
 
