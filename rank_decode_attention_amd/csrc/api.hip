@@ -324,14 +324,11 @@ palu_status project_impl(const palu_attn_desc* desc, const void* x, int32_t d_mo
   p.n_tok = n_tok; p.d_model = d_model; p.pos0 = pos0;
   p.G = desc->n_groups; p.seq = seq; p.quant = quant ? 1 : 0;
   int64_t col = 0;
-  int max_rank = 0;
   for (int j = 0; j < desc->n_groups; ++j) {
     p.rank[j] = desc->rank_k[j]; p.col_off[j] = col; col += desc->rank_k[j];
-    max_rank = desc->rank_k[j] > max_rank ? desc->rank_k[j] : max_rank;
   }
   for (int j = 0; j < desc->n_groups; ++j) {
     p.rank[desc->n_groups + j] = desc->rank_v[j]; p.col_off[desc->n_groups + j] = col; col += desc->rank_v[j];
-    max_rank = desc->rank_v[j] > max_rank ? desc->rank_v[j] : max_rank;
   }
   p.seq_bytes_k = L.seq_k; p.seq_bytes_v = L.seq_v; p.seq_sbytes_k = L.seq_sk; p.seq_sbytes_v = L.seq_sv;
   for (int j = 0; j < desc->n_groups; ++j) {
@@ -339,7 +336,14 @@ palu_status project_impl(const palu_attn_desc* desc, const void* x, int32_t d_mo
     p.soff_k[j] = L.soff_k[j]; p.soff_v[j] = L.soff_v[j];
     p.pk[j] = (int)L.pk[j]; p.pv[j] = (int)L.pv[j];
   }
-  hipError_t e = launch_project((int)desc->act_dtype, p, max_rank, stream);
+  int64_t ntiles = 0;
+  for (int j = 0; j < desc->n_groups; ++j) ntiles += (desc->rank_k[j] + kColTile - 1) / kColTile + (desc->rank_v[j] + kColTile - 1) / kColTile;
+  if (ntiles > kMaxColTiles) return fail(PALU_ERR_UNSUPPORTED, "more than %d column tiles of %d latent channels", kMaxColTiles, kColTile);
+  // (the kernel addresses A_kv and a 256-token slice of x with 32-bit byte offsets)
+  const int64_t esz = desc->act_dtype == PALU_F32 ? 4 : 2;
+  if (col * d_model * esz > (int64_t)UINT32_MAX || 256 * (int64_t)d_model * esz > (int64_t)UINT32_MAX)
+    return fail(PALU_ERR_UNSUPPORTED, "A_kv larger than 4 GiB");
+  hipError_t e = launch_project((int)desc->act_dtype, p, stream);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   return ok();
 }

@@ -6,6 +6,8 @@
 namespace palu {
 
 constexpr int kMaxLatentRows = 32;   // 2 * max groups
+constexpr int kMaxColTiles = 256;    // column tiles of <= 160 channels (e.g. 32 latent rows of rank <= 1280)
+constexpr int kColTile = 160;        // channels per column tile
 
 struct ProjectParams {
   const void* x;          // [n_tok][D]
@@ -24,9 +26,13 @@ struct ProjectParams {
   // goff_* / soff_* offsets inside a page); NULL for a contiguous cache
   const int* block_table;
   int page_shift, max_pages;
+  // column tiles (filled by launch_project): latent row << 16 | first channel
+  int ntiles;
+  int tile[kMaxColTiles];
 };
 
 // dtype: 0 = fp32, 1 = fp16, 2 = bf16 (x, A and non-quantised latents)
-hipError_t launch_project(int dtype, const ProjectParams& p, int max_rank, hipStream_t stream);
+// (fills p's column-tile list)
+hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream);
 
 }  // namespace palu

@@ -8,12 +8,11 @@
 //
 // Layout: x [n_tok][D] row-major; A is passed as its transpose A^T
 // [n_lat][D] (the weight layout of a Linear(D -> n_lat)), so both MFMA
-// operands are 16-byte contiguous runs of D.  Block = 256 tokens x up to 160
-// latent channels of one latent row (group j of keys or values); 8 waves in a
-// 4 x 2 grid of 64 tokens x 80 channels (two per SIMD); K-steps of 64 bytes
-// per row staged by LDS DMA in a ring of 5 stages (4 requested ahead), the
-// operands of the next stage read into registers while the MFMAs of the
-// current one run.
+// operands are 16-byte contiguous runs of D.  The latent channels are cut
+// into column tiles of at most 160 channels of one latent row (group j of
+// keys or values); a block computes 256 tokens x two consecutive column
+// tiles, 8 waves of 64 tokens x one tile (two per SIMD), with K-steps of 64
+// bytes per row staged by LDS DMA in a ring of 4 stages (3 requested ahead).
 #include "common.h"
 #include "project.h"
 
@@ -26,20 +25,20 @@ struct PrjCfg {
   typedef T_ T;
   static constexpr bool F32 = std::is_same<T, float>::value;
   static constexpr int ESZ = sizeof(T);
-  static constexpr int BM = 256, BN = 160, NW = 8, NT = 512;
-  static constexpr int WM = 4, WN = 2;                   // wave grid: 64 tokens x 80 channels per wave
+  static constexpr int BM = 256, TN = kColTile, NTB = 2, NW = 8, NT = 512;   // tokens, channels of a column tile, tiles per block
+  static constexpr int WM = 4;                           // wave w: tokens 64 (w % 4) .., column tile w / 4
   static constexpr int MT = BM / (16 * WM);              // m-tiles per wave (4)
-  static constexpr int NTL = BN / (16 * WN);             // n-tiles per wave (5)
+  static constexpr int NTL = TN / 16;                    // n-tiles per wave (10)
   static constexpr int ROWB = 64;                        // bytes of a row per K-step: four 16-byte chunks
   static constexpr int BK = ROWB / ESZ;                  // K per step (32 for 16-bit, 16 for fp32)
-  static constexpr int SXS = BM * 4, SAS = BN * 4;       // 16-byte slots of the x and A^T tiles of a stage
+  static constexpr int SXS = BM * 4, SAS = NTB * TN * 4; // 16-byte slots of the x and A^T tiles of a stage
   static constexpr int NIX = SXS / (64 * NW);            // DMA instructions per wave (x)
   static constexpr int NIA = cdiv(SAS, 64 * NW);         // (A^T; the last one only for waves inside the tile)
-  static constexpr int STG = SXS + SAS;                  // slots per stage (26 KB)
-  static constexpr int NS = 6;                           // stages (26 KB each): a ring of 6, refilled two at a time
-  static constexpr int TP = 68;                          // int4 epilogue: floats per staged column (64 tokens + pad)
+  static constexpr int STG = SXS + SAS;                  // slots per stage (36 KB)
+  static constexpr int NS = 4;                           // stages: 3 requested ahead of the one computed
+  static constexpr int TP = 20;                          // int4 epilogue: floats per staged column (16 tokens + pad)
   static_assert(SXS % (64 * NW) == 0 && SAS % 64 == 0, "DMA slots");
-  static_assert(BN * TP <= NS * STG * 4, "epilogue staging");
+  static_assert(NW * TN * TP <= NS * STG * 4, "epilogue staging");
 };
 
 template <class C, class OT>
@@ -53,29 +52,37 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // (wave-uniform: scalar registers)
-  const int wm = w & (C::WM - 1), wn = w / C::WM;
+  const int wm = w % C::WM, wt = w / C::WM;
   const int64_t m0 = (int64_t)blockIdx.x * C::BM;
-  const int j = blockIdx.y;                       // latent row: keys of groups 0..G-1, then values
-  const int r = p.rank[j];
-  const int n0 = blockIdx.z * C::BN;
-  if (n0 >= r) return;
-  const int64_t col0 = p.col_off[j] + n0;         // first row of A^T for this block
-  const int nvalid = min(C::BN, r - n0);
+  // the block's two column tiles (an odd tile count leaves the last block
+  // one tile: its second tile repeats the first and is not stored)
+  const int tb = 2 * blockIdx.y;
+  const int tile[2] = {tb, min(tb + 1, p.ntiles - 1)};
+  int jt[2], n0t[2], nvt[2];
+  int64_t colt[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    jt[t] = p.tile[tile[t]] >> 16;
+    n0t[t] = p.tile[tile[t]] & 0xFFFF;
+    nvt[t] = min(C::TN, p.rank[jt[t]] - n0t[t]);
+    colt[t] = p.col_off[jt[t]] + n0t[t];          // first row of A^T of the tile
+  }
+  const bool store = wt == 0 || tb + 1 < p.ntiles;   // (wave-uniform)
   const T* X = (const T*)p.x;
   const T* A = (const T*)p.A;
   const int64_t D = p.d_model;
 
   // Stage layout: row-major tiles of 64-byte rows (x: BM token rows, then
-  // A^T: BN channel rows), the four 16-byte chunks of row R stored at chunk
-  // position c ^ ((R >> 1) & 3): the LDS serves a 16-byte-per-lane read 8
-  // lanes (128 bytes) at a time, and the 8 rows of such a group (same
-  // logical chunk) then cover 8 distinct 16-byte slots of a 128-byte line
-  // (measured: no bank conflicts, where c ^ ((R >> 2) & 3) had two-way ones).  DMA
-  // instruction m of wave w fills slots (m * NW + w) * 64 + l of a region:
-  // row slot / 4, physical chunk slot % 4.  Rows past the tokens or the
-  // valid channels load the last valid row (never stored).
-  // Per-lane 32-bit byte offsets of the DMA sources inside the block's x
-  // and A^T tiles; the wave-uniform bases advance by one K-step per stage.
+  // A^T: TN channel rows of each column tile), the four 16-byte chunks of
+  // row R stored at chunk position c ^ ((R >> 1) & 3): the LDS serves a
+  // 16-byte-per-lane read 8 lanes (128 bytes) at a time, and the 8 rows of
+  // such a group (same logical chunk) then cover 8 distinct 16-byte slots
+  // of a 128-byte line (measured: no bank conflicts, where c ^ ((R >> 2) & 3)
+  // had two-way ones).  DMA instruction m of wave w fills slots
+  // (m * NW + w) * 64 + l of a region: row slot / 4, physical chunk
+  // slot % 4.  Rows past the tokens or a tile's valid channels load the
+  // last valid row (never stored).  Sources are a wave-uniform base plus a
+  // per-lane 32-bit byte offset; the bases advance by one K-step per stage.
   constexpr int EPC = 16 / C::ESZ;                 // elements per 16-byte chunk
   unsigned xoff[C::NIX], aoff[C::NIA];
 #pragma unroll
@@ -87,21 +94,21 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   }
 #pragma unroll
   for (int m = 0; m < C::NIA; ++m) {
-    const int slot = (m * C::NW + w) * 64 + l;
-    const int row = min(slot >> 2, nvalid - 1), lc = (slot & 3) ^ (((slot >> 2) >> 1) & 3);
-    aoff[m] = (unsigned)(((int64_t)row * D + lc * EPC) * C::ESZ);
+    const int slot = min((m * C::NW + w) * 64 + l, C::SAS - 1);
+    const int row = slot >> 2, lc = (slot & 3) ^ ((row >> 1) & 3);
+    const int t = row / C::TN, r = min(row - t * C::TN, nvt[t] - 1);
+    aoff[m] = (unsigned)(((colt[t] + r) * D + lc * EPC) * C::ESZ);
   }
   const T* xblk = X + m0 * D;
-  const T* ablk = A + col0 * D;
-  // (waves whose slots of an A^T instruction lie past the tile skip it: they
-  // issue one DMA instruction fewer per stage)
+  // (waves whose slots of an A^T instruction lie past the tiles skip it:
+  // they issue one DMA instruction fewer per stage)
   const bool afull = (C::NIA - 1) * C::NW * 64 + w * 64 < C::SAS;
   // stage ks into buffer BUF (a compile-time constant)
   auto issue = [&](auto bufc, int ks) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     const unsigned base = lds_addr(stg) + 16u * (unsigned)(BUF * C::STG);
     const T* xb = xblk + (int64_t)ks * C::BK;
-    const T* ab = ablk + (int64_t)ks * C::BK;
+    const T* ab = A + (int64_t)ks * C::BK;
 #pragma unroll
     for (int m = 0; m < C::NIX; ++m) dma16s(xb, xoff[m], base + 16u * ((m * C::NW + w) * 64));
 #pragma unroll
@@ -110,11 +117,11 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   };
   // wait until at most `after` stages issued after the next one are in flight
   auto wait_stages = [&](int after) __attribute__((always_inline)) {
-    constexpr int N4 = C::NIX + C::NIA, N3 = N4 - 1;
+    constexpr int NF = C::NIX + C::NIA, NP = NF - 1;
     if (afull) {
-      if (after >= 2) wait_vmcnt<2 * N4>(); else if (after == 1) wait_vmcnt<N4>(); else wait_vmcnt<0>();
+      if (after >= 2) wait_vmcnt<2 * NF>(); else if (after == 1) wait_vmcnt<NF>(); else wait_vmcnt<0>();
     } else {
-      if (after >= 2) wait_vmcnt<2 * N3>(); else if (after == 1) wait_vmcnt<N3>(); else wait_vmcnt<0>();
+      if (after >= 2) wait_vmcnt<2 * NP>(); else if (after == 1) wait_vmcnt<NP>(); else wait_vmcnt<0>();
     }
   };
 
@@ -131,28 +138,26 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
   // Every n-tile runs (branch-free, so the operand reads go out ahead of the
   // MFMAs): rows of A^T past the valid channels are copies of the last valid
   // row in LDS, and their columns are not stored.
-  struct Ops { op_t xa[C::MT], bv[C::NTL]; };
-  auto load = [&](auto bufc, Ops& o) __attribute__((always_inline)) {
+  auto step_mma = [&](auto bufc) __attribute__((always_inline)) {
     const uint8_t* sb = (const uint8_t*)stg + decltype(bufc)::value * C::STG * 16;
+    op_t xa[C::MT], bv[C::NTL];
 #pragma unroll
-    for (int a = 0; a < C::MT; ++a) o.xa[a] = *(const op_t*)(sb + (64 * wm + 16 * a) * C::ROWB + lo);
+    for (int a = 0; a < C::MT; ++a) xa[a] = *(const op_t*)(sb + (64 * wm + 16 * a) * C::ROWB + lo);
 #pragma unroll
-    for (int b = 0; b < C::NTL; ++b) o.bv[b] = *(const op_t*)(sb + 16 * C::SXS + (80 * wn + 16 * b) * C::ROWB + lo);
-  };
-  auto mma = [&](const Ops& o) __attribute__((always_inline)) {
+    for (int b = 0; b < C::NTL; ++b) bv[b] = *(const op_t*)(sb + 16 * C::SXS + (C::TN * wt + 16 * b) * C::ROWB + lo);
 #pragma unroll
     for (int b = 0; b < C::NTL; ++b)
 #pragma unroll
       for (int a = 0; a < C::MT; ++a) {
         if constexpr (C::F32) {
           f32x4 c = acc[a][b];
-          c = mfma16x16x4(o.xa[a][0], o.bv[b][0], c);
-          c = mfma16x16x4(o.xa[a][1], o.bv[b][1], c);
-          c = mfma16x16x4(o.xa[a][2], o.bv[b][2], c);
-          c = mfma16x16x4(o.xa[a][3], o.bv[b][3], c);
+          c = mfma16x16x4(xa[a][0], bv[b][0], c);
+          c = mfma16x16x4(xa[a][1], bv[b][1], c);
+          c = mfma16x16x4(xa[a][2], bv[b][2], c);
+          c = mfma16x16x4(xa[a][3], bv[b][3], c);
           acc[a][b] = c;
         } else {
-          acc[a][b] = mfma16x16x32(o.xa[a], o.bv[b], acc[a][b]);
+          acc[a][b] = mfma16x16x32(xa[a], bv[b], acc[a][b]);
         }
       }
   };
@@ -162,48 +167,33 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     asm volatile("" ::: "memory");
   };
 
-  // K loop: stage ks lives in buffer ks % 6, and steps go in pairs (ks even,
-  // ks + 1) with one barrier between them: behind it stages ks + 2 and
-  // ks + 3 have landed (two more stay in flight), and stages ks + 5 and
-  // ks + 6 go into the buffers of stages ks - 1 and ks, whose operands every
-  // wave past the barrier has already used in its MFMAs.  Within a step the
-  // next stage's operands are read while the MFMAs of the current one run.
-  // The loop is unrolled over the ring, so that every buffer index and LDS
+  // K loop: stage ks lives in buffer ks % NS, and NS - 1 stages are
+  // requested ahead.  Step ks waits for stage ks, refills the buffer of
+  // stage ks - 1 (every wave past the barrier has used its operands) and
+  // runs stage ks's operand reads and MFMAs.  One barrier per step; the
+  // loop is unrolled over the ring, so that every buffer index and LDS
   // address offset is a constant.
-  const int nk = (int)(D / C::BK);                  // even (d_model is a multiple of 64)
-  static_assert(C::NS == 6, "buffer constants below");
+  const int nk = (int)(D / C::BK);
+  static_assert(C::NS == 4, "buffer constants below");
   if (0 < nk) issue(std::integral_constant<int, 0>{}, 0);
   if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
   if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
-  if (3 < nk) issue(std::integral_constant<int, 3>{}, 3);
-  if (4 < nk) issue(std::integral_constant<int, 4>{}, 4);
-  // steps ks (buffer B, even) and ks + 1: o0 holds stage ks's operands
-  auto pair = [&](auto bufc, int ks, Ops& o0, Ops& o1) __attribute__((always_inline)) {
+  auto step = [&](auto bufc, int ks) __attribute__((always_inline)) {
     constexpr int B = decltype(bufc)::value;
-    load(std::integral_constant<int, (B + 1) % C::NS>{}, o1);
-    mma(o0);
-    if (ks + 2 < nk) {
-      wait_stages(min(nk - 1, ks + 4) - (ks + 3));   // stages ks + 2 and ks + 3 have landed
-      sync();
-      if (ks + 5 < nk) issue(std::integral_constant<int, (B + 5) % C::NS>{}, ks + 5);
-      if (ks + 6 < nk) issue(std::integral_constant<int, (B + 6) % C::NS>{}, ks + 6);
-      load(std::integral_constant<int, (B + 2) % C::NS>{}, o0);
-    }
-    mma(o1);
-  };
-  {
-    Ops o0, o1;
-    wait_stages(min(nk - 1, 4) - 1);   // stages 0 and 1 (and at most two more) have landed
+    wait_stages(min(nk - 1, ks + C::NS - 2) - ks);
     sync();
-    load(std::integral_constant<int, 0>{}, o0);
-    for (int ks = 0; ks < nk; ks += C::NS) {
-      pair(std::integral_constant<int, 0>{}, ks, o0, o1);
-      if (ks + 2 < nk) pair(std::integral_constant<int, 2>{}, ks + 2, o0, o1);
-      if (ks + 4 < nk) pair(std::integral_constant<int, 4>{}, ks + 4, o0, o1);
-    }
+    if (ks + C::NS - 1 < nk) issue(std::integral_constant<int, (B + C::NS - 1) % C::NS>{}, ks + C::NS - 1);
+    step_mma(bufc);
+  };
+  for (int ks = 0; ks < nk; ks += C::NS) {
+    step(std::integral_constant<int, 0>{}, ks);
+    if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
+    if (ks + 2 < nk) step(std::integral_constant<int, 2>{}, ks + 2);
+    if (ks + 3 < nk) step(std::integral_constant<int, 3>{}, ks + 3);
   }
 
-  // ---- epilogue
+  // ---- epilogue: this wave's column tile
+  const int j = jt[wt], n0 = n0t[wt], nvalid = nvt[wt], r = p.rank[j];
   const int gj = j % p.G, is_v = j >= p.G;
   const int pitch = is_v ? p.pv[gj] : p.pk[gj];
   // block of latent row t of the written sequence (paged: the page holding
@@ -223,6 +213,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
            tin * pitch;
   };
   if (p.quant == 0) {
+    if (!store) return;
 #pragma unroll
     for (int a = 0; a < C::MT; ++a)
 #pragma unroll
@@ -232,11 +223,11 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
           uint8_t* rowp = zrow(p.pos0 + tok);
 #pragma unroll
           for (int b = 0; b < C::NTL; ++b) {
-            const int n = 80 * wn + 16 * b + rr;
+            const int n = 16 * b + rr;
             if (n < nvalid) store_elem<C, T>(rowp + (n0 + n) * C::ESZ, from_f32<T>(acc[a][b][e]));
           }
-          // zero the row padding (pitch beyond the rank) once, from the last block
-          if (wn == 0 && n0 + C::BN >= r) {
+          // zero the row padding (pitch beyond the rank) once, from the row's last tile
+          if (n0 + C::TN >= r) {
             const int padn = pitch / C::ESZ;
             for (int n = r + rr; n < padn; n += 16) store_elem<C, T>(rowp + n * C::ESZ, from_f32<T>(0.f));
           }
@@ -244,10 +235,13 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
       }
   } else {
     // Quantise per (token, 32-element chunk) exactly as palu_quant_latent.
-    // The block stages 64 tokens at a time (m-tile a of every wave row) in
-    // LDS, transposed ([channel][token], 16-byte writes of a lane's four
-    // consecutive tokens), then a thread takes one (token, chunk) each.
-    float* zs = (float*)stg;
+    // Each wave stages one 16-token m-tile at a time in its own LDS region,
+    // transposed ([channel][token], 16-byte writes of a lane's four
+    // consecutive tokens), then its lanes take one (token, chunk) each.
+    wait_lgkm0();
+    __syncthreads();   // every wave's operand reads of the stages are done
+    if (!store) return;
+    float* zs = (float*)stg + w * (C::TN * C::TP);
     const int nc_row = cdiv(r, 32);
     auto srow = [&](int64_t t) __attribute__((always_inline)) {
       int64_t tin;
@@ -258,15 +252,13 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     const int nchunk = cdiv(nvalid, 32);
 #pragma unroll
     for (int a = 0; a < C::MT; ++a) {
-      wait_lgkm0();
-      __syncthreads();   // the stages (first round) or the previous round's staged tile are read
+      wait_lgkm0();   // (the previous m-tile's reads are done before it is overwritten)
 #pragma unroll
-      for (int b = 0; b < C::NTL; ++b)
-        *(f32x4*)(zs + (80 * wn + 16 * b + rr) * C::TP + 16 * wm + 4 * kq) = acc[a][b];
-      __syncthreads();
-      if (tid < 64 * nchunk) {
-        const int trow = tid & 63, c = tid >> 6;
-        const int64_t tok = m0 + 64 * (trow >> 4) + 16 * a + (trow & 15);
+      for (int b = 0; b < C::NTL; ++b) *(f32x4*)(zs + (16 * b + rr) * C::TP + 4 * kq) = acc[a][b];
+      wait_lgkm0();
+      for (int it = l; it < 16 * nchunk; it += 64) {
+        const int trow = it & 15, c = it >> 4;
+        const int64_t tok = m0 + 64 * wm + 16 * a + trow;
         const int cg = n0 / 32 + c;                // chunk index within the latent row
         const int n = min(32, r - cg * 32);
         if (tok < p.n_tok) {
@@ -317,18 +309,27 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
 }
 
 template <class C>
-static hipError_t launch_c(const ProjectParams& p, int max_rank, hipStream_t stream) {
-  dim3 grid((unsigned)cdiv64(p.n_tok, C::BM), (unsigned)(2 * p.G), (unsigned)cdiv(max_rank, C::BN));
+static hipError_t launch_c(const ProjectParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)cdiv64(p.n_tok, C::BM), (unsigned)cdiv(p.ntiles, C::NTB));
   hipLaunchKernelGGL(palu_project_kernel<C>, grid, dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_project(int dtype, const ProjectParams& p, int max_rank, hipStream_t stream) {
+hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream) {
   if (p.n_tok == 0) return hipSuccess;
+  // column tiles of at most 160 channels: every latent row in order, split
+  // where its rank exceeds 160; a block takes two consecutive tiles
+  p.ntiles = 0;
+  for (int j = 0; j < 2 * p.G; ++j)
+    for (int n0 = 0; n0 < p.rank[j]; n0 += kColTile) {
+      if (p.ntiles >= kMaxColTiles || n0 > 0xFFFF) return hipErrorInvalidValue;
+      p.tile[p.ntiles++] = j << 16 | n0;
+    }
+  if (p.ntiles == 0) return hipSuccess;
   switch (dtype) {
-    case 0: return launch_c<PrjCfg<float>>(p, max_rank, stream);
-    case 1: return launch_c<PrjCfg<_Float16>>(p, max_rank, stream);
-    case 2: return launch_c<PrjCfg<__bf16>>(p, max_rank, stream);
+    case 0: return launch_c<PrjCfg<float>>(p, stream);
+    case 1: return launch_c<PrjCfg<_Float16>>(p, stream);
+    case 2: return launch_c<PrjCfg<__bf16>>(p, stream);
   }
   return hipErrorInvalidValue;
 }

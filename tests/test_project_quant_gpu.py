@@ -247,3 +247,54 @@ def test_project_int4_fused(name, wl, n_tok, seq, pos0, sample):
             assert np.all(np.abs(deq - z) <= s_each * (0.5 + 2.0 ** -9) + 1e-6), f"{name}: dequantised off"
     assert n_code <= max(1, n_total // 1000), f"{name}: {n_code} of {n_total} codes differ"
     print(name, "code mismatches", n_code, "of", n_total)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "i4"])
+def test_project_uneven_column_tiles(fmt):
+    """Key and value ranks that differ, rows of several 160-channel column
+    tiles with short last tiles (330 = 160 + 160 + 10, 161 = 160 + 1) and an
+    odd tile count (7: the last block carries one tile), 300 tokens (a
+    ragged 256-token block): every element against the oracle."""
+    import torch
+    import rank_decode_attention_amd as R
+    rank_k, rank_v = [100, 330], [161, 40]
+    d_model, n_tok, max_len, seq, pos0 = 256, 300, 320, 1, 11
+    desc = R.AttnDesc(8, 8, 128, 2, rank_k, rank_v, use_rope=True, latent_dtype=fmt, act_dtype="bf16")
+    rng = np.random.default_rng(2024)
+    x = PI.to_format(rng.standard_normal((n_tok, d_model), dtype=np.float32), "bf16")
+    As = [PI.to_format(rng.standard_normal((d_model, r), dtype=np.float32) / np.float32(np.sqrt(d_model)), "bf16")
+          for r in rank_k + rank_v]
+    A_kv = np.concatenate([a.T for a in As], axis=0)
+    cache = R.alloc_cache(desc, 2, max_len)
+    for t in (cache.zk, cache.zv, cache.sk, cache.sv):
+        if t is not None:
+            t.fill_(0x5A)
+    R.palu_project(desc, to_device(x, "bf16"), to_device(np.ascontiguousarray(A_kv), "bf16"), cache, seq, pos0)
+    torch.cuda.synchronize()
+    host = {k: (None if t is None else t.cpu().numpy()) for k, t in
+            (("zk", cache.zk), ("zv", cache.zv), ("sk", cache.sk), ("sv", cache.sv))}
+    wl = PI.scaled("int4_prefill", max_len=max_len, batch=2, d_model=d_model)
+    xs = oracle.upcast(x, "bf16")
+    for which in (0, 1):
+        for j in range(2):
+            r = (rank_k if which == 0 else rank_v)[j]
+            z = oracle.project(xs, oracle.upcast(As[which * 2 + j], "bf16"))
+            rows = _rows_of(desc, host, wl, which, j, seq, pos0, n_tok)
+            if fmt == "bf16":
+                got = oracle.upcast(rows.view(np.uint16)[:, :r], "bf16")
+                gamma = d_model * 2.0 ** -24 / (1 - d_model * 2.0 ** -24)
+                bound = gamma * (np.abs(xs) @ np.abs(oracle.upcast(As[which * 2 + j], "bf16")))
+                assert np.all(np.abs(got - z) <= 0.5 * _ulp(z, "bf16") + bound), f"{which}/{j}: projection off"
+                assert np.all(rows.view(np.uint16)[:, r:] == 0), f"{which}/{j}: padding not zero"
+            else:
+                codes = oracle.unpack_int4(rows, r)
+                s = _rows_of(desc, host, wl, which, j, seq, pos0, n_tok, scales=True).view(np.float16)
+                ref_c, _ = oracle.quant_int4(z.astype(np.float32))
+                dq = np.abs(codes.astype(int) - ref_c.astype(int))
+                assert dq.max() <= 1 and (dq != 0).sum() <= max(1, dq.size // 1000), f"{which}/{j}: codes off"
+                deq = oracle.dequant_int4(codes, s)
+                s_each = np.repeat(s.astype(np.float64), 32, axis=-1)[..., :r]
+                assert np.all(np.abs(deq - z) <= s_each * (0.5 + 2.0 ** -9) + 1e-6), f"{which}/{j}: dequantised off"
+            # rows of the other sequence are untouched
+            other = _rows_of(desc, host, wl, which, j, 0, 0, max_len)
+            assert np.all(other == 0x5A), f"{which}/{j}: other sequence written"
