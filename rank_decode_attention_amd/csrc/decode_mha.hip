@@ -158,7 +158,10 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
 #pragma unroll
     for (int m = 0; m < NSI; ++m) {
       const int q = (m * C::NW + w) * 64 + l;     // 16-byte slot of the staged chunk
-      const int row = q >> 6, col = (q & 63) * 8;
+      // (row R's 16-byte chunk c lands at chunk position c ^ 2 (R & 3): the
+      // transposed reads below take 32 bytes from each of 4 consecutive rows
+      // of 1 KB, which the swizzle puts on 4 distinct 32-byte bank groups)
+      const int row = q >> 6, col = ((q & 63) ^ (2 * (row & 3))) * 8;
       const int kr = min(kc * 32 + row, rk - 1);
       dma16(Bg + (int64_t)kr * W + col, lds_addr(slots[slot]) + 16u * ((m * C::NW + w) * 64));
     }
@@ -173,8 +176,11 @@ __global__ void __launch_bounds__(512, 1) palu_decode_mha_kernel(const DecodePar
       // real row of B_k; int4: element i is rank 32 kc + 8 kq + i, set to
       // zero past the rank, so that the codes the cache holds there, which
       // the tiles carry unmasked, meet zero rows)
-      const i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * W + i0 + 4 * (s & 3));
-      const i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * W + i0 + 4 * (s & 3));
+      // (element el of rows 8 kq + s / 4 and 8 kq + 4 + s / 4, in the
+      // swizzled chunk positions of the staging)
+      const int el = i0 + 4 * (s & 3), pel = (((el >> 3) ^ (2 * (s >> 2))) << 3) | (el & 7);
+      const i16x4 lo = ds_read_tr16(sb + (8 * kq + (s >> 2)) * W + pel);
+      const i16x4 hi = ds_read_tr16(sb + (8 * kq + 4 + (s >> 2)) * W + pel);
       s8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       if constexpr (C::Q4) {
 #pragma unroll
