@@ -68,9 +68,9 @@ struct MhaCfg {
   static constexpr bool BREG_V = Q4 && NKC <= 5;
   static constexpr int AP = 17;                // angle-table row pitch in 16-byte units (68 floats)
   // int4: per-token scales of a tile's 32-rank chunks, fp32, [slot][row][SCP]
-  // (the pitch keeps the two 16-byte reads of a row aligned and spreads rows
-  // over the banks)
-  static constexpr int SCP = 12;
+  // (an odd pitch puts the rows that 32 consecutive lanes write, and the 16
+  // rows a half-wave reads, on distinct banks)
+  static constexpr int SCP = 9;
   static constexpr int NSK = Q4 ? NKB : 1, NSV = Q4 ? NVB : 1;
   static constexpr int STGB = 32 * DH * NH * 2;   // bytes of one staged B_k chunk (32 ranks x 512 columns)
   static_assert(NDT * 16 * NT == TILEB, "tile DMA");
