@@ -223,7 +223,9 @@ palu_status palu_dequant_latent(const void* codes, const void* scales, int64_t n
  * Errors: INVALID_ARG for null pointers, d_model <= 0, n_tok < 0, seq < 0,
  * pos0 < 0, pos0 + n_tok > max_len, misaligned buffers (x, A_kv and latent
  * buffers must be 16-byte aligned); UNSUPPORTED when latent_dtype is neither
- * act_dtype nor I4, or d_model is not a multiple of 64.
+ * act_dtype nor I4, d_model is not a multiple of 64, the latent rows need more
+ * than 256 column tiles of 160 channels (sum over rows of ceil(rank / 160)),
+ * or A_kv exceeds 4 GiB.
  */
 palu_status palu_project(const palu_attn_desc* desc, const void* x, int32_t d_model, int64_t n_tok,
                          const void* A_kv, const palu_latent_cache* cache, int32_t seq, int32_t pos0,

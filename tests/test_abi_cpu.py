@@ -159,3 +159,7 @@ def test_project_argument_errors(lib):
     d4 = _desc(latent_dtype="i4", act_dtype="f16")
     assert lib.palu_project(d4.ref(), p, 4096, 8, p, ctypes.byref(cache), 0, 0, None) == INVALID  # no scales
     assert lib.palu_project(d.ref(), p, 4096, 0, p, ctypes.byref(cache), 0, 0, None) == 0         # nothing to do
+    # latent rows are cut into column tiles of 160 channels, at most 256 per call:
+    # 32 rows of rank 1280 fit (8 tiles each), rank 1300 (9 each) does not
+    wide = _desc(n_groups=16, rank_k=[1300] * 16)
+    assert lib.palu_project(wide.ref(), p, 4096, 8, p, ctypes.byref(cache), 0, 0, None) == UNSUP
