@@ -22,8 +22,9 @@ namespace palu {
 // elements and stores their 4 bytes of codes (a chunk's 16 bytes are the
 // quad's 4 stores); lane 0 stores the scale.
 // code = rint(fl(z / s)) needs the correctly rounded binary32 quotient only
-// where it decides the rounding: t = z * fl(1 / s) lies within 1.5e-6 of
-// fl(z / s) for |t| < 8 (two roundings of relative size 2^-24 each), so
+// where it decides the rounding: with 1/s known within one ulp, t = z * (1/s)
+// lies within 1.9e-6 of fl(z / s) for |t| < 8 (relative errors 2^-23 for the
+// reciprocal, 2^-24 for the product and 2^-24 for fl(z / s) itself), so
 // rint(t) is the code unless t is within 4e-6 of a half-integer, where the
 // exact quotient is formed (also beyond |t| >= 8, where both clamp to +-7).
 // A lane's 8 elements are read as the whole 16-byte blocks that hold them
@@ -78,6 +79,17 @@ __device__ __forceinline__ void piece_values(const Piece<T>& pc, int n, float (&
   const T* el = (const T*)o;
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = i < n ? to_f32(el[i]) : 0.f;
+}
+
+// fl(a / 7) for finite a >= 0 without a divide: q0 = fl(a * fl(1/7)) is
+// corrected once by its exact residual a - 7 q0 (an fma, exact in binary32).
+// Checked against the correctly rounded quotient for every non-negative
+// finite binary32 a (tests/test_quant_host.py: on a sample of every
+// binade, and on all 2^31 - 2^23 values with PALU_EXHAUSTIVE=1).
+__device__ __forceinline__ float div7_rn(float a) {
+  const float c = 1.0f / 7.0f;   // fl(1/7), folded at compile time
+  const float q0 = a * c;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 7.0f, a), c, q0);
 }
 
 // t within 4e-6 of a half-integer (|t - rint(t)| <= 1/2 always; beyond
@@ -139,12 +151,17 @@ __device__ __forceinline__ void quant_quad(float (&v)[8], int qi, int c, int r, 
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = fmaxf(amax, dpp<0xB1>(amax));
   amax = fmaxf(amax, dpp<0x4E>(amax));
-  const float s32 = __fdiv_rn(amax, 7.0f);
+  float s32 = div7_rn(amax);
+  // (held as binary32: the compiler would otherwise fuse the last fma with
+  // the conversion below into one fma rounding straight to fp16)
+  asm volatile("" : "+v"(s32));
   const _Float16 s16 = (_Float16)s32;
   const float sf = (float)s16;
   unsigned word = 0u;   // element 8 qi + i in nibble i
   if (sf != 0.f) {
-    const float inv = __fdiv_rn(1.0f, sf);
+    // 1/s within one ulp: the hardware reciprocal and one Newton step
+    const float r0 = __builtin_amdgcn_rcpf(sf);
+    const float inv = __builtin_fmaf(r0, __builtin_fmaf(-sf, r0, 1.0f), r0);
     float qf[8];
     bool near = false;
 #pragma unroll
@@ -173,11 +190,13 @@ __device__ __forceinline__ void quant_quad(float (&v)[8], int qi, int c, int r, 
   }
 }
 
-// A wave quantises 64 consecutive chunks (of the flattened (row, chunk)
+// A wave quantises 32 consecutive chunks (of the flattened (row, chunk)
 // list) in kQRounds rounds of 16: in round k, lane l takes quarter l % 4 of
-// chunk 16 k + l / 4.  Every round's loads are issued before any chunk is
-// quantised, so that a wave keeps 4 KB of rows in flight.
-constexpr int kQRounds = 4;
+// chunk 16 k + l / 4.  Both rounds' loads are issued before any chunk is
+// quantised (measured: two rounds per wave, twice the waves, about 3%
+// faster than four rounds, which leave the last wave of blocks of each CU
+// partly idle).
+constexpr int kQRounds = 2;
 
 template <class T, bool ROT>
 __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z, int64_t n_rows, int r,
@@ -224,7 +243,7 @@ template <class T, bool ROT>
 static hipError_t launch_q(const void* z, int64_t n_rows, int r, int64_t stride, void* codes, void* scales,
                            hipStream_t stream) {
   const int nc = cdiv(r, 32);
-  const int64_t work = n_rows * nc;     // chunks, 4 lanes each, 64 per wave
+  const int64_t work = n_rows * nc;     // chunks, 4 lanes each, 16 kQRounds per wave
   if (work == 0) return hipSuccess;
   const unsigned magic = (unsigned)((0xFFFFFFFFull / (unsigned)nc) + 1);   // ceil(2^32 / nc) for nc > 1
   const int64_t blocks = cdiv64(work, 4 * 16 * kQRounds);
