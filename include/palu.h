@@ -381,7 +381,8 @@ size_t palu_decode_chunk_workspace_bytes(const palu_attn_desc* desc, int32_t bat
  * palu_profile_events - timing hook for benchmark harnesses (not part of the
  * method).  When both are set (non-NULL), every later palu_decode_attn call
  * on the calling thread launches its main decode kernel (the one that reads
- * the latent cache, before the merge) with
+ * the latent cache, before the merge), and every later palu_project call its
+ * projection kernel, with
  * hipExtLaunchKernel, which stamps `before_main` at the kernel's start and
  * `after_main` at its end, so that hipEventElapsedTime gives that kernel's
  * duration.  The caller owns the events (hipEventCreate) and must keep them

@@ -293,7 +293,8 @@ def decode_workspace_bytes(desc: AttnDesc, batch: int, max_len: int) -> int:
 
 def palu_profile_events(before_main, after_main):
     """Set (or clear with None, None) HIP events that palu_decode_attn records
-    around its main kernel on the calling thread (palu_profile_events)."""
+    around its main kernel, and palu_project around its projection kernel, on
+    the calling thread (palu_profile_events)."""
     _check(load().palu_profile_events(before_main, after_main))
 
 

@@ -343,7 +343,9 @@ palu_status project_impl(const palu_attn_desc* desc, const void* x, int32_t d_mo
   const int64_t esz = desc->act_dtype == PALU_F32 ? 4 : 2;
   if (col * d_model * esz > (int64_t)UINT32_MAX || 256 * (int64_t)d_model * esz > (int64_t)UINT32_MAX)
     return fail(PALU_ERR_UNSUPPORTED, "A_kv larger than 4 GiB");
-  hipError_t e = launch_project((int)desc->act_dtype, p, stream);
+  const bool prof = g_prof_before && g_prof_after;
+  hipError_t e = launch_project((int)desc->act_dtype, p, stream, prof ? g_prof_before : nullptr,
+                                prof ? g_prof_after : nullptr);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   return ok();
 }

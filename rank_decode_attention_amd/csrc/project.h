@@ -32,7 +32,9 @@ struct ProjectParams {
 };
 
 // dtype: 0 = fp32, 1 = fp16, 2 = bf16 (x, A and non-quantised latents)
-// (fills p's column-tile list)
-hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream);
+// (fills p's column-tile list).  With t0 and t1 set the kernel is launched by
+// hipExtLaunchKernel, which records them at its start and end.
+hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream, hipEvent_t t0 = nullptr,
+                          hipEvent_t t1 = nullptr);
 
 }  // namespace palu

@@ -16,6 +16,7 @@
 #include "common.h"
 #include "project.h"
 
+#include <hip/hip_ext.h>
 #include <type_traits>
 
 namespace palu {
@@ -237,7 +238,7 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
     // Quantise per (token, 32-element chunk) exactly as palu_quant_latent.
     // Each wave stages one 16-token m-tile at a time in its own LDS region,
     // transposed ([channel][token], 16-byte writes of a lane's four
-    // consecutive tokens), then its lanes take one (token, chunk) each.
+    // consecutive tokens), then four lanes take each (token, chunk).
     wait_lgkm0();
     __syncthreads();   // every wave's operand reads of the stages are done
     if (!store) return;
@@ -250,58 +251,83 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
              (is_v ? p.soff_v[gj] : p.soff_k[gj]) + tin * 2 * nc_row;
     };
     const int nchunk = cdiv(nvalid, 32);
+    // lane l: token l / 4 of the m-tile, elements 8 (l % 4) .. + 7 of every
+    // chunk (the quad's amax crosses its four lanes by DPP); one round per
+    // 32-element chunk of the tile
+    const int qi = l & 3, trow = l >> 2;
 #pragma unroll
     for (int a = 0; a < C::MT; ++a) {
       wait_lgkm0();   // (the previous m-tile's reads are done before it is overwritten)
 #pragma unroll
       for (int b = 0; b < C::NTL; ++b) *(f32x4*)(zs + (16 * b + rr) * C::TP + 4 * kq) = acc[a][b];
       wait_lgkm0();
-      for (int it = l; it < 16 * nchunk; it += 64) {
-        const int trow = it & 15, c = it >> 4;
-        const int64_t tok = m0 + 64 * wm + 16 * a + trow;
-        const int cg = n0 / 32 + c;                // chunk index within the latent row
-        const int n = min(32, r - cg * 32);
-        if (tok < p.n_tok) {
-          const float* vs = zs + (32 * c) * C::TP + trow;
-          float v[32];
+      const int64_t tok = m0 + 64 * wm + 16 * a + trow;
+      const bool live = tok < p.n_tok;        // (the same for the four lanes of a quad)
+      uint8_t* crow = nullptr;
+      _Float16* srw = nullptr;
+      if (live) {
+        crow = zrow(p.pos0 + tok);
+        srw = (_Float16*)srow(p.pos0 + tok);
+      }
 #pragma unroll
-          for (int i = 0; i < 32; ++i) v[i] = i < n ? vs[i * C::TP] : 0.f;
-          float amax = 0.f;
+      for (int c = 0; c < C::TN / 32; ++c) {
+        if (c >= nchunk) break;                // (wave-uniform)
+        const int cg = n0 / 32 + c;            // chunk index within the latent row
+        const int nv = min(32, r - cg * 32) - 8 * qi;   // valid elements of this lane
+        const float* vs = zs + (32 * c + 8 * qi) * C::TP + trow;
+        float v[8];
+        if (cg * 32 + 32 <= r) {               // (wave-uniform) a whole chunk: no masking
 #pragma unroll
-          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-          const float s32 = __fdiv_rn(amax, 7.0f);
-          const _Float16 s16 = (_Float16)s32;
-          const float sf = (float)s16;
-          unsigned int words[4] = {0u, 0u, 0u, 0u};
-          if (sf != 0.f) {
-            // code = rint(fl(z / s)): t = z * fl(1 / s) is within 1.5e-6 of
-            // fl(z / s) for |t| < 8, so rint(t) is the code unless t lies
-            // within 4e-6 of a half-integer, where the correctly rounded
-            // quotient is formed (for |t| >= 8 both clamp to +-7)
-            const float inv = __fdiv_rn(1.0f, sf);
-            float qf[32];
-            bool near = false;
+          for (int i = 0; i < 8; ++i) v[i] = vs[i * C::TP];
+        } else {                               // the row's last, partial chunk: zero past the rank
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+          for (int i = 0; i < 8; ++i) v[i] = i < nv ? vs[i * C::TP] : 0.f;
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, dpp<0xB1>(amax));
+        amax = fmaxf(amax, dpp<0x4E>(amax));
+        // s = fl(amax / 7): the product by fl(1/7) corrected once by its exact
+        // residual (equal to the correctly rounded quotient for every
+        // non-negative binary32), held as binary32 before the fp16 rounding
+        const float q0 = amax * (1.0f / 7.0f);
+        float s32 = __builtin_fmaf(__builtin_fmaf(-q0, 7.0f, amax), 1.0f / 7.0f, q0);
+        asm volatile("" : "+v"(s32));
+        const _Float16 s16 = (_Float16)s32;
+        const float sf = (float)s16;
+        unsigned word = 0u;   // element 8 qi + i in nibble i
+        if (sf != 0.f) {
+          // code = rint(fl(z / s)): with 1/s within one ulp, t = z * (1/s) is
+          // within 1.9e-6 of fl(z / s) for |t| < 8, so rint(t) is the code
+          // unless t lies within 4e-6 of a half-integer, where the correctly
+          // rounded quotient is formed (for |t| >= 8 both clamp to +-7)
+          const float r0 = __builtin_amdgcn_rcpf(sf);
+          const float inv = __builtin_fmaf(r0, __builtin_fmaf(-sf, r0, 1.0f), r0);
+          float qf[8];
+          bool near = false;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float t = v[i] * inv;
+            qf[i] = rintf(t);
+            near |= fabsf(t - qf[i]) > 0.5f - 4e-6f;
+          }
+          if (near) {   // (rare)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
               const float t = v[i] * inv;
-              qf[i] = rintf(t);
-              near |= fabsf(t - qf[i]) > 0.5f - 4e-6f;
-            }
-            if (near) {   // (rare)
-#pragma unroll
-              for (int i = 0; i < 32; ++i) {
-                const float t = v[i] * inv;
-                if (fabsf(t - rintf(t)) > 0.5f - 4e-6f) qf[i] = rintf(__fdiv_rn(v[i], sf));
-              }
-            }
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-              const int q = (int)__builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
-              words[i >> 3] |= (unsigned int)(q & 0xF) << (4 * (i & 7));
+              if (fabsf(t - rintf(t)) > 0.5f - 4e-6f) qf[i] = rintf(__fdiv_rn(v[i], sf));
             }
           }
-          *(uint4*)(zrow(p.pos0 + tok) + 16 * cg) = make_uint4(words[0], words[1], words[2], words[3]);
-          ((_Float16*)srow(p.pos0 + tok))[cg] = s16;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int q = (int)__builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
+            word |= (unsigned)(q & 0xF) << (4 * i);
+          }
+        }
+        if (live) {
+          *(unsigned*)(crow + 16 * cg + 4 * qi) = word;
+          if (qi == 0) srw[cg] = s16;
         }
       }
     }
@@ -309,13 +335,16 @@ __global__ void __launch_bounds__(C::NT, 1) palu_project_kernel(const ProjectPar
 }
 
 template <class C>
-static hipError_t launch_c(const ProjectParams& p, hipStream_t stream) {
+static hipError_t launch_c(const ProjectParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   dim3 grid((unsigned)cdiv64(p.n_tok, C::BM), (unsigned)cdiv(p.ntiles, C::NTB));
-  hipLaunchKernelGGL(palu_project_kernel<C>, grid, dim3(C::NT), 0, stream, p);
+  if (t0 && t1)
+    hipExtLaunchKernelGGL(palu_project_kernel<C>, grid, dim3(C::NT), 0, stream, t0, t1, 0, p);
+  else
+    hipLaunchKernelGGL(palu_project_kernel<C>, grid, dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream) {
+hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (p.n_tok == 0) return hipSuccess;
   // column tiles of at most 160 channels: every latent row in order, split
   // where its rank exceeds 160; a block takes two consecutive tiles
@@ -327,9 +356,9 @@ hipError_t launch_project(int dtype, ProjectParams& p, hipStream_t stream) {
     }
   if (p.ntiles == 0) return hipSuccess;
   switch (dtype) {
-    case 0: return launch_c<PrjCfg<float>>(p, stream);
-    case 1: return launch_c<PrjCfg<_Float16>>(p, stream);
-    case 2: return launch_c<PrjCfg<__bf16>>(p, stream);
+    case 0: return launch_c<PrjCfg<float>>(p, stream, t0, t1);
+    case 1: return launch_c<PrjCfg<_Float16>>(p, stream, t0, t1);
+    case 2: return launch_c<PrjCfg<__bf16>>(p, stream, t0, t1);
   }
   return hipErrorInvalidValue;
 }
