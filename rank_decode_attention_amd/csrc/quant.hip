@@ -163,26 +163,30 @@ __device__ __forceinline__ void quant_quad(float (&v)[8], int qi, int c, int r, 
     const float r0 = __builtin_amdgcn_rcpf(sf);
     const float inv = __builtin_fmaf(r0, __builtin_fmaf(-sf, r0, 1.0f), r0);
     float qf[8];
-    bool near = false;
+    float dmax = 0.f;   // the largest |t - rint(t)| of the lane's elements
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float t = v[i] * inv;
       qf[i] = rintf(t);
-      near |= near_half(t, qf[i]);
+      dmax = fmaxf(dmax, fabsf(t - qf[i]));
     }
-    if (near) {   // (rare) the exact quotient where it decides the rounding
+    if (dmax > 0.5f - 4e-6f) {   // (rare) the exact quotient where it decides the rounding
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float t = v[i] * inv;
         if (near_half(t, rintf(t))) qf[i] = rintf(__fdiv_rn(v[i], sf));
       }
     }
+    // nibble i = q_i & 15: 0x88888888 + sum q_i 16^i holds q_i + 8 (1 .. 15,
+    // no carries) in nibble i, and q + 8 = (q & 15) ^ 8 for -8 <= q <= 7
+    word = 0x88888888u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // (elements past the row are zero: code 0)
       const int q = (int)__builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
-      word |= (unsigned)(q & 0xF) << (4 * i);
+      word += (unsigned)q << (4 * i);
     }
+    word ^= 0x88888888u;
   }
   if (live) {
     *(unsigned*)(crow + 16 * c + 4 * qi) = word;
