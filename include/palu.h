@@ -158,7 +158,8 @@ int64_t palu_latent_offset(const palu_attn_desc* desc, int32_t max_len, int32_t 
  * even, code = 0 where s == 0.  Pad nibbles are written as zero.
  * n_rows == 0 is a no-op after the argument checks (pointers may be NULL).
  * Errors: INVALID_ARG for null pointers, n_rows < 0, r <= 0, z_row_stride < r,
- * codes not 16-byte aligned; UNSUPPORTED for z_dtype == I4.
+ * codes not 16-byte aligned; UNSUPPORTED for z_dtype == I4 and for rows
+ * more than 64 MiB apart (z_row_stride times the element size).
  */
 palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows, int32_t r,
                               int64_t z_row_stride, void* codes, void* scales, hipStream_t stream);

@@ -625,6 +625,8 @@ palu_status palu_quant_latent(const void* z, palu_dtype z_dtype, int64_t n_rows,
   if (n_rows == 0) return ok();
   if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (z_row_stride > (int64_t)kQuantMaxStrideBytes / (z_dtype == PALU_F32 ? 4 : 2))
+    return fail(PALU_ERR_UNSUPPORTED, "z_row_stride above %u bytes", kQuantMaxStrideBytes);
   hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream);
   if (e != hipSuccess) return hip_fail(e, "quantiser launch");
   return ok();
@@ -638,6 +640,8 @@ palu_status palu_quant_latent_rotated(const void* z, palu_dtype z_dtype, int64_t
   if (n_rows == 0) return ok();
   if (!z || !codes || !scales) return fail(PALU_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(codes)) return fail(PALU_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (z_row_stride > (int64_t)kQuantMaxStrideBytes / (z_dtype == PALU_F32 ? 4 : 2))
+    return fail(PALU_ERR_UNSUPPORTED, "z_row_stride above %u bytes", kQuantMaxStrideBytes);
   hipError_t e = launch_quant((int)z_dtype, z, n_rows, r, z_row_stride, codes, scales, stream, true);
   if (e != hipSuccess) return hip_fail(e, "quantiser launch");
   return ok();

@@ -6,6 +6,10 @@
 namespace palu {
 // dtype: 0 = fp32, 1 = fp16, 2 = bf16 input rows; rotate: quantise z H on
 // every full 32-element chunk (H the Sylvester Hadamard matrix of order 32)
+// Largest distance between consecutive input rows of the quantiser, in
+// bytes (its loads use 32-bit offsets spanning up to 34 rows).
+constexpr unsigned kQuantMaxStrideBytes = 1u << 26;
+
 hipError_t launch_quant(int dtype, const void* z, int64_t n_rows, int r, int64_t stride, void* codes,
                         void* scales, hipStream_t stream, bool rotate = false);
 

@@ -28,10 +28,13 @@ namespace palu {
 // rint(t) is the code unless t is within 4e-6 of a half-integer, where the
 // exact quotient is formed (also beyond |t| >= 8, where both clamp to +-7).
 // A lane's 8 elements are read as the whole 16-byte blocks that hold them
-// (two for 16-bit elements, three for binary32; a block is loaded only if
-// it holds bytes of the piece, so no load leaves the pages of the row) and
-// realigned in registers; loads and realignment are separate steps so that
-// a wave issues several pieces' loads before it uses any.
+// (two for 16-bit elements, three for binary32) and realigned in registers;
+// blocks are addressed by 32-bit byte offsets from a 16-byte-aligned,
+// wave-uniform row base, each clamped to the block of the piece's last byte
+// (a lane without elements reads the base block), so every load reads a
+// block holding bytes of the input and none leaves its pages; loads and
+// realignment are separate steps so that a wave issues several pieces'
+// loads before it uses any.
 template <class T>
 struct Piece {
   static constexpr int NS = 8 * (int)sizeof(T) / 16 + 1;   // 16-byte blocks a piece can touch
@@ -39,17 +42,15 @@ struct Piece {
   unsigned sh;                                           // the piece's byte offset in its first block
 };
 
+// zb: 16-byte aligned and wave-uniform; off: the piece's byte offset from
+// zb; n: its elements (0..8)
 template <class T>
-__device__ __forceinline__ void piece_load(Piece<T>& pc, const T* p, int n) {
-  const uintptr_t a = (uintptr_t)p;
-  const uintptr_t base = a & ~(uintptr_t)15;
-  const uintptr_t end = a + (uintptr_t)n * sizeof(T);     // one past the piece's last element
-  pc.sh = (unsigned)(a & 15);
+__device__ __forceinline__ void piece_load(Piece<T>& pc, const char* zb, unsigned off, int n) {
+  pc.sh = off & 15u;
+  const unsigned first = n > 0 ? off & ~15u : 0u;
+  const unsigned last = n > 0 ? (off + (unsigned)n * (unsigned)sizeof(T) - 1u) & ~15u : 0u;
 #pragma unroll
-  for (int i = 0; i < Piece<T>::NS; ++i) {
-    pc.seg[i] = uint4{0u, 0u, 0u, 0u};
-    if (n > 0 && base + 16 * i < end) pc.seg[i] = *(const uint4*)(base + 16 * i);
-  }
+  for (int i = 0; i < Piece<T>::NS; ++i) pc.seg[i] = *(const uint4*)(zb + min(first + 16u * i, last));
 }
 
 template <class T>
@@ -217,6 +218,11 @@ __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z
   const int64_t row0 = w0 / nc;
   const int c0 = (int)(w0 - row0 * nc);
   const T* zrow0 = z + row0 * stride;
+  // the wave's 16-byte-aligned base and each lane's 32-bit offsets from it
+  // (the host bounds the row stride so that 34 rows fit in 32 bits)
+  const unsigned zoff = (unsigned)((uintptr_t)zrow0 & 15);
+  const char* zb = (const char*)zrow0 - zoff;   // (pointer arithmetic keeps the global address space)
+  const unsigned stride_b = (unsigned)stride * (unsigned)sizeof(T);
   uint8_t* crow0 = codes + row0 * (int64_t)(16 * nc);
   _Float16* srow0 = scales + row0 * nc;
   Piece<T> pc[kQRounds];
@@ -232,7 +238,7 @@ __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z
     const int e0 = 32 * c[k] + 8 * qi;            // this lane's first element in the row
     int m = live[k] ? r - e0 : 0;
     n[k] = m < 0 ? 0 : (m > 8 ? 8 : m);
-    piece_load<T>(pc[k], zrow0 + (int64_t)rrel[k] * stride + e0, n[k]);
+    piece_load<T>(pc[k], zb, zoff + rrel[k] * stride_b + (unsigned)e0 * (unsigned)sizeof(T), n[k]);
   }
   // (the whole wave takes part; quads past the end carry zeros)
 #pragma unroll

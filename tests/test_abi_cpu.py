@@ -133,6 +133,10 @@ def test_quant_argument_errors(lib):
     assert lib.palu_quant_latent(p, 3, 4, 32, 32, p, p, None) == UNSUP     # int4 input
     assert lib.palu_quant_latent(p, 0, 4, 32, 32, ctypes.c_void_p(8), p, None) == INVALID  # misaligned codes
     assert lib.palu_quant_latent(p, 0, 0, 32, 32, p, p, None) == 0        # nothing to do
+    # rows more than 64 MiB apart (the kernel addresses 34 rows with 32-bit offsets)
+    assert lib.palu_quant_latent(p, 0, 4, 32, (1 << 24) + 1, p, p, None) == UNSUP     # fp32: 4 B per element
+    assert lib.palu_quant_latent(p, 1, 4, 32, (1 << 25) + 1, p, p, None) == UNSUP     # fp16: 2 B per element
+    assert lib.palu_quant_latent_rotated(p, 2, 4, 32, (1 << 25) + 1, p, p, None) == UNSUP
 
 
 def test_dequant_argument_errors(lib):
