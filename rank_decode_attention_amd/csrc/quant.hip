@@ -215,6 +215,9 @@ __global__ void __launch_bounds__(256) palu_quant_kernel(const T* __restrict__ z
   // row row0, i.e. in row row0 + rel / nc (rel / nc by a multiply with
   // ceil(2^32 / nc), exact for rel < 2^32 / nc; nc = 1 needs none)
   const int64_t w0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * (16 * kQRounds);
+  // (the last block's waves past the work end here: their row base would lie
+  // past the input, and lanes without elements read the base block)
+  if (w0 >= work) return;
   const int64_t row0 = w0 / nc;
   const int c0 = (int)(w0 - row0 * nc);
   const T* zrow0 = z + row0 * stride;

@@ -105,6 +105,30 @@ def test_quant_unaligned_and_long_rows(fmt, r, stride, off):
     assert np.array_equal(got, ref), f"codes differ in {int((got != ref).sum())} bytes"
 
 
+@pytest.mark.parametrize("r", [7, 154])
+def test_quant_rows_at_the_largest_stride(r):
+    """fp16 rows 64 MiB apart, the largest row distance palu_quant_latent
+    takes (its loads address a wave's rows by 32-bit offsets from one row
+    base: with r = 7 a wave's 32 chunks span 32 rows, offsets near 2 GiB)."""
+    import torch
+    import rank_decode_attention_amd as R
+    n_rows, stride = 40, 1 << 25
+    stored = _quant_rows("f16", n_rows, r, seed=r + 11)
+    z = torch.zeros((n_rows, stride), dtype=torch.float16, device="cuda")
+    z[:, :r] = to_device(stored, "f16")
+    nc = oracle.chunks_per_row(r)
+    codes = torch.full((n_rows, 16 * nc), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n_rows, nc), -1, dtype=torch.int16, device="cuda")
+    R.palu_quant_latent(z, r, stride, codes, scales)
+    torch.cuda.synchronize()
+    del z
+    ref_codes, ref_scales = oracle.quant_int4(oracle.upcast(stored, "f16").astype(np.float32))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_scales.view(np.uint16)), "scales differ"
+    got = codes.cpu().numpy()
+    ref = oracle.pack_int4(ref_codes)
+    assert np.array_equal(got, ref), f"codes differ in {int((got != ref).sum())} bytes"
+
+
 def test_quant_empty_is_noop():
     import torch
     import rank_decode_attention_amd as R
