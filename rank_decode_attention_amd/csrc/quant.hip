@@ -180,13 +180,16 @@ __device__ __forceinline__ void quant_quad(float (&v)[8], int qi, int c, int r, 
     }
     // nibble i = q_i & 15: 0x88888888 + sum q_i 16^i holds q_i + 8 (1 .. 15,
     // no carries) in nibble i, and q + 8 = (q & 15) ^ 8 for -8 <= q <= 7
+    // The clamp to +-7 only acts when the scale is an fp16 subnormal: a
+    // normal fp16 scale is within 2^-11 of amax / 7, so |t| < 7.01 and
+    // rint(t) lies in -7 .. 7 already (an infinite scale gives t = 0).
+    if (sf < 0x1p-14f) {   // (rare)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[i] = __builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
+    }
     word = 0x88888888u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // (elements past the row are zero: code 0)
-      const int q = (int)__builtin_amdgcn_fmed3f(qf[i], -7.f, 7.f);
-      word += (unsigned)q << (4 * i);
-    }
+    for (int i = 0; i < 8; ++i) word += (unsigned)(int)qf[i] << (4 * i);   // (elements past the row: code 0)
     word ^= 0x88888888u;
   }
   if (live) {
